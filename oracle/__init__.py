@@ -1,0 +1,183 @@
+"""CPU oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package. The product library (the HIP kernels behind the C ABI) never
+imports, links or calls it, and the two share no code.
+
+The arithmetic lives in `pa_oracle.c` (plain C, float64, OpenMP over
+(sequence, KV head)); this module builds it with gcc and marshals numpy
+arrays into it. Each C function states the passage of the pages it follows.
+Every oracle function here is pinned by a CPU test against something other
+than itself (a library routine, a closed form, an invariant or brute force);
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+KV_BF16 = 1
+KV_FP8_E4M3FN = 2
+
+
+def build(force: bool = False) -> str:
+    """Compile pa_oracle.c with gcc (no fast-math) into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
+        lib.oracle_f32_to_e4m3fn.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_e4m3fn.restype = ctypes.c_uint8
+        lib.oracle_quantize_bf16.argtypes = [ctypes.c_uint16, ctypes.c_float]
+        lib.oracle_quantize_bf16.restype = ctypes.c_uint8
+        lib.oracle_cache_write.argtypes = [P, P, P, i64, i64, i64, i64, i64, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_float, P, P]
+        lib.oracle_cache_write.restype = i64
+        lib.oracle_decode_units.argtypes = [P, P, P, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                            P, P, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                                            P, i64, P, ctypes.c_int]
+        lib.oracle_decode_units.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(bits, dtype=np.uint16).reshape(-1)
+    return np.array([lib.oracle_bf16_to_f64(int(b)) for b in flat], dtype=np.float64).reshape(np.shape(bits))
+
+
+def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    return np.array([lib.oracle_e4m3fn_to_f64(int(c)) for c in flat], dtype=np.float64).reshape(np.shape(codes))
+
+
+def f32_to_e4m3fn(x: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(x, dtype=np.float32).reshape(-1)
+    return np.array([lib.oracle_f32_to_e4m3fn(float(v)) for v in flat], dtype=np.uint8).reshape(np.shape(x))
+
+
+def quantize_bf16(bits: np.ndarray, scale: float) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(bits, dtype=np.uint16).reshape(-1)
+    return np.array([lib.oracle_quantize_bf16(int(b), scale) for b in flat], dtype=np.uint8).reshape(np.shape(bits))
+
+
+def cache_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
+                k_cache: np.ndarray, v_cache: np.ndarray, *, kv_dtype: int = KV_BF16,
+                k_scale: float = 1.0, v_scale: float = 1.0) -> int:
+    """In-place paged cache write. Caches: uint16 bf16 bits or uint8 e4m3fn codes, [N, bs, Hkv, D]."""
+    lib = _load()
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    N, bs, Hkv, D = k_cache.shape
+    T = int(slots.shape[0])
+    assert k.shape == (T, Hkv, D) and v.shape == (T, Hkv, D)
+    want = np.uint16 if kv_dtype == KV_BF16 else np.uint8
+    assert k_cache.dtype == want and v_cache.dtype == want
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    n = lib.oracle_cache_write(_ptr(k), _ptr(v), _ptr(slots), T, Hkv, D, bs, N, kv_dtype,
+                               k_scale, v_scale, _ptr(k_cache), _ptr(v_cache))
+    if n < 0:
+        raise ValueError("slot outside the pool")
+    return int(n)
+
+
+def decode_units(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
+                 units: Sequence[int], num_q_heads: int, *, kv_dtype: int = KV_BF16,
+                 k_scale: float = 1.0, v_scale: float = 1.0, threads: int = 0) -> np.ndarray:
+    """Decode for (seq * Hkv + kv_head) units -> float64 [n_units, g, D]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    S, Hq, D = q.shape
+    assert Hq == num_q_heads
+    N, bs, Hkv, D2 = k_cache.shape
+    assert D2 == D and Hq % Hkv == 0
+    g = Hq // Hkv
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    MB = tables.shape[1]
+    units = np.ascontiguousarray(np.asarray(units, dtype=np.int64))
+    out = np.zeros((len(units), g, D), dtype=np.float64)
+    kc = np.ascontiguousarray(k_cache)
+    vc = np.ascontiguousarray(v_cache)
+    rc = lib.oracle_decode_units(_ptr(q), _ptr(kc), _ptr(vc), kv_dtype, k_scale, v_scale,
+                                 _ptr(tables), _ptr(ctx), S, Hq, Hkv, D, bs, N, MB, float(scale),
+                                 _ptr(units), len(units), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("block id outside the pool or context longer than its table row")
+    return out
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, kv_dtype: int = KV_BF16,
+           k_scale: float = 1.0, v_scale: float = 1.0, threads: int = 0) -> np.ndarray:
+    """Full decode -> float64 [S, Hq, D]."""
+    S, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    out = decode_units(q, k_cache, v_cache, block_tables, context_lens, scale,
+                       np.arange(S * Hkv), Hq, kv_dtype=kv_dtype, k_scale=k_scale,
+                       v_scale=v_scale, threads=threads)
+    return out.reshape(S, Hq, D)
+
+
+def decode_workload(w, *, units: Optional[Sequence[int]] = None, kv_dtype: int = KV_BF16,
+                    k_cache=None, v_cache=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                    threads: int = 0) -> np.ndarray:
+    """Decode a generated workload (all units -> [S, Hq, D], else [n_units, g, D])."""
+    kc = w.k_cache if k_cache is None else k_cache
+    vc = w.v_cache if v_cache is None else v_cache
+    if units is None:
+        return decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, kv_dtype=kv_dtype,
+                      k_scale=k_scale, v_scale=v_scale, threads=threads)
+    return decode_units(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, units,
+                        w.spec.num_q_heads, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
+                        threads=threads)
+
+
+def quantize_pool(bits: np.ndarray, scale: float) -> np.ndarray:
+    """fp8 codes of a whole bf16 pool, through the oracle's cache write (every row written)."""
+    N, bs, Hkv, D = bits.shape
+    rows = np.ascontiguousarray(bits.reshape(N * bs, Hkv, D))
+    out_k = np.zeros((N, bs, Hkv, D), dtype=np.uint8)
+    out_v = np.zeros((N, bs, Hkv, D), dtype=np.uint8)
+    cache_write(rows, rows, np.arange(N * bs, dtype=np.int64), out_k, out_v,
+                kv_dtype=KV_FP8_E4M3FN, k_scale=scale, v_scale=scale)
+    return out_k
