@@ -1,0 +1,191 @@
+/*
+ * pa.h -- paged KV-cache decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Every pointer argument marked
+ * "device" is a device address on the current HIP device; every call is
+ * asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ * default stream) and returns after the launches are queued. The library
+ * allocates nothing and keeps no state between calls: the caller owns every
+ * buffer, including the split-K workspace.
+ *
+ * Pages cited (titles as printed at the top of each page):
+ *   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
+ *   nanoVLLM = «大模型推理优化技术：从nano-vLLM到连续批处理»
+ *   TGI      = «TGI技术解析：大规模语言模型高效推理实践»
+ *   ToPG     = «ToPG框架解析：大模型推理性能优化与三阶段流水线设计»
+ *
+ * Layouts (all row-major, innermost dimension last, no padding):
+ *   q, out        [num_seqs, num_q_heads, head_dim]             bfloat16
+ *   k, v          [num_tokens, num_kv_heads, head_dim]          bfloat16
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim]
+ *   v_cache         bfloat16 (PA_KV_BF16) or fp8 e4m3fn codes (PA_KV_FP8_E4M3FN).
+ *                 This is the physical block pool of Tutorial §4.2
+ *                 "PagedAttention" (PagedKVCache.block_pool) for one layer and
+ *                 one of K/V; nanoVLLM §4.3 sizes a block the same way.
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32: entry b of row i is
+ *                 the physical block holding tokens b*block_size ..
+ *                 b*block_size + block_size - 1 of sequence i (Tutorial §4.2,
+ *                 block_tables; nanoVLLM §4.2 logical-to-physical map).
+ *   context_lens  [num_seqs] int32: cached tokens sequence i attends to.
+ *   slot_mapping  [num_tokens] int64: slot s names row s % block_size of
+ *                 physical block s / block_size (Tutorial §4.2, append_token's
+ *                 block index and offset, flattened).
+ *
+ * Status: every entry point returns PA_OK (0) or a negative PA_ERR_* code.
+ * Arguments are checked on the host before anything is launched; nothing
+ * is read back from the device. Device-side contents (slot ids, block ids,
+ * context lengths) are preconditions: the kernels clamp block ids into the
+ * pool and ignore out-of-pool slots so that a bad table cannot fault the GPU,
+ * but the results are then unspecified.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PA_ERR_SHAPE (-2)       /* a size is negative, zero where it may not be, or inconsistent */
+#define PA_ERR_UNSUPPORTED (-3) /* valid, but outside what the kernels implement */
+#define PA_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
+#define PA_ERR_DTYPE (-5)       /* unknown kv_dtype, or a bad fp8 scale */
+#define PA_ERR_WORKSPACE (-6)   /* workspace missing or smaller than pa_decode_workspace_size */
+#define PA_ERR_LAUNCH (-7)      /* the HIP runtime rejected a launch */
+#define PA_ERR_DEVICE (-8)      /* the current device could not be queried */
+
+/* KV-cache element types. */
+#define PA_KV_BF16 1
+#define PA_KV_FP8_E4M3FN 2 /* OCP FP8 E4M3FN, per-tensor scale (ToPG: fp8 KV compression) */
+
+/* Decode kernel families. */
+#define PA_VARIANT_AUTO 0
+#define PA_VARIANT_VALU 1 /* dot products on the vector ALUs, DPP row reductions */
+#define PA_VARIANT_MFMA 2 /* q.K^T and P.V as 16x16 bf16 MFMA tiles (GQA groups) */
+
+/* Optional decode tuning; pass NULL for the defaults. */
+typedef struct pa_decode_opts {
+    int32_t partition_tokens; /* 0 = chosen by the library; -1 = never split the
+                                 context; >0 = split every context into
+                                 partitions of this many tokens (multiple of 16),
+                                 merged by log-sum-exp. */
+    int32_t variant;          /* PA_VARIANT_* */
+    int32_t waves_per_group;  /* 0 = chosen; else 1, 2, 4 or 8 wavefronts per
+                                 workgroup sharing one partition */
+    int32_t reserved;         /* must be 0 */
+} pa_decode_opts;
+
+/* What pa_decode will launch for a given set of arguments (for tests and
+ * profiling). */
+typedef struct pa_decode_plan {
+    int32_t variant;          /* PA_VARIANT_VALU or PA_VARIANT_MFMA */
+    int32_t waves_per_group;
+    int32_t partition_tokens; /* tokens per partition */
+    int32_t num_partitions;   /* partitions per (sequence, KV head); 1 = no split */
+    int64_t num_workgroups;   /* decode kernel grid size */
+    size_t workspace_bytes;   /* bytes of workspace pa_decode needs (0 if no split) */
+} pa_decode_plan;
+
+/*
+ * pa_cache_write -- store num_tokens new tokens' K and V rows in the paged
+ * caches (Tutorial §4.2, PagedKVCache.append_token: the new K/V row goes to
+ * row `offset` of physical block `block`).
+ *
+ *   k, v           device, [num_tokens, num_kv_heads, head_dim] bfloat16
+ *   slot_mapping   device, [num_tokens] int64; slot < 0 = skip this token;
+ *                  slots must be distinct (concurrent writers otherwise race)
+ *   k_cache,       device, [num_blocks, block_size, num_kv_heads, head_dim]
+ *   v_cache          of kv_dtype; only the addressed rows are written
+ *   kv_dtype       PA_KV_BF16: rows are copied bit for bit.
+ *                  PA_KV_FP8_E4M3FN: each element x becomes the e4m3fn code
+ *                  nearest to float32(x) / scale (correctly rounded division,
+ *                  ties to the even code, magnitudes above 448 saturate to
+ *                  448, NaN stays NaN), with scale = k_scale for K and
+ *                  v_scale for V (Tutorial §3.1 "量化基础", symmetric_quantize:
+ *                  value / scale, rounded and clamped to the code range).
+ *   k_scale,       fp8 only: finite and > 0 (ignored for bf16)
+ *   v_scale
+ * Pointers must be 16-byte aligned; head_dim in {64, 128}; block_size a
+ * power of two in [1, 1024]. num_tokens == 0 returns PA_OK with no launch.
+ */
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
+                   void* k_cache, void* v_cache,
+                   int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int64_t num_blocks,
+                   int32_t kv_dtype, float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode -- one decode step of paged attention: every sequence's single
+ * query token attends over its context_lens[i] cached tokens, reached
+ * through its block-table row (Tutorial §4.2, PagedKVCache.get_kv;
+ * nanoVLLM §4.2, attention through the logical-to-physical block map).
+ * For query head h of sequence i, with g = num_q_heads / num_kv_heads and
+ * KV head kh = h / g (Tutorial §4.4, GroupedQueryAttention: repeat_interleave
+ * of the KV heads):
+ *     s_j      = scale * sum_d q[i,h,d] * K_j[kh,d]      j < context_lens[i]
+ *     out[i,h] = sum_j softmax(s)_j * V_j[kh,:]
+ * with K_j, V_j row j mod block_size of block block_tables[i][j / block_size];
+ * for fp8 caches K_j = code * k_scale and V_j = code * v_scale. Arithmetic is
+ * float32 with bfloat16 inputs (ToPG §2: accumulate in FP32); out is rounded
+ * to bfloat16 (nearest even). A sequence with context length 0 gets zeros.
+ *
+ *   q                device, [num_seqs, num_q_heads, head_dim] bfloat16
+ *   k_cache, v_cache device, [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_tables     device, [num_seqs, max_blocks_per_seq] int32; entries
+ *                    past ceil(context_lens[i] / block_size) are never read
+ *   context_lens     device, [num_seqs] int32, each in
+ *                    [0, max_blocks_per_seq * block_size]
+ *   scale            the score scale (usually 1/sqrt(head_dim))
+ *   out              device, [num_seqs, num_q_heads, head_dim] bfloat16
+ *   workspace        device, >= pa_decode_workspace_size(...) bytes when the
+ *                    plan splits contexts (may be NULL when it does not);
+ *                    scratch, overwritten by each call
+ *   opts             NULL or tuning options
+ * Supported: head_dim in {64, 128}; g in [1, 16]; block_size a power of
+ * two in [16, 1024]; block_size * num_kv_heads * head_dim * element size
+ * < 2^31 bytes. Calls that share a workspace must be ordered on one stream.
+ */
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens,
+              float scale, void* out,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+              int32_t kv_dtype, float k_scale, float v_scale,
+              void* workspace, size_t workspace_bytes,
+              const pa_decode_opts* opts, void* stream);
+
+/*
+ * pa_decode_get_plan -- the launch plan pa_decode would use for these sizes
+ * on the current device (no launch). Returns PA_OK and fills *plan, or the
+ * error pa_decode would return for these sizes.
+ */
+int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                       int32_t kv_dtype, const pa_decode_opts* opts, pa_decode_plan* plan);
+
+/* Bytes of workspace pa_decode needs for these sizes (0 when it does not
+ * split, or when the sizes are invalid). */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t kv_dtype, const pa_decode_opts* opts);
+
+/* Host-side reference of the kernels' fp8 encoder (same source as the
+ * device code): n float32 inputs, already divided by the scale, to e4m3fn
+ * codes. Host pointers. For testing the rounding rule without a GPU. */
+void pa_fp8_e4m3fn_encode_host(const float* x, uint8_t* codes, int64_t n);
+
+/* Static description of a status code. */
+const char* pa_strerror(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

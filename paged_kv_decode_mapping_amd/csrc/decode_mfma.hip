@@ -1,0 +1,251 @@
+// decode_mfma.hip -- paged decode attention with q.K^T and P.V on the
+// matrix cores; the kernel for GQA groups (g >= 4 query heads per KV head).
+//
+// Pages cited (titles as printed at the top of each page):
+//   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
+//   nanoVLLM = «大模型推理优化技术：从nano-vLLM到连续批处理»
+//   ToPG     = «ToPG框架解析：大模型推理性能优化与三阶段流水线设计»
+//
+// What it computes: the same as the VALU kernel -- for the g query heads of
+// one KV head (Tutorial §4.4, GroupedQueryAttention: the heads of a group
+// share one K/V), softmax(q.K^T * scale).V over K/V rows reached through the
+// block table (Tutorial §4.2, get_kv; nanoVLLM §4.2). With g query rows
+// against a 16-token tile, q.K^T is a [g x D] x [D x 16] product and P.V a
+// [g x 16] x [16 x D] one: real dense contractions, so they run as bf16
+// MFMA with fp32 accumulation (ToPG §2: FP32 accumulation).
+//
+// Layout of one 16-token tile in a wave (lane l, c = l % 16, gq = l / 16):
+//   * S = K Q^T by v_mfma_f32_16x16x32_bf16, D/32 times: the A operand is K
+//     (row = token c, eight d values of chunk gq), loaded straight from HBM
+//     with 16-byte buffer loads; B is Q^T (column = head c), kept in
+//     registers. Lane l receives S[token 4*gq + r][head c], r = 0..3.
+//   * The online softmax of head c needs the tile max over the four lane
+//     groups: two cross-lane exchanges per tile.
+//   * O^T = V^T P^T by v_mfma_f32_16x16x16_bf16, D/16 times: B is P^T
+//     (token 4*gq + r, head c) -- exactly the lane's own four probabilities,
+//     rounded to bf16 -- and A is V^T (row = d, token 4*gq + r), read from
+//     the tile's copy in LDS. V goes HBM -> registers -> LDS with
+//     fully-coalesced 16-byte loads (each instruction covers whole rows) so
+//     that the transpose happens in LDS. Lane l accumulates O[d = 16 j +
+//     4 gq + r][head c], so the softmax rescale of head c stays in-lane.
+//   * fp8 caches: codes are widened to bf16 exactly (every e4m3fn value is a
+//     bf16 value) with v_cvt_scalef32_pk_bf16_fp8; the scales are folded into
+//     the score scale and the output.
+//   * Tiles are double-buffered in registers as in the VALU kernel.
+#include "pa_epilogue.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16 fp8 codes -> 16 bf16 (two 8-element halves), exact.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4& hi) {
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        r[2 * i] = __builtin_bit_cast(uint32_t, a);
+        r[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
+    }
+    lo = u32x4{r[0], r[1], r[2], r[3]};
+    hi = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr int NQK = D / 32;         // q.K^T MFMAs per tile
+    constexpr int NPV = D / 16;         // P.V MFMAs per tile
+    constexpr int NIK = D * ESZ / 64;   // 16-byte K loads per lane per tile
+    constexpr int EPL = 16 / ESZ;       // V elements per 16-byte lane load
+    constexpr int LPR = D / EPL;        // lanes per V row
+    constexpr int RPI = 64 / LPR;       // V rows per load instruction
+    constexpr int NIV = kTile / RPI;    // V loads per lane per tile
+    constexpr int RS = D + 8;           // LDS row stride (bf16 elements): +16 bytes per row
+    static_assert(NIV >= 1 && kTile % RPI == 0, "tile shape");
+
+    extern __shared__ float smem[];
+    const WorkItem wi = decode_work_item(a);
+    if (!wi.active) return;
+
+    const int W = (int)(blockDim.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = (int)(threadIdx.x & 63);
+    const int c = lane & 15;
+    const int gq = lane >> 4;
+    const int g = a.group;
+    uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * kTile * RS;
+
+    // Q^T operands: MFMA j takes d = dq(j) + 0..7 of head c, where dq(j) is
+    // the d offset the lane's K operand of MFMA j holds.
+    bf16x8 qb[NQK];
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
+        const int d0 = FP8 ? (64 * (j >> 1) + 16 * gq + 8 * (j & 1)) : (32 * j + 8 * gq);
+        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        if (c < g) w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + c) * D + d0);
+        qb[j] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    float m = -INFINITY;  // running max of head c (log2 units), same in all four lane groups
+    float l = 0.0f;       // running sum over this lane's tokens
+    f32x4 o[NPV];
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int span = wi.t_end - wi.t_begin;
+    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
+    const uint32_t head_off = (uint32_t)wi.kvh * a.head_bytes;
+    const uint32_t koff = (uint32_t)c * a.slot_bytes + head_off + 16u * (uint32_t)gq;
+    const uint32_t voff = (uint32_t)(lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
+    const int bs_mask = (1 << a.block_size_log2) - 1;
+    const float qk = a.qk_scale_log2;
+
+    u32x4 kb0[NIK], vb0[NIV], kb1[NIK], vb1[NIV];
+
+    auto issue = [&](int t, u32x4 (&kb)[NIK], u32x4 (&vb)[NIV]) {
+        const int t0 = wi.t_begin + t * kTile;
+        const int64_t blk = physical_block(a, wi.seq, t0);
+        const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
+        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, a.block_bytes);
+        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, a.block_bytes);
+#pragma unroll
+        for (int i = 0; i < NIK; ++i) kb[i] = buf_load_b128(rk, koff + row0 + 64u * i);
+#pragma unroll
+        for (int i = 0; i < NIV; ++i) vb[i] = buf_load_b128(rv, voff + row0 + (uint32_t)(i * RPI) * a.slot_bytes);
+    };
+
+    auto consume = [&](int t, const u32x4 (&kb)[NIK], const u32x4 (&vb)[NIV]) {
+        const int t0 = wi.t_begin + t * kTile;
+        const int valid = wi.t_end - t0;
+        const bool full = valid >= kTile;
+
+        // V rows -> LDS as bf16 (rows past the context are zeroed: their
+        // weight is 0, but 0 * NaN would not be).
+#pragma unroll
+        for (int i = 0; i < NIV; ++i) {
+            const int row = i * RPI + lane / LPR;
+            u32x4 w = vb[i];
+            if (!full && row >= valid) w = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (!FP8) {
+                *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 8) = w;
+            } else {
+                u32x4 lo, hi;
+                fp8x16_to_bf16(w, lo, hi);
+                *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16) = lo;
+                *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16 + 8) = hi;
+            }
+        }
+
+        // S = K Q^T
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NQK; ++j) {
+            bf16x8 ka;
+            if constexpr (!FP8) {
+                ka = __builtin_bit_cast(bf16x8, kb[j]);
+            } else {
+                u32x4 lo, hi;
+                fp8x16_to_bf16(kb[j >> 1], lo, hi);
+                ka = __builtin_bit_cast(bf16x8, (j & 1) ? hi : lo);
+            }
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j], s, 0, 0, 0);
+        }
+
+        // online softmax for head c over tokens 4*gq + r
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (!full && 4 * gq + r >= valid) ? -INFINITY : s[r] * qk;
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, xor_shfl(mx, 16));
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = fast_exp2(m - ms);
+        m = m_new;
+        bf16x4 pb;
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
+            pb[r] = b;
+            psum += (float)b;
+        }
+        l = fmaf(l, alpha, psum);
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+
+        // O^T += V^T P^T
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const uint16_t* src = vs + (4 * gq) * RS + 16 * j + c;
+            const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[RS] << 16);
+            const uint32_t v23 = (uint32_t)src[2 * RS] | ((uint32_t)src[3 * RS] << 16);
+            const bf16x4 va = __builtin_bit_cast(bf16x4, u32x2{v01, v23});
+            o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    int t = wave;
+    if (t < ntiles) issue(t, kb0, vb0);
+    while (t < ntiles) {
+        if (t + W < ntiles) issue(t + W, kb1, vb1);
+        consume(t, kb0, vb0);
+        t += W;
+        if (t >= ntiles) break;
+        if (t + W < ntiles) issue(t + W, kb0, vb0);
+        consume(t, kb1, vb1);
+        t += W;
+    }
+
+    // the four lane groups hold disjoint token subsets of the same state
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+
+    __syncthreads();  // V staging is dead; reuse LDS for the combine
+    float* sm_ml = smem;
+    float* sm_o = smem + W * g * 2;
+    if (c < g) {
+        if (gq == 0) {
+            sm_ml[(wave * g + c) * 2] = m;
+            sm_ml[(wave * g + c) * 2 + 1] = l;
+        }
+#pragma unroll
+        for (int j = 0; j < NPV; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm_o[(wave * g + c) * D + 16 * j + 4 * gq + r] = o[j][r];
+    }
+    __syncthreads();
+    combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+}
+
+template <int D, bool FP8>
+hipError_t launch_d(const DecodeArgs& a, int waves, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
+    const dim3 block((unsigned)(64 * waves));
+    const size_t stage = (size_t)waves * kTile * (D + 8) * sizeof(uint16_t);
+    const size_t comb = (size_t)waves * a.group * (D + 2) * sizeof(float);
+    const size_t lds = stage > comb ? stage : comb;
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, int waves, hipStream_t s) {
+    if (head_dim == 64) return fp8 ? launch_d<64, true>(a, waves, s) : launch_d<64, false>(a, waves, s);
+    return fp8 ? launch_d<128, true>(a, waves, s) : launch_d<128, false>(a, waves, s);
+}
+
+}  // namespace pa

@@ -1,0 +1,250 @@
+// decode_valu.hip -- paged decode attention with the dot products on the
+// vector ALUs; the kernel for small GQA groups (MHA and g = 2), where a
+// 16-row matrix tile would be mostly padding.
+//
+// Pages cited (titles as printed at the top of each page):
+//   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
+//   nanoVLLM = «大模型推理优化技术：从nano-vLLM到连续批处理»
+//
+// What it computes: for every (sequence, KV head, partition) workgroup, the
+// softmax(q.K^T * scale).V of Tutorial §4.4 (GroupedQueryAttention.forward)
+// for the g query heads that read that KV head, over K/V rows gathered
+// through the block table as in Tutorial §4.2 (PagedKVCache.get_kv) --
+// the "second-level addressing" nanoVLLM §4.2 says standard attention
+// kernels lack.
+//
+// Mapping to gfx950:
+//   * A token row of one KV head (D elements) is covered by LPR lanes, each
+//     holding one 16-byte chunk; one buffer_load_dwordx4 per lane brings
+//     RPI = 64 / LPR whole rows, so every load instruction reads complete
+//     256-byte (bf16, D = 128) rows: full cache lines, no partial sectors.
+//   * The partial dot product of each lane is summed over its row's LPR
+//     lanes with four DPP adds (quad_perm, quad_perm, row_half_mirror,
+//     row_mirror), leaving the score in every lane of the row.
+//   * Each row position of the wave keeps its own online-softmax state (m,
+//     l, o) over the tokens it sees, so the tile loop needs no cross-row
+//     exchange; the RPI states are combined once, after the loop.
+//   * The block id of a 16-token tile is wave-uniform (block_size >= 16),
+//     fetched with a scalar load, and becomes the base of a buffer resource
+//     limited to that block.
+//   * Tiles are double-buffered: the loads of tile t + W are issued before
+//     tile t is consumed.
+#include "pa_epilogue.h"
+
+namespace pa {
+namespace {
+
+template <bool FP8, int EPL>
+__device__ __forceinline__ void unpack(const u32x4& w, float (&f)[EPL]) {
+    if constexpr (!FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_lo(w[i]);
+            f[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+            f[4 * i] = lo[0];
+            f[4 * i + 1] = lo[1];
+            f[4 * i + 2] = hi[0];
+            f[4 * i + 3] = hi[1];
+        }
+    }
+}
+
+template <int D, bool FP8, int GM>
+__global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr int EPL = 16 / ESZ;    // elements per lane per 16-byte load
+    constexpr int LPR = D / EPL;     // lanes per token row
+    constexpr int RPI = 64 / LPR;    // token rows per load instruction
+    constexpr int NI = kTile / RPI;  // load instructions per 16-token tile
+    static_assert(NI >= 1 && kTile % RPI == 0, "tile shape");
+
+    extern __shared__ float smem[];
+    const WorkItem wi = decode_work_item(a);
+    if (!wi.active) return;
+
+    const int W = (int)(blockDim.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = (int)(threadIdx.x & 63);
+    const int r_in = lane / LPR;
+    const int c = lane % LPR;
+    const int g = a.group;
+
+    // q for this lane's EPL dims of each head of the group, as float.
+    float qf[GM][EPL];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        if (h < g) {
+            const uint16_t* qp = a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + h) * D + c * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 8) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(qp + e);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qf[h][e + 2 * i] = bf16_lo(w[i]);
+                    qf[h][e + 2 * i + 1] = bf16_hi(w[i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qf[h][e] = 0.0f;
+        }
+    }
+
+    float m[GM], l[GM], o[GM][EPL];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
+    }
+
+    const int span = wi.t_end - wi.t_begin;
+    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
+    const uint32_t lane_off = (uint32_t)r_in * a.slot_bytes + (uint32_t)wi.kvh * a.head_bytes + (uint32_t)c * 16u;
+    const int bs_mask = (1 << a.block_size_log2) - 1;
+    const float qk = a.qk_scale_log2;
+
+    u32x4 kb0[NI], vb0[NI], kb1[NI], vb1[NI];
+
+    auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
+        const int t0 = wi.t_begin + t * kTile;
+        const int64_t blk = physical_block(a, wi.seq, t0);
+        const uint32_t row0 = (uint32_t)(t0 & bs_mask);
+        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, a.block_bytes);
+        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, a.block_bytes);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t off = lane_off + (row0 + (uint32_t)(i * RPI)) * a.slot_bytes;
+            kb[i] = buf_load_b128(rk, off);
+            vb[i] = buf_load_b128(rv, off);
+        }
+    };
+
+    auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
+        const int t0 = wi.t_begin + t * kTile;
+        const int valid = wi.t_end - t0;
+        const bool full = valid >= kTile;
+        float x[NI][GM];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float kf[EPL];
+            unpack<FP8, EPL>(kb[i], kf);
+            const bool dead = !full && (i * RPI + r_in) >= valid;
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                float s = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s = fmaf(qf[h][e], kf[e], s);
+                s = group_sum<LPR>(s);
+                x[i][h] = dead ? -INFINITY : s * qk;
+            }
+        }
+        float p[NI][GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            float mx = x[0][h];
+#pragma unroll
+            for (int i = 1; i < NI; ++i) mx = fmaxf(mx, x[i][h]);
+            const float m_new = fmaxf(m[h], mx);
+            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m[h] - ms);
+            m[h] = m_new;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                p[i][h] = fast_exp2(x[i][h] - ms);
+                lsum += p[i][h];
+            }
+            l[h] = fmaf(l[h], alpha, lsum);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            u32x4 w = vb[i];
+            if (!full && (i * RPI + r_in) >= valid) w = u32x4{0u, 0u, 0u, 0u};
+            float vf[EPL];
+            unpack<FP8, EPL>(w, vf);
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[i][h], vf[e], o[h][e]);
+            }
+        }
+    };
+
+    int t = wave;
+    if (t < ntiles) issue(t, kb0, vb0);
+    while (t < ntiles) {
+        if (t + W < ntiles) issue(t + W, kb1, vb1);
+        consume(t, kb0, vb0);
+        t += W;
+        if (t >= ntiles) break;
+        if (t + W < ntiles) issue(t + W, kb0, vb0);
+        consume(t, kb1, vb1);
+        t += W;
+    }
+
+    // Combine the RPI row states of the wave (lanes differing in row bits).
+    float* sm_ml = smem;
+    float* sm_o = smem + W * g * 2;
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        float M = m[h];
+#pragma unroll
+        for (int mask = LPR; mask < 64; mask <<= 1) M = fmaxf(M, xor_shfl(M, mask));
+        const float f = state_weight(m[h], M);
+        float lh = l[h] * f;
+#pragma unroll
+        for (int mask = LPR; mask < 64; mask <<= 1) lh += xor_shfl(lh, mask);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            float v = o[h][e] * f;
+#pragma unroll
+            for (int mask = LPR; mask < 64; mask <<= 1) v += xor_shfl(v, mask);
+            o[h][e] = v;
+        }
+        if (h < g) {
+            if (lane == 0) {
+                sm_ml[(wave * g + h) * 2] = M;
+                sm_ml[(wave * g + h) * 2 + 1] = lh;
+            }
+            if (r_in == 0) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm_o[(wave * g + h) * D + c * EPL + e] = o[h][e];
+            }
+        }
+    }
+    __syncthreads();
+    combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+}
+
+template <int D, bool FP8>
+hipError_t launch_d(const DecodeArgs& a, int waves, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
+    const dim3 block((unsigned)(64 * waves));
+    const size_t lds = (size_t)waves * a.group * (D + 2) * sizeof(float);
+    const int g = a.group;
+    if (g <= 1) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 1>), grid, block, lds, s, a);
+    else if (g <= 2) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 2>), grid, block, lds, s, a);
+    else if (g <= 4) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 4>), grid, block, lds, s, a);
+    else if (g <= 8) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 8>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 16>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, int waves, hipStream_t s) {
+    if (head_dim == 64) return fp8 ? launch_d<64, true>(a, waves, s) : launch_d<64, false>(a, waves, s);
+    return fp8 ? launch_d<128, true>(a, waves, s) : launch_d<128, false>(a, waves, s);
+}
+
+}  // namespace pa

@@ -1,0 +1,286 @@
+// pa_api.hip -- the C ABI of libpa: argument checks, launch planning and
+// kernel dispatch. Host code only; nothing here reads device memory or
+// synchronises.
+//
+// Pages cited (titles as printed at the top of each page):
+//   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
+//   nanoVLLM = «大模型推理优化技术：从nano-vLLM到连续批处理»
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/pa.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached per device).
+int current_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < kMaxDevices) {
+        const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return -1;
+    if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+    int variant = PA_VARIANT_VALU;
+    int waves = 4;
+    int partition_tokens = 0;
+    int num_partitions = 1;
+    int64_t num_workgroups = 0;
+    size_t ml_bytes = 0;   // split partial (m, l) array
+    size_t workspace = 0;  // total workspace bytes
+};
+
+int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB,
+                int32_t kv_dtype) {
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || MB <= 0 || bs <= 0 || D <= 0) return PA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return PA_ERR_SHAPE;
+    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
+    if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
+    const int g = Hq / Hkv;
+    if (g > 16) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(bs) || bs < pa::kTile || bs > 1024) return PA_ERR_UNSUPPORTED;
+    const int64_t esz = kv_dtype == PA_KV_BF16 ? 2 : 1;
+    if ((int64_t)bs * Hkv * D * esz >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)MB * bs >= (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB, int32_t kv_dtype,
+              const pa_decode_opts* opts, Plan* plan) {
+    int st = check_sizes(S, Hq, Hkv, D, bs, MB, kv_dtype);
+    if (st != PA_OK) return st;
+    pa_decode_opts o{};
+    if (opts) o = *opts;
+    if (o.reserved != 0) return PA_ERR_SHAPE;
+    const int g = Hq / Hkv;
+    Plan p;
+    // Family: matrix tiles once the GQA group fills a useful part of a
+    // 16-row tile (g >= 4); below that the dot products stay on the VALU.
+    if (o.variant != PA_VARIANT_AUTO && o.variant != PA_VARIANT_VALU && o.variant != PA_VARIANT_MFMA)
+        return PA_ERR_SHAPE;
+    p.variant = o.variant != PA_VARIANT_AUTO ? o.variant : (g >= 4 ? PA_VARIANT_MFMA : PA_VARIANT_VALU);
+    if (o.waves_per_group != 0) {
+        if (o.waves_per_group != 1 && o.waves_per_group != 2 && o.waves_per_group != 4 &&
+            o.waves_per_group != 8)
+            return PA_ERR_SHAPE;
+        p.waves = o.waves_per_group;
+    }
+    // The epilogue stages W * g * (D + 2) floats in LDS; stay within 64 KiB.
+    while (p.waves > 1 && (size_t)p.waves * g * (D + 2) * sizeof(float) > 65536) p.waves /= 2;
+    const int64_t cap = (int64_t)MB * bs;  // longest context the tables can hold
+    const int64_t cap16 = align_up((size_t)cap, pa::kTile);
+    const int64_t units = (int64_t)S * Hkv;
+    int64_t P;
+    if (o.partition_tokens > 0) {
+        if (o.partition_tokens % pa::kTile) return PA_ERR_SHAPE;
+        P = o.partition_tokens;
+    } else if (o.partition_tokens < 0) {
+        P = cap16;
+    } else {
+        const int cus = current_cu_count();
+        if (cus <= 0) return PA_ERR_DEVICE;
+        // Enough workgroups to fill the chip several times over, but no split
+        // while whole contexts already give that and stay short.
+        if (cap <= 4096 && units >= 2 * cus) {
+            P = cap16;
+        } else {
+            P = 4096;
+            while (P > 512 && units * ((cap + P - 1) / P) < 4 * cus) P /= 2;
+        }
+    }
+    if (P >= cap16) P = cap16;
+    p.partition_tokens = (int)P;
+    p.num_partitions = (int)((cap + P - 1) / P);
+    if (p.num_partitions < 1) p.num_partitions = 1;
+    p.num_workgroups = units * p.num_partitions;
+    if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if (p.num_partitions > 1) {
+        const size_t rows = (size_t)S * Hq * p.num_partitions;
+        p.ml_bytes = align_up(rows * 2 * sizeof(float), 256);
+        p.workspace = p.ml_bytes + rows * D * sizeof(float);
+    }
+    *plan = p;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int64_t num_blocks, int32_t kv_dtype, float k_scale,
+                   float v_scale, void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_UNSUPPORTED;
+    if (kv_dtype == PA_KV_FP8_E4M3FN &&
+        (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+        return PA_ERR_DTYPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0) return PA_ERR_ALIGN;
+    if (num_tokens * num_kv_heads * (head_dim / 8) >= (int64_t(1) << 40)) return PA_ERR_SHAPE;
+    pa::CacheWriteArgs a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.slot_mapping = slot_mapping;
+    a.k_cache = static_cast<uint8_t*>(k_cache);
+    a.v_cache = static_cast<uint8_t*>(v_cache);
+    a.num_tokens = num_tokens;
+    a.num_slots = num_blocks * block_size;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.k_scale = kv_dtype == PA_KV_FP8_E4M3FN ? k_scale : 1.0f;
+    a.v_scale = kv_dtype == PA_KV_FP8_E4M3FN ? v_scale : 1.0f;
+    const hipError_t e =
+        pa::launch_cache_write(a, kv_dtype == PA_KV_FP8_E4M3FN, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                       const pa_decode_opts* opts, pa_decode_plan* plan) {
+    if (!plan) return PA_ERR_NULL;
+    Plan p;
+    const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, kv_dtype, opts, &p);
+    if (st != PA_OK) return st;
+    plan->variant = p.variant;
+    plan->waves_per_group = p.waves;
+    plan->partition_tokens = p.partition_tokens;
+    plan->num_partitions = p.num_partitions;
+    plan->num_workgroups = p.num_workgroups;
+    plan->workspace_bytes = p.workspace;
+    return PA_OK;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t kv_dtype, const pa_decode_opts* opts) {
+    Plan p;
+    if (make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                  kv_dtype, opts, &p) != PA_OK)
+        return 0;
+    return p.workspace;
+}
+
+int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_blocks_per_seq, int64_t num_blocks, int32_t kv_dtype, float k_scale,
+              float v_scale, void* workspace, size_t workspace_bytes, const pa_decode_opts* opts,
+              void* stream) {
+    Plan p;
+    int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                       kv_dtype, opts, &p);
+    if (st != PA_OK) return st;
+    if (num_blocks <= 0) return PA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
+    if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+        return PA_ERR_DTYPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return PA_ERR_ALIGN;
+    if (p.num_partitions > 1) {
+        if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+    }
+    const int64_t esz = fp8 ? 1 : 2;
+    pa::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    if (p.num_partitions > 1) {
+        a.part_ml = static_cast<float*>(workspace);
+        a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ml_bytes);
+    }
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.block_size_log2 = log2i(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.partition_tokens = p.partition_tokens;
+    a.num_partitions = p.num_partitions;
+    a.num_blocks = num_blocks;
+    a.head_bytes = (uint32_t)(head_dim * esz);
+    a.slot_bytes = (uint32_t)((int64_t)num_kv_heads * head_dim * esz);
+    a.block_bytes = (uint32_t)((int64_t)block_size * num_kv_heads * head_dim * esz);
+    a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, p.waves, s)
+                                                : pa::launch_decode_valu(a, head_dim, fp8, p.waves, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+    if (p.num_partitions > 1) {
+        pa::MergeArgs m{};
+        m.context_lens = context_lens;
+        m.part_ml = a.part_ml;
+        m.part_o = a.part_o;
+        m.out = a.out;
+        m.num_seqs = num_seqs;
+        m.num_q_heads = num_q_heads;
+        m.head_dim = head_dim;
+        m.partition_tokens = p.partition_tokens;
+        m.num_partitions = p.num_partitions;
+        m.max_context = max_blocks_per_seq * block_size;
+        e = pa::launch_merge(m, s);
+        if (e != hipSuccess) return PA_ERR_LAUNCH;
+    }
+    return PA_OK;
+}
+
+void pa_fp8_e4m3fn_encode_host(const float* x, uint8_t* codes, int64_t n) {
+    if (!x || !codes) return;
+    for (int64_t i = 0; i < n; ++i) codes[i] = pa::fp8_e4m3fn_encode(x[i]);
+}
+
+const char* pa_strerror(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "a required pointer is NULL";
+        case PA_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case PA_ERR_UNSUPPORTED: return "valid but not supported by the kernels";
+        case PA_ERR_ALIGN: return "a pointer is not suitably aligned";
+        case PA_ERR_DTYPE: return "unknown kv dtype or bad fp8 scale";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case PA_ERR_DEVICE: return "the current HIP device could not be queried";
+        default: return "unknown status";
+    }
+}
+
+int pa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// pa_epilogue.h -- the part of a decode workgroup after its tile loop:
+// combine the per-wave online-softmax states and store either the final
+// bf16 output or a split-K partial.
+//
+// A state over a token subset T is (m, l, o) with m = max_{j in T} x_j (x =
+// score in log2 units), l = sum 2^(x_j - m), o = sum 2^(x_j - m) V_j. Two
+// states combine exactly: M = max(m1, m2), l = l1 2^(m1-M) + l2 2^(m2-M),
+// o = o1 2^(m1-M) + o2 2^(m2-M); the output is o / l. This is the
+// softmax of Tutorial «大模型推理优化与加速完全教程» §4.4 evaluated in pieces
+// (the tiling idea TGI «TGI技术解析» §5.2 credits to Flash Attention).
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// Scale factor 2^(m_w - M) of a state with max m_w inside a combination with
+// max M; an empty state (m_w = -inf) contributes nothing.
+__device__ __forceinline__ float state_weight(float m_w, float M) {
+    return (m_w == -INFINITY) ? 0.0f : fast_exp2(m_w - M);
+}
+
+// sm_ml: [W][g][2] (m, l); sm_o: [W][g][D]. Called by all threads of the
+// workgroup after a barrier that follows the writes into LDS.
+template <int D>
+__device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const float* sm_ml,
+                                                  const float* sm_o, int W, int seq, int kvh,
+                                                  int part, bool final_out) {
+    const int g = a.group;
+    for (int idx = (int)threadIdx.x; idx < g * D; idx += (int)blockDim.x) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = -INFINITY;
+        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_ml[(w * g + h) * 2]);
+        float L = 0.0f, O = 0.0f;
+        if (M != -INFINITY) {
+            for (int w = 0; w < W; ++w) {
+                const float f = state_weight(sm_ml[(w * g + h) * 2], M);
+                L += sm_ml[(w * g + h) * 2 + 1] * f;
+                O += sm_o[(w * g + h) * D + d] * f;
+            }
+        }
+        const int hq = kvh * g + h;
+        const int64_t row = (int64_t)seq * a.num_q_heads + hq;
+        if (final_out) {
+            const float y = (L > 0.0f) ? (O * a.v_scale) / L : 0.0f;
+            a.out[row * D + d] = f32_to_bf16_rne(y);
+        } else {
+            const int64_t prow = row * a.num_partitions + part;
+            a.part_o[prow * D + d] = O * a.v_scale;
+            if (d == 0) {
+                a.part_ml[prow * 2] = M;
+                a.part_ml[prow * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// Which tokens a decode workgroup owns and what it must store.
+struct WorkItem {
+    int seq, kvh, part;
+    int t_begin, t_end;   // token range [t_begin, t_end) of the sequence
+    bool final_out;       // store the bf16 output (else a partial)
+    bool active;          // false: nothing to do (empty partition)
+};
+
+__device__ __forceinline__ WorkItem decode_work_item(const DecodeArgs& a) {
+    WorkItem w;
+    const int bid = (int)blockIdx.x;
+    const int P = a.num_partitions;
+    w.part = bid % P;
+    const int unit = bid / P;
+    w.kvh = unit % a.num_kv_heads;
+    w.seq = unit / a.num_kv_heads;
+    int ctx = a.context_lens[w.seq];
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int parts_used = (ctx + a.partition_tokens - 1) / a.partition_tokens;
+    w.t_begin = w.part * a.partition_tokens;
+    w.t_end = min(w.t_begin + a.partition_tokens, ctx);
+    // Partition 0 always runs, so that a zero-length context still gets its
+    // (all-zero) output row.
+    w.active = (w.part < parts_used) || (w.part == 0);
+    w.final_out = (P == 1) || (parts_used <= 1);
+    return w;
+}
+
+// Physical block of a token, clamped into the pool so that a bad table entry
+// cannot address memory outside it.
+__device__ __forceinline__ int64_t physical_block(const DecodeArgs& a, int seq, int token) {
+    int64_t b = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + (token >> a.block_size_log2)];
+    b = b < 0 ? 0 : b;
+    b = b >= a.num_blocks ? a.num_blocks - 1 : b;
+    return b;
+}
+
+}  // namespace pa

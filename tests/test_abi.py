@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: exports, status strings, host-side checks and plans,
+and the kernels' fp8 encoder (same source, built for the host) against the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_decode_mapping_amd as pa
+from paged_kv_decode_mapping_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.fail("libpa.so is not built (python -m paged_kv_decode_mapping_amd.build)")
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert {"pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(0, -9, -1):
+        s = pa.strerror(code)
+        assert s and s != "unknown status"
+    assert pa.strerror(-99) == "unknown status"
+    assert lib.pa_version() >= 100
+
+
+def test_host_fp8_encoder_matches_oracle_on_all_bf16_values(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = W.bf16_bits_to_f32(bits)
+    got = pa.fp8_encode_host(x)
+    want = oracle.f32_to_e4m3fn(x)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("scale", [1.0, 4.7 / 448, 0.0123, 3.0e-3, 17.0])
+def test_host_fp8_quantiser_matches_oracle(lib, scale):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(all="ignore"):
+        y = W.bf16_bits_to_f32(bits) / np.float32(scale)  # IEEE float32 division
+    assert np.array_equal(pa.fp8_encode_host(y), oracle.quantize_bf16(bits, scale))
+
+
+# Fake, never-dereferenced device addresses for argument checks that must
+# fail before anything is launched.
+A = 0x10000
+
+
+def _decode(lib, **kw):
+    args = dict(q=A, k=A, v=A, bt=A, cl=A, scale=0.125, out=A, S=4, Hq=8, Hkv=2, D=64, bs=16, MB=7, N=32,
+                kvd=1, ks=1.0, vs=1.0, ws=None, wsb=0, opts=pa._opts(partition_tokens=-1))
+    args.update(kw)
+    o = args["opts"]
+    return lib.pa_decode(args["q"], args["k"], args["v"], args["bt"], args["cl"], args["scale"], args["out"],
+                         args["S"], args["Hq"], args["Hkv"], args["D"], args["bs"], args["MB"], args["N"],
+                         args["kvd"], args["ks"], args["vs"], args["ws"], args["wsb"],
+                         ctypes.byref(o) if o is not None else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), -3), (dict(D=256), -3), (dict(Hq=6, Hkv=4), -2), (dict(Hq=64, Hkv=2), -3),
+    (dict(bs=8), -3), (dict(bs=24), -3), (dict(kvd=7), -5), (dict(MB=0), -2), (dict(S=-1), -2),
+    (dict(N=0), -2), (dict(q=None), -1), (dict(bt=None), -1), (dict(out=A + 8), -4), (dict(k=A + 2), -4),
+    (dict(kvd=2, ks=0.0), -5), (dict(kvd=2, vs=float("nan")), -5), (dict(scale=float("inf")), -2),
+    (dict(opts=pa._opts(partition_tokens=24)), -2), (dict(opts=pa._opts(waves=3)), -2),
+    (dict(opts=pa._opts(partition_tokens=32)), -6),
+    (dict(opts=pa._opts(partition_tokens=32), ws=A, wsb=16), -6),
+])
+def test_decode_rejects_bad_arguments_without_launching(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_zero_sequences_is_a_no_op(lib):
+    assert _decode(lib, S=0, q=None, out=None) == 0
+
+
+def test_plan_with_explicit_partitions(lib):
+    p = pa.pa_decode_get_plan(128, 64, 8, 128, 16, 256, partition_tokens=512, variant="valu", waves=4)
+    assert p["num_partitions"] == 8 and p["partition_tokens"] == 512
+    assert p["num_workgroups"] == 128 * 8 * 8
+    rows = 128 * 64 * 8
+    ml = -(-rows * 8 // 256) * 256
+    assert p["workspace_bytes"] == ml + rows * 128 * 4
+    p1 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1)
+    assert p1["num_partitions"] == 1 and p1["workspace_bytes"] == 0
+    assert p1["partition_tokens"] == 112
+    # a partition longer than the longest possible context is no split
+    p2 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=4096)
+    assert p2["num_partitions"] == 1
+
+
+def _cw(lib, **kw):
+    args = dict(k=A, v=A, slots=A, kc=A, vc=A, T=4, Hkv=2, D=64, bs=16, N=32, kvd=1, ks=1.0, vs=1.0)
+    args.update(kw)
+    return lib.pa_cache_write(args["k"], args["v"], args["slots"], args["kc"], args["vc"], args["T"], args["Hkv"],
+                              args["D"], args["bs"], args["N"], args["kvd"], args["ks"], args["vs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(kvd=3), -5), (dict(D=80), -3),
+    (dict(bs=12), -3), (dict(k=None), -1), (dict(slots=None), -1), (dict(kc=A + 4), -4),
+    (dict(slots=A + 4), -4), (dict(kvd=2, ks=-1.0), -5), (dict(kvd=2, vs=float("inf")), -5),
+])
+def test_cache_write_rejects_bad_arguments(lib, kw, code):
+    assert _cw(lib, **kw) == code
+
+
+def test_cache_write_zero_tokens_is_a_no_op(lib):
+    assert _cw(lib, T=0, k=None, v=None, slots=None) == 0
