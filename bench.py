@@ -18,7 +18,6 @@ Prints progress on stderr and ONE JSON line on stdout:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -53,15 +52,6 @@ def write_bytes(w, kv_bytes: int) -> int:
     return int(T * s.num_kv_heads * s.head_dim * (2 * 2 + 2 * kv_bytes) + 8 * T)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_kv_decode_mapping_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload: str, kv: str):
     """HBM traffic per decode launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources."""
@@ -72,6 +62,7 @@ def load_traffic(workload: str, kv: str):
         d = json.load(open(p))
     except Exception:
         return None
+    from paged_kv_decode_mapping_amd.profiling import kernel_source_hash
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("bytes_per_launch")
@@ -116,6 +107,10 @@ def main() -> int:
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
+    ap.add_argument("--prefetch", type=int, default=0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, copy this many MiB device-to-device once (a plain copy kernel "
+                         "of known size, the reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -168,7 +163,8 @@ def main() -> int:
     kv_b = 2 if args.kv == "bf16" else 1
     plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
                                  w.max_blocks_per_seq, pa.PA_KV_BF16 if args.kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
-                                 partition_tokens=args.partition, variant=args.variant, waves=args.waves)
+                                 partition_tokens=args.partition, variant=args.variant, waves=args.waves,
+                                 prefetch=args.prefetch)
     log(f"plan {plan}")
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -181,9 +177,20 @@ def main() -> int:
         if ev is not None:
             ev[1].record(stream)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
-                     workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves)
+                     workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
+                     prefetch=args.prefetch)
         if ev is not None:
             ev[2].record(stream)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -213,7 +220,8 @@ def main() -> int:
         import oracle
         units = np.random.default_rng(9).choice(s.num_seqs * s.num_kv_heads, 32, replace=False)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
-                     workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves)
+                     workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
+                     prefetch=args.prefetch)
         got = out.cpu().view(torch.int16).numpy().view(np.uint16)
         kvd = oracle.KV_BF16 if args.kv == "bf16" else oracle.KV_FP8_E4M3FN
         if args.kv == "fp8" and kq is None:

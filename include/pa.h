@@ -64,7 +64,7 @@ extern "C" {
 
 /* Decode kernel families. */
 #define PA_VARIANT_AUTO 0
-#define PA_VARIANT_VALU 1 /* dot products on the vector ALUs, DPP row reductions */
+#define PA_VARIANT_VALU 1 /* dot products on the vector ALUs, DPP row reductions (g <= 4) */
 #define PA_VARIANT_MFMA 2 /* q.K^T and P.V as 16x16 bf16 MFMA tiles (GQA groups) */
 
 /* Optional decode tuning; pass NULL for the defaults. */
@@ -76,6 +76,9 @@ typedef struct pa_decode_opts {
     int32_t variant;          /* PA_VARIANT_* */
     int32_t waves_per_group;  /* 0 = chosen; else 1, 2, 4 or 8 wavefronts per
                                  workgroup sharing one partition */
+    int32_t prefetch_tiles;   /* 0 = chosen; else 1..3: 16-token tiles each
+                                 wavefront keeps in flight ahead of the one it
+                                 consumes */
     int32_t reserved;         /* must be 0 */
 } pa_decode_opts;
 
@@ -86,6 +89,8 @@ typedef struct pa_decode_plan {
     int32_t waves_per_group;
     int32_t partition_tokens; /* tokens per partition */
     int32_t num_partitions;   /* partitions per (sequence, KV head); 1 = no split */
+    int32_t prefetch_tiles;
+    int32_t reserved;
     int64_t num_workgroups;   /* decode kernel grid size */
     size_t workspace_bytes;   /* bytes of workspace pa_decode needs (0 if no split) */
 } pa_decode_plan;

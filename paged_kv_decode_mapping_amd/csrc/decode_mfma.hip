@@ -31,7 +31,8 @@
 //   * fp8 caches: codes are widened to bf16 exactly (every e4m3fn value is a
 //     bf16 value) with v_cvt_scalef32_pk_bf16_fp8; the scales are folded into
 //     the score scale and the output.
-//   * Tiles are double-buffered in registers as in the VALU kernel.
+//   * Each wave keeps a ring of NB tiles in registers: NB - 1 tiles are in
+//     flight while one is consumed (the same scheme as the VALU kernel).
 #include "pa_epilogue.h"
 
 namespace pa {
@@ -56,7 +57,7 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4&
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int NB>
 __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int NQK = D / 32;         // q.K^T MFMAs per tile
@@ -106,14 +107,21 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
     const int bs_mask = (1 << a.block_size_log2) - 1;
     const float qk = a.qk_scale_log2;
 
-    u32x4 kb0[NIK], vb0[NIV], kb1[NIK], vb1[NIV];
+    u32x4 kb[NB][NIK], vb[NB][NIV];  // ring of NB tiles: NB - 1 in flight while one is consumed
 
+    // Loads for tile t. A tile past the end (the prefetch after the last
+    // one) still issues its loads, against a zero-byte buffer: they return
+    // zeros without touching memory, and every path through the loop keeps
+    // the same number of loads in flight, so the wait before a tile's use
+    // never has to drain the prefetch behind it.
     auto issue = [&](int t, u32x4 (&kb)[NIK], u32x4 (&vb)[NIV]) {
-        const int t0 = wi.t_begin + t * kTile;
+        const bool live = t < ntiles;
+        const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
         const int64_t blk = physical_block(a, wi.seq, t0);
         const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
-        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, a.block_bytes);
-        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, a.block_bytes);
+        const uint32_t nbytes = live ? a.block_bytes : 0u;
+        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
+        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
 #pragma unroll
         for (int i = 0; i < NIK; ++i) kb[i] = buf_load_b128(rk, koff + row0 + 64u * i);
 #pragma unroll
@@ -197,16 +205,26 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    int t = wave;
-    if (t < ntiles) issue(t, kb0, vb0);
-    while (t < ntiles) {
-        if (t + W < ntiles) issue(t + W, kb1, vb1);
-        consume(t, kb0, vb0);
-        t += W;
-        if (t >= ntiles) break;
-        if (t + W < ntiles) issue(t + W, kb0, vb0);
-        consume(t, kb1, vb1);
-        t += W;
+    if (ntiles > 0) {
+        // The ring is unrolled so that every buffer index is a constant.
+        // sched_barrier keeps the compiler from sinking the prefetch below
+        // the waits of the tile being consumed.
+        int t = wave;
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
+        bool go = t < ntiles;
+        while (go) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (go) {
+                    issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    consume(t, kb[b], vb[b]);
+                    t += W;
+                    go = t < ntiles;
+                }
+            }
+        }
     }
 
     // the four lane groups hold disjoint token subsets of the same state
@@ -230,22 +248,30 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
     combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int NB>
 hipError_t launch_d(const DecodeArgs& a, int waves, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
     const dim3 block((unsigned)(64 * waves));
     const size_t stage = (size_t)waves * kTile * (D + 8) * sizeof(uint16_t);
     const size_t comb = (size_t)waves * a.group * (D + 2) * sizeof(float);
     const size_t lds = stage > comb ? stage : comb;
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB>), grid, block, lds, s, a);
     return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_nb(const DecodeArgs& a, int waves, int depth, hipStream_t s) {
+    if (depth <= 2) return launch_d<D, FP8, 2>(a, waves, s);
+    if (depth == 3) return launch_d<D, FP8, 3>(a, waves, s);
+    return launch_d<D, FP8, 4>(a, waves, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, int waves, hipStream_t s) {
-    if (head_dim == 64) return fp8 ? launch_d<64, true>(a, waves, s) : launch_d<64, false>(a, waves, s);
-    return fp8 ? launch_d<128, true>(a, waves, s) : launch_d<128, false>(a, waves, s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, int waves, int depth, hipStream_t s) {
+    if (head_dim == 64)
+        return fp8 ? launch_nb<64, true>(a, waves, depth, s) : launch_nb<64, false>(a, waves, depth, s);
+    return fp8 ? launch_nb<128, true>(a, waves, depth, s) : launch_nb<128, false>(a, waves, depth, s);
 }
 
 }  // namespace pa

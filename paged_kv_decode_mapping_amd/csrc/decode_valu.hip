@@ -27,8 +27,9 @@
 //   * The block id of a 16-token tile is wave-uniform (block_size >= 16),
 //     fetched with a scalar load, and becomes the base of a buffer resource
 //     limited to that block.
-//   * Tiles are double-buffered: the loads of tile t + W are issued before
-//     tile t is consumed.
+//   * Each wave keeps a ring of NB tiles in registers: the loads of tile
+//     t + (NB - 1) W are issued before tile t is consumed.
+//   * g <= 4 only (the plan sends larger groups to the MFMA kernel).
 #include "pa_epilogue.h"
 
 namespace pa {
@@ -55,7 +56,7 @@ __device__ __forceinline__ void unpack(const u32x4& w, float (&f)[EPL]) {
     }
 }
 
-template <int D, bool FP8, int GM>
+template <int D, bool FP8, int GM, int NB>
 __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int EPL = 16 / ESZ;    // elements per lane per 16-byte load
@@ -111,14 +112,21 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
     const int bs_mask = (1 << a.block_size_log2) - 1;
     const float qk = a.qk_scale_log2;
 
-    u32x4 kb0[NI], vb0[NI], kb1[NI], vb1[NI];
+    u32x4 kb[NB][NI], vb[NB][NI];  // ring of NB tiles: NB - 1 in flight while one is consumed
 
+    // Loads for tile t. A tile past the end (the prefetch after the last
+    // one) still issues its loads, against a zero-byte buffer: they return
+    // zeros without touching memory, and every path through the loop keeps
+    // the same number of loads in flight, so the wait before a tile's use
+    // never has to drain the prefetch behind it.
     auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
-        const int t0 = wi.t_begin + t * kTile;
+        const bool live = t < ntiles;
+        const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
         const int64_t blk = physical_block(a, wi.seq, t0);
         const uint32_t row0 = (uint32_t)(t0 & bs_mask);
-        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, a.block_bytes);
-        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, a.block_bytes);
+        const uint32_t nbytes = live ? a.block_bytes : 0u;
+        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
+        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const uint32_t off = lane_off + (row0 + (uint32_t)(i * RPI)) * a.slot_bytes;
@@ -180,16 +188,26 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
         }
     };
 
-    int t = wave;
-    if (t < ntiles) issue(t, kb0, vb0);
-    while (t < ntiles) {
-        if (t + W < ntiles) issue(t + W, kb1, vb1);
-        consume(t, kb0, vb0);
-        t += W;
-        if (t >= ntiles) break;
-        if (t + W < ntiles) issue(t + W, kb0, vb0);
-        consume(t, kb1, vb1);
-        t += W;
+    if (ntiles > 0) {
+        // The ring is unrolled so that every buffer index is a constant.
+        // sched_barrier keeps the compiler from sinking the prefetch below
+        // the waits of the tile being consumed.
+        int t = wave;
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
+        bool go = t < ntiles;
+        while (go) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (go) {
+                    issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    consume(t, kb[b], vb[b]);
+                    t += W;
+                    go = t < ntiles;
+                }
+            }
+        }
     }
 
     // Combine the RPI row states of the wave (lanes differing in row bits).
@@ -226,25 +244,30 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
     combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
 }
 
-template <int D, bool FP8>
-hipError_t launch_d(const DecodeArgs& a, int waves, hipStream_t s) {
+template <int D, bool FP8, int GM>
+hipError_t launch_g(const DecodeArgs& a, int waves, int depth, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
     const dim3 block((unsigned)(64 * waves));
     const size_t lds = (size_t)waves * a.group * (D + 2) * sizeof(float);
-    const int g = a.group;
-    if (g <= 1) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 1>), grid, block, lds, s, a);
-    else if (g <= 2) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 2>), grid, block, lds, s, a);
-    else if (g <= 4) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 4>), grid, block, lds, s, a);
-    else if (g <= 8) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 8>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, 16>), grid, block, lds, s, a);
+    if (depth <= 2) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, 2>), grid, block, lds, s, a);
+    else if (depth == 3) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, 3>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, 4>), grid, block, lds, s, a);
     return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_d(const DecodeArgs& a, int waves, int depth, hipStream_t s) {
+    if (a.group <= 1) return launch_g<D, FP8, 1>(a, waves, depth, s);
+    if (a.group <= 2) return launch_g<D, FP8, 2>(a, waves, depth, s);
+    return launch_g<D, FP8, 4>(a, waves, depth, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, int waves, hipStream_t s) {
-    if (head_dim == 64) return fp8 ? launch_d<64, true>(a, waves, s) : launch_d<64, false>(a, waves, s);
-    return fp8 ? launch_d<128, true>(a, waves, s) : launch_d<128, false>(a, waves, s);
+hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, int waves, int depth, hipStream_t s) {
+    if (head_dim == 64)
+        return fp8 ? launch_d<64, true>(a, waves, depth, s) : launch_d<64, false>(a, waves, depth, s);
+    return fp8 ? launch_d<128, true>(a, waves, depth, s) : launch_d<128, false>(a, waves, depth, s);
 }
 
 }  // namespace pa

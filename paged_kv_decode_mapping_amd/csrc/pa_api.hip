@@ -45,6 +45,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Plan {
     int variant = PA_VARIANT_VALU;
     int waves = 4;
+    int depth = 3;  // register-ring tiles per wave (prefetch distance + 1)
     int partition_tokens = 0;
     int num_partitions = 1;
     int64_t num_workgroups = 0;
@@ -81,6 +82,9 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     if (o.variant != PA_VARIANT_AUTO && o.variant != PA_VARIANT_VALU && o.variant != PA_VARIANT_MFMA)
         return PA_ERR_SHAPE;
     p.variant = o.variant != PA_VARIANT_AUTO ? o.variant : (g >= 4 ? PA_VARIANT_MFMA : PA_VARIANT_VALU);
+    if (p.variant == PA_VARIANT_VALU && g > 4) return PA_ERR_UNSUPPORTED;
+    if (o.prefetch_tiles < 0 || o.prefetch_tiles > 3) return PA_ERR_SHAPE;
+    if (o.prefetch_tiles > 0) p.depth = o.prefetch_tiles + 1;
     if (o.waves_per_group != 0) {
         if (o.waves_per_group != 1 && o.waves_per_group != 2 && o.waves_per_group != 4 &&
             o.waves_per_group != 8)
@@ -174,6 +178,8 @@ int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     plan->waves_per_group = p.waves;
     plan->partition_tokens = p.partition_tokens;
     plan->num_partitions = p.num_partitions;
+    plan->prefetch_tiles = p.depth - 1;
+    plan->reserved = 0;
     plan->num_workgroups = p.num_workgroups;
     plan->workspace_bytes = p.workspace;
     return PA_OK;
@@ -240,8 +246,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, p.waves, s)
-                                                : pa::launch_decode_valu(a, head_dim, fp8, p.waves, s);
+    hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, p.waves, p.depth, s)
+                                                : pa::launch_decode_valu(a, head_dim, fp8, p.waves, p.depth, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
     if (p.num_partitions > 1) {
         pa::MergeArgs m{};

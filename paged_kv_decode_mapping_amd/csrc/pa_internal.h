@@ -52,8 +52,9 @@ struct CacheWriteArgs {
 };
 
 // Launchers: return the hipError_t of the launch.
-hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, int waves, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, int waves, hipStream_t s);
+// `depth` = tiles a wave keeps in its register ring (2..4).
+hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, int waves, int depth, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, int waves, int depth, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool fp8, hipStream_t s);
 

@@ -1,0 +1,135 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    python -m paged_kv_decode_mapping_amd.profiling stats  <rocprof dir> <out.md> --cmd "<command>"
+    python -m paged_kv_decode_mapping_amd.profiling traffic <fetch dir> <write dir> <out.json> \
+        --workload NAME --kv bf16 --copy-bytes N --cmd "<commands>"
+
+`stats` reads the kernel statistics CSV of a `rocprofv3 --kernel-trace
+--stats --output-format csv` run. `traffic` reads the counter-collection CSVs
+of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of the same
+command (which starts with a device copy of `copy-bytes` bytes), scales each
+counter by what it reads for that copy (bytes moved / counter value), and
+writes the HBM bytes per decode launch, tagged with a hash of the kernel
+sources so that a stale figure is not reported after the kernels change.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_decode_mapping_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[-1]
+
+
+def _short(name: str) -> str:
+    n = name.split("(")[0]
+    for p in ("void ", "pa::(anonymous namespace)::", "pa::"):
+        n = n.replace(p, "")
+    return n.strip()
+
+
+def stats(d: str) -> list:
+    rows = []
+    with open(_find(d, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": r.get("Name", ""), "calls": int(float(r.get("Calls", 0))),
+                         "total_ns": float(r.get("TotalDurationNs", 0)), "avg_ns": float(r.get("AverageNs", 0)),
+                         "min_ns": float(r.get("MinNs", 0)), "max_ns": float(r.get("MaxNs", 0)),
+                         "pct": float(r.get("Percentage", 0))})
+    rows.sort(key=lambda r: -r["total_ns"])
+    return rows
+
+
+def counters(d: str) -> dict:
+    """{kernel name: {counter: [value per dispatch]}}"""
+    out = defaultdict(lambda: defaultdict(list))
+    with open(_find(d, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            out[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def cmd_stats(a) -> None:
+    rows = stats(a.dir)
+    lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+             "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['name'])}` | {r['calls']} | {r['avg_ns'] / 1e3:.2f} | {r['min_ns'] / 1e3:.2f} | "
+                     f"{r['max_ns'] / 1e3:.2f} | {r['pct']:.1f} |")
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_traffic(a) -> None:
+    fetch = counters(a.fetch_dir)
+    write = counters(a.write_dir)
+
+    def pick(cs, key_sub, counter):
+        for k, v in cs.items():
+            if key_sub in k and counter in v:
+                return k, v[counter]
+        raise KeyError(f"{key_sub} / {counter} not in the counter CSV: {list(cs)}")
+
+    # the copy kernel is the first non-pa kernel in the run
+    copy_name = next(k for k in fetch if "pa_" not in k)
+    cf = fetch[copy_name]["FETCH_SIZE"][0]
+    cw = write[copy_name]["WRITE_SIZE"][0]
+    f_scale = a.copy_bytes / cf
+    w_scale = a.copy_bytes / cw
+    dname, dfetch = pick(fetch, "pa_decode_", "FETCH_SIZE")
+    _, dwrite = pick(write, "pa_decode_", "WRITE_SIZE")
+    fb = sorted(dfetch)[len(dfetch) // 2] * f_scale
+    wb = sorted(dwrite)[len(dwrite) // 2] * w_scale
+    res = {"workload": a.workload, "kv": a.kv, "kernel": _short(dname),
+           "copy_kernel": _short(copy_name), "copy_bytes": a.copy_bytes,
+           "fetch_counter_per_copy_byte": cf / a.copy_bytes, "write_counter_per_copy_byte": cw / a.copy_bytes,
+           "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
+           "dispatches": len(dfetch), "kernel_source_hash": kernel_source_hash(), "command": a.cmd}
+    json.dump(res, open(a.out, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel statistics")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("out")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--kv", default="bf16")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

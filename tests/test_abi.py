@@ -81,7 +81,8 @@ def _decode(lib, **kw):
     (dict(N=0), -2), (dict(q=None), -1), (dict(bt=None), -1), (dict(out=A + 8), -4), (dict(k=A + 2), -4),
     (dict(kvd=2, ks=0.0), -5), (dict(kvd=2, vs=float("nan")), -5), (dict(scale=float("inf")), -2),
     (dict(opts=pa._opts(partition_tokens=24)), -2), (dict(opts=pa._opts(waves=3)), -2),
-    (dict(opts=pa._opts(partition_tokens=32)), -6),
+    (dict(opts=pa._opts(partition_tokens=32)), -6), (dict(opts=pa._opts(prefetch=4)), -2),
+    (dict(opts=pa._opts(prefetch=-1)), -2), (dict(Hq=16, Hkv=2, opts=pa._opts(variant="valu")), -3),
     (dict(opts=pa._opts(partition_tokens=32), ws=A, wsb=16), -6),
 ])
 def test_decode_rejects_bad_arguments_without_launching(lib, kw, code):
@@ -93,14 +94,16 @@ def test_decode_zero_sequences_is_a_no_op(lib):
 
 
 def test_plan_with_explicit_partitions(lib):
-    p = pa.pa_decode_get_plan(128, 64, 8, 128, 16, 256, partition_tokens=512, variant="valu", waves=4)
+    p = pa.pa_decode_get_plan(128, 32, 8, 128, 16, 256, partition_tokens=512, variant="valu", waves=4)
     assert p["num_partitions"] == 8 and p["partition_tokens"] == 512
     assert p["num_workgroups"] == 128 * 8 * 8
-    rows = 128 * 64 * 8
+    rows = 128 * 32 * 8
     ml = -(-rows * 8 // 256) * 256
     assert p["workspace_bytes"] == ml + rows * 128 * 4
-    p1 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1)
-    assert p1["num_partitions"] == 1 and p1["workspace_bytes"] == 0
+    assert p["variant"] == "valu" and p["prefetch_tiles"] == 2
+    p1 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, prefetch=3)
+    assert p1["num_partitions"] == 1 and p1["workspace_bytes"] == 0 and p1["prefetch_tiles"] == 3
+    assert p1["variant"] == "mfma"
     assert p1["partition_tokens"] == 112
     # a partition longer than the longest possible context is no split
     p2 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=4096)

@@ -41,11 +41,15 @@ def _oracle(w, **kw):
 
 
 @pytest.mark.parametrize("name", list(REDUCED))
-@pytest.mark.parametrize("variant", ["auto", "valu"])
+@pytest.mark.parametrize("variant", ["auto", "valu", "mfma"])
 def test_decode_matches_oracle(lib, name, variant):
     w = W.make_workload(name, **REDUCED[name])
-    ref = _oracle(w)
     d = DeviceWorkload(w)
+    if variant == "valu" and w.spec.group > 4:
+        with pytest.raises(pa.PAError):
+            d.decode(variant=variant)
+        return
+    ref = _oracle(w)
     note(f"decode {name} variant={variant} plan={pa.pa_decode_get_plan(*_sizes(w), variant=variant)}")
     out = d.decode(variant=variant)
     torch.cuda.synchronize()
@@ -60,26 +64,30 @@ def _sizes(w):
 @pytest.mark.parametrize("name", ["tiny", "long_splitk", "mixed_batch"])
 @pytest.mark.parametrize("partition", [16, 48, 512, -1])
 @pytest.mark.parametrize("waves", [1, 2, 4, 8])
-def test_split_and_waves_agree_with_oracle(lib, name, partition, waves):
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_split_and_waves_agree_with_oracle(lib, name, partition, waves, variant):
     w = W.make_workload(name, **REDUCED[name])
     ref = _oracle(w)
     d = DeviceWorkload(w)
-    note(f"decode {name} partition={partition} waves={waves}")
-    out = d.decode(partition_tokens=partition, waves=waves)
+    prefetch = 1 + (waves + partition) % 3  # every ring depth, spread over the cases
+    note(f"decode {name} partition={partition} waves={waves} variant={variant} prefetch={prefetch}")
+    out = d.decode(partition_tokens=partition, waves=waves, variant=variant, prefetch=prefetch)
     torch.cuda.synchronize()
     compare(host_bits(out), ref, *BF16_TOL)
 
 
-def test_decode_is_deterministic(lib):
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_decode_is_deterministic(lib, variant):
     w = W.make_workload("mixed_batch", **REDUCED["mixed_batch"])
     d = DeviceWorkload(w)
-    note("determinism mixed_batch")
-    a = host_bits(d.decode(partition_tokens=512))
-    b = host_bits(d.decode(partition_tokens=512))
+    note(f"determinism mixed_batch {variant}")
+    a = host_bits(d.decode(partition_tokens=512, variant=variant))
+    b = host_bits(d.decode(partition_tokens=512, variant=variant))
     assert np.array_equal(a, b)
 
 
-def test_edge_contexts(lib):
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_edge_contexts(lib, variant):
     """ctx 0 (zeros), 1 (V exactly), exact multiples of the tile and block,
     and a context filling its whole table row."""
     ctx = [0, 1, 15, 16, 17, 32, 255, 256, 257]
@@ -87,8 +95,8 @@ def test_edge_contexts(lib):
     ref = _oracle(w)
     d = DeviceWorkload(w)
     for part in (-1, 16, 64):
-        note(f"edge contexts partition={part}")
-        got = host_bits(d.decode(partition_tokens=part))
+        note(f"edge contexts partition={part} variant={variant}")
+        got = host_bits(d.decode(partition_tokens=part, variant=variant))
         torch.cuda.synchronize()
         compare(got, ref, *BF16_TOL)
         assert np.all(got[0] == 0)
@@ -98,26 +106,30 @@ def test_edge_contexts(lib):
             assert np.array_equal(got[1, h], w.v_cache[b, o, h // g])
 
 
-def test_context_one_returns_v_bits(lib):
+@pytest.mark.parametrize("variant,name", [("valu", "llama7b_mha"), ("valu", "tiny"), ("mfma", "tiny"),
+                                          ("mfma", "llama70b_gqa")])
+def test_context_one_returns_v_bits(lib, variant, name):
     """ctx = 1 for every sequence: out is V's bf16 bits exactly."""
-    w = W.make_workload("llama70b_gqa", num_seqs=8, context=("list", [1] * 8))
+    w = W.make_workload(name, num_seqs=4, context=("list", [1] * 4))
     d = DeviceWorkload(w)
-    note("ctx=1 exact")
-    got = host_bits(d.decode())
+    note(f"ctx=1 exact {variant}")
+    got = host_bits(d.decode(variant=variant))
     g = w.spec.group
-    for i in range(8):
+    for i in range(4):
         b = w.block_tables[i, 0]
         for h in range(w.spec.num_q_heads):
             assert np.array_equal(got[i, h], w.v_cache[b, 0, h // g])
 
 
-def test_long_block_size_128_partial_tiles(lib):
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_long_block_size_128_partial_tiles(lib, variant):
     w = W.make_workload("long_splitk", num_seqs=3, context=("list", [129, 1000, 300]))
     ref = _oracle(w)
     d = DeviceWorkload(w)
     for part in (-1, 512, 128, 16):
-        note(f"bs128 partition={part}")
-        compare(host_bits(d.decode(partition_tokens=part)), ref, *BF16_TOL)
+        for prefetch in (1, 2, 3):
+            note(f"bs128 partition={part} variant={variant} prefetch={prefetch}")
+            compare(host_bits(d.decode(partition_tokens=part, variant=variant, prefetch=prefetch)), ref, *BF16_TOL)
 
 
 def test_write_then_decode_next_position(lib):
@@ -197,22 +209,26 @@ def test_cache_write_fp8_every_bf16_input(lib, scale):
 
 # ---------------------------------------------------------------- fp8 decode
 
-@pytest.mark.parametrize("name", ["tiny", "mixed_batch", "llama70b_gqa"])
-def test_decode_fp8_matches_oracle(lib, name):
+@pytest.mark.parametrize("name", ["tiny", "mixed_batch", "llama70b_gqa", "llama7b_mha"])
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_decode_fp8_matches_oracle(lib, name, variant):
     w = W.make_workload(name, **REDUCED[name])
+    if variant == "valu" and w.spec.group > 4:
+        pytest.skip("the VALU kernel takes groups of at most 4 query heads")
     ks, vs = w.fp8_scales
     kq = oracle.quantize_pool(w.k_cache, ks)
     vq = oracle.quantize_pool(w.v_cache, vs)
     ref = _oracle(w, kv_dtype=oracle.KV_FP8_E4M3FN, k_cache=kq, v_cache=vq, k_scale=ks, v_scale=vs)
     d = DeviceWorkload(w, kq, vq)
-    note(f"decode fp8 {name}")
-    out = d.decode(k_scale=ks, v_scale=vs)
+    note(f"decode fp8 {name} {variant}")
+    out = d.decode(k_scale=ks, v_scale=vs, variant=variant)
     compare(host_bits(out), ref, *FP8_TOL)
     # reported, and expected to hold: the kernel error alone is bf16-small
     compare(host_bits(out), ref, *BF16_TOL)
 
 
-def test_fp8_decode_reads_every_code_exactly(lib):
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_fp8_decode_reads_every_code_exactly(lib, variant):
     """ctx = 1 with V rows holding all 256 codes: out = code * v_scale exactly
     (NaN codes give NaN), so the device's e4m3fn decoding is the format's."""
     w = W.make_workload("tiny", num_seqs=2, context=("list", [1, 1]))
@@ -222,8 +238,8 @@ def test_fp8_decode_reads_every_code_exactly(lib):
     for i in range(2):
         vq[w.block_tables[i, 0], 0] = codes[i]
     d = DeviceWorkload(w, kq, vq)
-    note("fp8 all codes")
-    got = host_bits(d.decode(k_scale=1.0, v_scale=1.0))
+    note(f"fp8 all codes {variant}")
+    got = host_bits(d.decode(k_scale=1.0, v_scale=1.0, variant=variant))
     want = oracle.e4m3fn_to_f64(codes)
     g = w.spec.group
     for i in range(2):
