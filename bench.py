@@ -108,6 +108,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
     ap.add_argument("--prefetch", type=int, default=0)
+    ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy this many MiB device-to-device once (a plain copy kernel "
                          "of known size, the reference for hardware byte counters)")
@@ -164,7 +165,7 @@ def main() -> int:
     plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
                                  w.max_blocks_per_seq, pa.PA_KV_BF16 if args.kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
                                  partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                                 prefetch=args.prefetch)
+                                 prefetch=args.prefetch, schedule=args.schedule)
     log(f"plan {plan}")
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -178,7 +179,7 @@ def main() -> int:
             ev[1].record(stream)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
                      workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                     prefetch=args.prefetch)
+                     prefetch=args.prefetch, schedule=args.schedule)
         if ev is not None:
             ev[2].record(stream)
 
@@ -187,7 +188,7 @@ def main() -> int:
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.add(src, 1, out=dst)  # an elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         log(f"copy probe: {n} bytes read, {n} bytes written")
         del src, dst
@@ -221,7 +222,7 @@ def main() -> int:
         units = np.random.default_rng(9).choice(s.num_seqs * s.num_kv_heads, 32, replace=False)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
                      workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                     prefetch=args.prefetch)
+                     prefetch=args.prefetch, schedule=args.schedule)
         got = out.cpu().view(torch.int16).numpy().view(np.uint16)
         kvd = oracle.KV_BF16 if args.kv == "bf16" else oracle.KV_FP8_E4M3FN
         if args.kv == "fp8" and kq is None:

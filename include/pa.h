@@ -79,6 +79,10 @@ typedef struct pa_decode_opts {
     int32_t prefetch_tiles;   /* 0 = chosen; else 1..3: 16-token tiles each
                                  wavefront keeps in flight ahead of the one it
                                  consumes */
+    int32_t schedule;         /* 0 or 1 = build the work list on the device
+                                 (longest first, no empty workgroups) and run
+                                 a persistent grid over it; -1 = one workgroup
+                                 per (sequence, KV head, partition) */
     int32_t reserved;         /* must be 0 */
 } pa_decode_opts;
 
@@ -90,9 +94,10 @@ typedef struct pa_decode_plan {
     int32_t partition_tokens; /* tokens per partition */
     int32_t num_partitions;   /* partitions per (sequence, KV head); 1 = no split */
     int32_t prefetch_tiles;
-    int32_t reserved;
-    int64_t num_workgroups;   /* decode kernel grid size */
-    size_t workspace_bytes;   /* bytes of workspace pa_decode needs (0 if no split) */
+    int32_t scheduled;        /* 1 = device-built work list + persistent grid */
+    int64_t num_workgroups;   /* decode kernel grid size (direct grid), or the
+                                 upper bound on work items (scheduled) */
+    size_t workspace_bytes;   /* bytes of workspace pa_decode needs */
 } pa_decode_plan;
 
 /*
@@ -146,9 +151,10 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
  *                    [0, max_blocks_per_seq * block_size]
  *   scale            the score scale (usually 1/sqrt(head_dim))
  *   out              device, [num_seqs, num_q_heads, head_dim] bfloat16
- *   workspace        device, >= pa_decode_workspace_size(...) bytes when the
- *                    plan splits contexts (may be NULL when it does not);
- *                    scratch, overwritten by each call
+ *   workspace        device, >= pa_decode_workspace_size(...) bytes, 256-byte
+ *                    aligned (may be NULL when that size is 0): the work list
+ *                    and the split-K partials; scratch, overwritten by each
+ *                    call
  *   opts             NULL or tuning options
  * Supported: head_dim in {64, 128}; g in [1, 16]; block_size a power of
  * two in [16, 1024]; block_size * num_kv_heads * head_dim * element size
@@ -172,8 +178,8 @@ int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                        int32_t kv_dtype, const pa_decode_opts* opts, pa_decode_plan* plan);
 
-/* Bytes of workspace pa_decode needs for these sizes (0 when it does not
- * split, or when the sizes are invalid). */
+/* Bytes of workspace pa_decode needs for these sizes (0 when it needs none,
+ * or when the sizes are invalid). */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t kv_dtype, const pa_decode_opts* opts);

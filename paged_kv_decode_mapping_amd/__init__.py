@@ -38,13 +38,13 @@ class PAError(RuntimeError):
 class pa_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("waves_per_group", ctypes.c_int32), ("prefetch_tiles", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class pa_decode_plan(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
                 ("partition_tokens", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
-                ("prefetch_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("prefetch_tiles", ctypes.c_int32), ("scheduled", ctypes.c_int32),
                 ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -83,9 +83,10 @@ def strerror(status: int) -> str:
     return load_library().pa_strerror(int(status)).decode()
 
 
-def _opts(partition_tokens: int = 0, variant="auto", waves: int = 0, prefetch: int = 0) -> pa_decode_opts:
+def _opts(partition_tokens: int = 0, variant="auto", waves: int = 0, prefetch: int = 0,
+          schedule: int = 0) -> pa_decode_opts:
     v = _VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    return pa_decode_opts(int(partition_tokens), v, int(waves), int(prefetch), 0)
+    return pa_decode_opts(int(partition_tokens), v, int(waves), int(prefetch), int(schedule), 0)
 
 
 def _kv_dtype(t) -> int:
@@ -142,9 +143,10 @@ def pa_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v
 
 
 def pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                       kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0) -> dict:
+                       kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0,
+                       schedule=0) -> dict:
     lib = load_library()
-    o = _opts(partition_tokens, variant, waves, prefetch)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule)
     p = pa_decode_plan()
     st = lib.pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, kv_dtype, ctypes.byref(o), ctypes.byref(p))
@@ -152,18 +154,19 @@ def pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size
         raise PAError(st, "pa_decode_get_plan")
     return {"variant": {1: "valu", 2: "mfma"}[p.variant], "waves_per_group": p.waves_per_group,
             "partition_tokens": p.partition_tokens, "num_partitions": p.num_partitions,
-            "prefetch_tiles": p.prefetch_tiles, "num_workgroups": p.num_workgroups,
+            "prefetch_tiles": p.prefetch_tiles, "scheduled": bool(p.scheduled),
+            "num_workgroups": p.num_workgroups,
             "workspace_bytes": p.workspace_bytes}
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
               k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, partition_tokens: int = 0,
-              variant="auto", waves: int = 0, prefetch: int = 0, stream=None):
+              variant="auto", waves: int = 0, prefetch: int = 0, schedule: int = 0, stream=None):
     """Decode step: q [S, Hq, D] bf16 attends through block_tables [S, MB] int32 and
     context_lens [S] int32 over the paged caches [N, bs, Hkv, D]. Returns out [S, Hq, D] bf16.
 
-    `workspace` (a uint8 device tensor) is allocated here when the plan splits
-    contexts and none is passed."""
+    `workspace` (a uint8 device tensor, 256-byte aligned) is allocated here when
+    the plan needs one and none is passed."""
     import torch
     lib = load_library()
     _check(q, "q", torch.bfloat16, 3)
@@ -185,7 +188,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
         _check(out, "out", torch.bfloat16, 3)
         if out.shape != q.shape:
             raise ValueError("out shape")
-    o = _opts(partition_tokens, variant, waves, prefetch)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule)
     need = lib.pa_decode_workspace_size(S, Hq, Hkv, D, bs, MB, kvd, ctypes.byref(o))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -201,8 +204,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                             kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0) -> int:
-    o = _opts(partition_tokens, variant, waves, prefetch)
+                             kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0,
+                             schedule=0) -> int:
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule)
     return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                        block_size, max_blocks_per_seq, kv_dtype,
                                                        ctypes.byref(o)))

@@ -71,207 +71,207 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
     static_assert(NIV >= 1 && kTile % RPI == 0, "tile shape");
 
     extern __shared__ float smem[];
-    const WorkItem wi = decode_work_item(a);
-    if (!wi.active) return;
+    for_each_item(a, [&](const WorkItem& wi) {
+        const int W = (int)(blockDim.x >> 6);
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        const int lane = (int)(threadIdx.x & 63);
+        const int c = lane & 15;
+        const int gq = lane >> 4;
+        const int g = a.group;
+        uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * kTile * RS;
 
-    const int W = (int)(blockDim.x >> 6);
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int lane = (int)(threadIdx.x & 63);
-    const int c = lane & 15;
-    const int gq = lane >> 4;
-    const int g = a.group;
-    uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * kTile * RS;
-
-    // Q^T operands: MFMA j takes d = dq(j) + 0..7 of head c, where dq(j) is
-    // the d offset the lane's K operand of MFMA j holds.
-    bf16x8 qb[NQK];
-#pragma unroll
-    for (int j = 0; j < NQK; ++j) {
-        const int d0 = FP8 ? (64 * (j >> 1) + 16 * gq + 8 * (j & 1)) : (32 * j + 8 * gq);
-        u32x4 w = u32x4{0u, 0u, 0u, 0u};
-        if (c < g) w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + c) * D + d0);
-        qb[j] = __builtin_bit_cast(bf16x8, w);
-    }
-
-    float m = -INFINITY;  // running max of head c (log2 units), same in all four lane groups
-    float l = 0.0f;       // running sum over this lane's tokens
-    f32x4 o[NPV];
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int span = wi.t_end - wi.t_begin;
-    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
-    const uint32_t head_off = (uint32_t)wi.kvh * a.head_bytes;
-    const uint32_t koff = (uint32_t)c * a.slot_bytes + head_off + 16u * (uint32_t)gq;
-    const uint32_t voff = (uint32_t)(lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
-    const int bs_mask = (1 << a.block_size_log2) - 1;
-    const float qk = a.qk_scale_log2;
-
-    u32x4 kb[NB][NIK], vb[NB][NIV];  // ring of NB tiles: NB - 1 in flight while one is consumed
-
-    // Loads for tile t. A tile past the end (the prefetch after the last
-    // one) still issues its loads, against a zero-byte buffer: they return
-    // zeros without touching memory, and every path through the loop keeps
-    // the same number of loads in flight, so the wait before a tile's use
-    // never has to drain the prefetch behind it.
-    auto issue = [&](int t, u32x4 (&kb)[NIK], u32x4 (&vb)[NIV]) {
-        const bool live = t < ntiles;
-        const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
-        const int64_t blk = physical_block(a, wi.seq, t0);
-        const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
-        const uint32_t nbytes = live ? a.block_bytes : 0u;
-        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
-        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
-#pragma unroll
-        for (int i = 0; i < NIK; ++i) kb[i] = buf_load_b128(rk, koff + row0 + 64u * i);
-#pragma unroll
-        for (int i = 0; i < NIV; ++i) vb[i] = buf_load_b128(rv, voff + row0 + (uint32_t)(i * RPI) * a.slot_bytes);
-    };
-
-    auto consume = [&](int t, const u32x4 (&kb)[NIK], const u32x4 (&vb)[NIV]) {
-        const int t0 = wi.t_begin + t * kTile;
-        const int valid = wi.t_end - t0;
-        const bool full = valid >= kTile;
-
-        // V rows -> LDS as bf16 (rows past the context are zeroed: their
-        // weight is 0, but 0 * NaN would not be).
-#pragma unroll
-        for (int i = 0; i < NIV; ++i) {
-            const int row = i * RPI + lane / LPR;
-            u32x4 w = vb[i];
-            if (!full && row >= valid) w = u32x4{0u, 0u, 0u, 0u};
-            if constexpr (!FP8) {
-                *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 8) = w;
-            } else {
-                u32x4 lo, hi;
-                fp8x16_to_bf16(w, lo, hi);
-                *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16) = lo;
-                *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16 + 8) = hi;
-            }
-        }
-
-        // S = K Q^T
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Q^T operands: MFMA j takes d = dq(j) + 0..7 of head c, where dq(j) is
+        // the d offset the lane's K operand of MFMA j holds.
+        bf16x8 qb[NQK];
 #pragma unroll
         for (int j = 0; j < NQK; ++j) {
-            bf16x8 ka;
-            if constexpr (!FP8) {
-                ka = __builtin_bit_cast(bf16x8, kb[j]);
-            } else {
-                u32x4 lo, hi;
-                fp8x16_to_bf16(kb[j >> 1], lo, hi);
-                ka = __builtin_bit_cast(bf16x8, (j & 1) ? hi : lo);
+            const int d0 = FP8 ? (64 * (j >> 1) + 16 * gq + 8 * (j & 1)) : (32 * j + 8 * gq);
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (c < g) w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + c) * D + d0);
+            qb[j] = __builtin_bit_cast(bf16x8, w);
+        }
+
+        float m = -INFINITY;  // running max of head c (log2 units), same in all four lane groups
+        float l = 0.0f;       // running sum over this lane's tokens
+        f32x4 o[NPV];
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        const int span = wi.t_end - wi.t_begin;
+        const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
+        const uint32_t head_off = (uint32_t)wi.kvh * a.head_bytes;
+        const uint32_t koff = (uint32_t)c * a.slot_bytes + head_off + 16u * (uint32_t)gq;
+        const uint32_t voff = (uint32_t)(lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
+        const int bs_mask = (1 << a.block_size_log2) - 1;
+        const float qk = a.qk_scale_log2;
+
+        u32x4 kb[NB][NIK], vb[NB][NIV];  // ring of NB tiles: NB - 1 in flight while one is consumed
+
+        // Loads for tile t. A tile past the end (the prefetch after the last
+        // one) still issues its loads, against a zero-byte buffer: they return
+        // zeros without touching memory, and every path through the loop keeps
+        // the same number of loads in flight, so the wait before a tile's use
+        // never has to drain the prefetch behind it.
+        auto issue = [&](int t, u32x4 (&kb)[NIK], u32x4 (&vb)[NIV]) {
+            const bool live = t < ntiles;
+            const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
+            const int64_t blk = physical_block(a, wi.seq, t0);
+            const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
+            const uint32_t nbytes = live ? a.block_bytes : 0u;
+            const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
+            const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
+#pragma unroll
+            for (int i = 0; i < NIK; ++i) kb[i] = buf_load_b128(rk, koff + row0 + 64u * i);
+#pragma unroll
+            for (int i = 0; i < NIV; ++i) vb[i] = buf_load_b128(rv, voff + row0 + (uint32_t)(i * RPI) * a.slot_bytes);
+        };
+
+        auto consume = [&](int t, const u32x4 (&kb)[NIK], const u32x4 (&vb)[NIV]) {
+            const int t0 = wi.t_begin + t * kTile;
+            const int valid = wi.t_end - t0;
+            const bool full = valid >= kTile;
+
+            // V rows -> LDS as bf16 (rows past the context are zeroed: their
+            // weight is 0, but 0 * NaN would not be).
+#pragma unroll
+            for (int i = 0; i < NIV; ++i) {
+                const int row = i * RPI + lane / LPR;
+                u32x4 w = vb[i];
+                if (!full && row >= valid) w = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (!FP8) {
+                    *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 8) = w;
+                } else {
+                    u32x4 lo, hi;
+                    fp8x16_to_bf16(w, lo, hi);
+                    *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16) = lo;
+                    *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16 + 8) = hi;
+                }
             }
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j], s, 0, 0, 0);
-        }
 
-        // online softmax for head c over tokens 4*gq + r
-        float x[4];
+            // S = K Q^T
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = (!full && 4 * gq + r >= valid) ? -INFINITY : s[r] * qk;
-        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mx = fmaxf(mx, xor_shfl(mx, 16));
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m - ms);
-        m = m_new;
-        bf16x4 pb;
-        float psum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
-            pb[r] = b;
-            psum += (float)b;
-        }
-        l = fmaf(l, alpha, psum);
-#pragma unroll
-        for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+            for (int j = 0; j < NQK; ++j) {
+                bf16x8 ka;
+                if constexpr (!FP8) {
+                    ka = __builtin_bit_cast(bf16x8, kb[j]);
+                } else {
+                    u32x4 lo, hi;
+                    fp8x16_to_bf16(kb[j >> 1], lo, hi);
+                    ka = __builtin_bit_cast(bf16x8, (j & 1) ? hi : lo);
+                }
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j], s, 0, 0, 0);
+            }
 
-        // O^T += V^T P^T
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // online softmax for head c over tokens 4*gq + r
+            float x[4];
 #pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const uint16_t* src = vs + (4 * gq) * RS + 16 * j + c;
-            const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[RS] << 16);
-            const uint32_t v23 = (uint32_t)src[2 * RS] | ((uint32_t)src[3 * RS] << 16);
-            const bf16x4 va = __builtin_bit_cast(bf16x4, u32x2{v01, v23});
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
+            for (int r = 0; r < 4; ++r) x[r] = (!full && 4 * gq + r >= valid) ? -INFINITY : s[r] * qk;
+            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            mx = fmaxf(mx, xor_shfl(mx, 16));
+            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float m_new = fmaxf(m, mx);
+            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m - ms);
+            m = m_new;
+            bf16x4 pb;
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
+                pb[r] = b;
+                psum += (float)b;
+            }
+            l = fmaf(l, alpha, psum);
+#pragma unroll
+            for (int j = 0; j < NPV; ++j) o[j] *= alpha;
 
-    if (ntiles > 0) {
-        // The ring is unrolled so that every buffer index is a constant.
-        // sched_barrier keeps the compiler from sinking the prefetch below
-        // the waits of the tile being consumed.
-        int t = wave;
+            // O^T += V^T P^T
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
-        bool go = t < ntiles;
-        while (go) {
+            for (int j = 0; j < NPV; ++j) {
+                const uint16_t* src = vs + (4 * gq) * RS + 16 * j + c;
+                const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[RS] << 16);
+                const uint32_t v23 = (uint32_t)src[2 * RS] | ((uint32_t)src[3 * RS] << 16);
+                const bf16x4 va = __builtin_bit_cast(bf16x4, u32x2{v01, v23});
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+
+        if (ntiles > 0) {
+            // The ring is unrolled so that every buffer index is a constant.
+            // sched_barrier keeps the compiler from sinking the prefetch below
+            // the waits of the tile being consumed.
+            int t = wave;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (go) {
-                    issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    consume(t, kb[b], vb[b]);
-                    t += W;
-                    go = t < ntiles;
+            for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
+            bool go = t < ntiles;
+            while (go) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (go) {
+                        issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        consume(t, kb[b], vb[b]);
+                        t += W;
+                        go = t < ntiles;
+                    }
                 }
             }
         }
-    }
 
-    // the four lane groups hold disjoint token subsets of the same state
-    l += xor_shfl(l, 16);
-    l += xor_shfl(l, 32);
+        // the four lane groups hold disjoint token subsets of the same state
+        l += xor_shfl(l, 16);
+        l += xor_shfl(l, 32);
 
-    __syncthreads();  // V staging is dead; reuse LDS for the combine
-    float* sm_ml = smem;
-    float* sm_o = smem + W * g * 2;
-    if (c < g) {
-        if (gq == 0) {
-            sm_ml[(wave * g + c) * 2] = m;
-            sm_ml[(wave * g + c) * 2 + 1] = l;
+        __syncthreads();  // V staging is dead; reuse LDS for the combine
+        float* sm_ml = smem;
+        float* sm_o = smem + W * g * 2;
+        if (c < g) {
+            if (gq == 0) {
+                sm_ml[(wave * g + c) * 2] = m;
+                sm_ml[(wave * g + c) * 2 + 1] = l;
+            }
+#pragma unroll
+            for (int j = 0; j < NPV; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm_o[(wave * g + c) * D + 16 * j + 4 * gq + r] = o[j][r];
         }
-#pragma unroll
-        for (int j = 0; j < NPV; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm_o[(wave * g + c) * D + 16 * j + 4 * gq + r] = o[j][r];
-    }
-    __syncthreads();
-    combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+        __syncthreads();
+        combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+    });
 }
 
 template <int D, bool FP8, int NB>
-hipError_t launch_d(const DecodeArgs& a, int waves, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
-    const dim3 block((unsigned)(64 * waves));
-    const size_t stage = (size_t)waves * kTile * (D + 8) * sizeof(uint16_t);
-    const size_t comb = (size_t)waves * a.group * (D + 2) * sizeof(float);
+hipError_t launch_d(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
+    const dim3 block((unsigned)(64 * ls.waves));
+    const size_t stage = (size_t)ls.waves * kTile * (D + 8) * sizeof(uint16_t);
+    const size_t comb = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
     const size_t lds = stage > comb ? stage : comb;
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB>), grid, block, lds, s, a);
+    const auto kernel = pa_decode_mfma_kernel<D, FP8, NB>;
+    const int64_t nwg = grid_size(reinterpret_cast<const void*>(kernel), a, ls, lds);
+    if (nwg <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), block, lds, s, a);
     return hipGetLastError();
 }
 
 template <int D, bool FP8>
-hipError_t launch_nb(const DecodeArgs& a, int waves, int depth, hipStream_t s) {
-    if (depth <= 2) return launch_d<D, FP8, 2>(a, waves, s);
-    if (depth == 3) return launch_d<D, FP8, 3>(a, waves, s);
-    return launch_d<D, FP8, 4>(a, waves, s);
+hipError_t launch_nb(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
+    if (ls.depth <= 2) return launch_d<D, FP8, 2>(a, ls, s);
+    if (ls.depth == 3) return launch_d<D, FP8, 3>(a, ls, s);
+    return launch_d<D, FP8, 4>(a, ls, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, int waves, int depth, hipStream_t s) {
-    if (head_dim == 64)
-        return fp8 ? launch_nb<64, true>(a, waves, depth, s) : launch_nb<64, false>(a, waves, depth, s);
-    return fp8 ? launch_nb<128, true>(a, waves, depth, s) : launch_nb<128, false>(a, waves, depth, s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s) {
+    if (head_dim == 64) return fp8 ? launch_nb<64, true>(a, ls, s) : launch_nb<64, false>(a, ls, s);
+    return fp8 ? launch_nb<128, true>(a, ls, s) : launch_nb<128, false>(a, ls, s);
 }
 
 }  // namespace pa

@@ -66,208 +66,213 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
     static_assert(NI >= 1 && kTile % RPI == 0, "tile shape");
 
     extern __shared__ float smem[];
-    const WorkItem wi = decode_work_item(a);
-    if (!wi.active) return;
+    for_each_item(a, [&](const WorkItem& wi) {
+        const int W = (int)(blockDim.x >> 6);
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        const int lane = (int)(threadIdx.x & 63);
+        const int r_in = lane / LPR;
+        const int c = lane % LPR;
+        const int g = a.group;
 
-    const int W = (int)(blockDim.x >> 6);
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int lane = (int)(threadIdx.x & 63);
-    const int r_in = lane / LPR;
-    const int c = lane % LPR;
-    const int g = a.group;
-
-    // q for this lane's EPL dims of each head of the group, as float.
-    float qf[GM][EPL];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        if (h < g) {
-            const uint16_t* qp = a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + h) * D + c * EPL;
-#pragma unroll
-            for (int e = 0; e < EPL; e += 8) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(qp + e);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qf[h][e + 2 * i] = bf16_lo(w[i]);
-                    qf[h][e + 2 * i + 1] = bf16_hi(w[i]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) qf[h][e] = 0.0f;
-        }
-    }
-
-    float m[GM], l[GM], o[GM][EPL];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
-    }
-
-    const int span = wi.t_end - wi.t_begin;
-    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
-    const uint32_t lane_off = (uint32_t)r_in * a.slot_bytes + (uint32_t)wi.kvh * a.head_bytes + (uint32_t)c * 16u;
-    const int bs_mask = (1 << a.block_size_log2) - 1;
-    const float qk = a.qk_scale_log2;
-
-    u32x4 kb[NB][NI], vb[NB][NI];  // ring of NB tiles: NB - 1 in flight while one is consumed
-
-    // Loads for tile t. A tile past the end (the prefetch after the last
-    // one) still issues its loads, against a zero-byte buffer: they return
-    // zeros without touching memory, and every path through the loop keeps
-    // the same number of loads in flight, so the wait before a tile's use
-    // never has to drain the prefetch behind it.
-    auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
-        const bool live = t < ntiles;
-        const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
-        const int64_t blk = physical_block(a, wi.seq, t0);
-        const uint32_t row0 = (uint32_t)(t0 & bs_mask);
-        const uint32_t nbytes = live ? a.block_bytes : 0u;
-        const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
-        const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint32_t off = lane_off + (row0 + (uint32_t)(i * RPI)) * a.slot_bytes;
-            kb[i] = buf_load_b128(rk, off);
-            vb[i] = buf_load_b128(rv, off);
-        }
-    };
-
-    auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
-        const int t0 = wi.t_begin + t * kTile;
-        const int valid = wi.t_end - t0;
-        const bool full = valid >= kTile;
-        float x[NI][GM];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            float kf[EPL];
-            unpack<FP8, EPL>(kb[i], kf);
-            const bool dead = !full && (i * RPI + r_in) >= valid;
-#pragma unroll
-            for (int h = 0; h < GM; ++h) {
-                float s = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) s = fmaf(qf[h][e], kf[e], s);
-                s = group_sum<LPR>(s);
-                x[i][h] = dead ? -INFINITY : s * qk;
-            }
-        }
-        float p[NI][GM];
+        // q for this lane's EPL dims of each head of the group, as float.
+        float qf[GM][EPL];
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-            float mx = x[0][h];
+            if (h < g) {
+                const uint16_t* qp = a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + h) * D + c * EPL;
 #pragma unroll
-            for (int i = 1; i < NI; ++i) mx = fmaxf(mx, x[i][h]);
-            const float m_new = fmaxf(m[h], mx);
-            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m[h] - ms);
-            m[h] = m_new;
-            float lsum = 0.0f;
+                for (int e = 0; e < EPL; e += 8) {
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(qp + e);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        qf[h][e + 2 * i] = bf16_lo(w[i]);
+                        qf[h][e + 2 * i + 1] = bf16_hi(w[i]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) qf[h][e] = 0.0f;
+            }
+        }
+
+        float m[GM], l[GM], o[GM][EPL];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            m[h] = -INFINITY;
+            l[h] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
+        }
+
+        const int span = wi.t_end - wi.t_begin;
+        const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
+        const uint32_t lane_off = (uint32_t)r_in * a.slot_bytes + (uint32_t)wi.kvh * a.head_bytes + (uint32_t)c * 16u;
+        const int bs_mask = (1 << a.block_size_log2) - 1;
+        const float qk = a.qk_scale_log2;
+
+        u32x4 kb[NB][NI], vb[NB][NI];  // ring of NB tiles: NB - 1 in flight while one is consumed
+
+        // Loads for tile t. A tile past the end (the prefetch after the last
+        // one) still issues its loads, against a zero-byte buffer: they return
+        // zeros without touching memory, and every path through the loop keeps
+        // the same number of loads in flight, so the wait before a tile's use
+        // never has to drain the prefetch behind it.
+        auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
+            const bool live = t < ntiles;
+            const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
+            const int64_t blk = physical_block(a, wi.seq, t0);
+            const uint32_t row0 = (uint32_t)(t0 & bs_mask);
+            const uint32_t nbytes = live ? a.block_bytes : 0u;
+            const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
+            const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                p[i][h] = fast_exp2(x[i][h] - ms);
-                lsum += p[i][h];
+                const uint32_t off = lane_off + (row0 + (uint32_t)(i * RPI)) * a.slot_bytes;
+                kb[i] = buf_load_b128(rk, off);
+                vb[i] = buf_load_b128(rv, off);
             }
-            l[h] = fmaf(l[h], alpha, lsum);
+        };
+
+        auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
+            const int t0 = wi.t_begin + t * kTile;
+            const int valid = wi.t_end - t0;
+            const bool full = valid >= kTile;
+            float x[NI][GM];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-        }
+            for (int i = 0; i < NI; ++i) {
+                float kf[EPL];
+                unpack<FP8, EPL>(kb[i], kf);
+                const bool dead = !full && (i * RPI + r_in) >= valid;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            u32x4 w = vb[i];
-            if (!full && (i * RPI + r_in) >= valid) w = u32x4{0u, 0u, 0u, 0u};
-            float vf[EPL];
-            unpack<FP8, EPL>(w, vf);
+                for (int h = 0; h < GM; ++h) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) s = fmaf(qf[h][e], kf[e], s);
+                    s = group_sum<LPR>(s);
+                    x[i][h] = dead ? -INFINITY : s * qk;
+                }
+            }
+            float p[NI][GM];
 #pragma unroll
             for (int h = 0; h < GM; ++h) {
+                float mx = x[0][h];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[i][h], vf[e], o[h][e]);
+                for (int i = 1; i < NI; ++i) mx = fmaxf(mx, x[i][h]);
+                const float m_new = fmaxf(m[h], mx);
+                const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+                const float alpha = fast_exp2(m[h] - ms);
+                m[h] = m_new;
+                float lsum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    p[i][h] = fast_exp2(x[i][h] - ms);
+                    lsum += p[i][h];
+                }
+                l[h] = fmaf(l[h], alpha, lsum);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
             }
-        }
-    };
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                u32x4 w = vb[i];
+                if (!full && (i * RPI + r_in) >= valid) w = u32x4{0u, 0u, 0u, 0u};
+                float vf[EPL];
+                unpack<FP8, EPL>(w, vf);
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p[i][h], vf[e], o[h][e]);
+                }
+            }
+        };
 
-    if (ntiles > 0) {
-        // The ring is unrolled so that every buffer index is a constant.
-        // sched_barrier keeps the compiler from sinking the prefetch below
-        // the waits of the tile being consumed.
-        int t = wave;
+        if (ntiles > 0) {
+            // The ring is unrolled so that every buffer index is a constant.
+            // sched_barrier keeps the compiler from sinking the prefetch below
+            // the waits of the tile being consumed.
+            int t = wave;
 #pragma unroll
-        for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
-        bool go = t < ntiles;
-        while (go) {
+            for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
+            bool go = t < ntiles;
+            while (go) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (go) {
-                    issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    consume(t, kb[b], vb[b]);
-                    t += W;
-                    go = t < ntiles;
+                for (int b = 0; b < NB; ++b) {
+                    if (go) {
+                        issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        consume(t, kb[b], vb[b]);
+                        t += W;
+                        go = t < ntiles;
+                    }
                 }
             }
         }
-    }
 
-    // Combine the RPI row states of the wave (lanes differing in row bits).
-    float* sm_ml = smem;
-    float* sm_o = smem + W * g * 2;
+        // Combine the RPI row states of the wave (lanes differing in row bits).
+        float* sm_ml = smem;
+        float* sm_o = smem + W * g * 2;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        float M = m[h];
+        for (int h = 0; h < GM; ++h) {
+            float M = m[h];
 #pragma unroll
-        for (int mask = LPR; mask < 64; mask <<= 1) M = fmaxf(M, xor_shfl(M, mask));
-        const float f = state_weight(m[h], M);
-        float lh = l[h] * f;
+            for (int mask = LPR; mask < 64; mask <<= 1) M = fmaxf(M, xor_shfl(M, mask));
+            const float f = state_weight(m[h], M);
+            float lh = l[h] * f;
 #pragma unroll
-        for (int mask = LPR; mask < 64; mask <<= 1) lh += xor_shfl(lh, mask);
+            for (int mask = LPR; mask < 64; mask <<= 1) lh += xor_shfl(lh, mask);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float v = o[h][e] * f;
+            for (int e = 0; e < EPL; ++e) {
+                float v = o[h][e] * f;
 #pragma unroll
-            for (int mask = LPR; mask < 64; mask <<= 1) v += xor_shfl(v, mask);
-            o[h][e] = v;
-        }
-        if (h < g) {
-            if (lane == 0) {
-                sm_ml[(wave * g + h) * 2] = M;
-                sm_ml[(wave * g + h) * 2 + 1] = lh;
+                for (int mask = LPR; mask < 64; mask <<= 1) v += xor_shfl(v, mask);
+                o[h][e] = v;
             }
-            if (r_in == 0) {
+            if (h < g) {
+                if (lane == 0) {
+                    sm_ml[(wave * g + h) * 2] = M;
+                    sm_ml[(wave * g + h) * 2 + 1] = lh;
+                }
+                if (r_in == 0) {
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) sm_o[(wave * g + h) * D + c * EPL + e] = o[h][e];
+                    for (int e = 0; e < EPL; ++e) sm_o[(wave * g + h) * D + c * EPL + e] = o[h][e];
+                }
             }
         }
-    }
-    __syncthreads();
-    combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+        __syncthreads();
+        combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+    });
 }
 
-template <int D, bool FP8, int GM>
-hipError_t launch_g(const DecodeArgs& a, int waves, int depth, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
-    const dim3 block((unsigned)(64 * waves));
-    const size_t lds = (size_t)waves * a.group * (D + 2) * sizeof(float);
-    if (depth <= 2) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, 2>), grid, block, lds, s, a);
-    else if (depth == 3) hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, 3>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, 4>), grid, block, lds, s, a);
+template <int D, bool FP8, int GM, int NB>
+hipError_t launch_k(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
+    const dim3 block((unsigned)(64 * ls.waves));
+    const size_t lds = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
+    const auto kernel = pa_decode_valu_kernel<D, FP8, GM, NB>;
+    const int64_t nwg = grid_size(reinterpret_cast<const void*>(kernel), a, ls, lds);
+    if (nwg <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), block, lds, s, a);
     return hipGetLastError();
 }
 
+template <int D, bool FP8, int GM>
+hipError_t launch_g(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
+    if (ls.depth <= 2) return launch_k<D, FP8, GM, 2>(a, ls, s);
+    if (ls.depth == 3) return launch_k<D, FP8, GM, 3>(a, ls, s);
+    return launch_k<D, FP8, GM, 4>(a, ls, s);
+}
+
 template <int D, bool FP8>
-hipError_t launch_d(const DecodeArgs& a, int waves, int depth, hipStream_t s) {
-    if (a.group <= 1) return launch_g<D, FP8, 1>(a, waves, depth, s);
-    if (a.group <= 2) return launch_g<D, FP8, 2>(a, waves, depth, s);
-    return launch_g<D, FP8, 4>(a, waves, depth, s);
+hipError_t launch_d(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
+    if (a.group <= 1) return launch_g<D, FP8, 1>(a, ls, s);
+    if (a.group <= 2) return launch_g<D, FP8, 2>(a, ls, s);
+    return launch_g<D, FP8, 4>(a, ls, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, int waves, int depth, hipStream_t s) {
-    if (head_dim == 64)
-        return fp8 ? launch_d<64, true>(a, waves, depth, s) : launch_d<64, false>(a, waves, depth, s);
-    return fp8 ? launch_d<128, true>(a, waves, depth, s) : launch_d<128, false>(a, waves, depth, s);
+hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s) {
+    if (head_dim == 64) return fp8 ? launch_d<64, true>(a, ls, s) : launch_d<64, false>(a, ls, s);
+    return fp8 ? launch_d<128, true>(a, ls, s) : launch_d<128, false>(a, ls, s);
 }
 
 }  // namespace pa

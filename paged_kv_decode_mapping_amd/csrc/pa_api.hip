@@ -48,10 +48,14 @@ struct Plan {
     int depth = 3;  // register-ring tiles per wave (prefetch distance + 1)
     int partition_tokens = 0;
     int num_partitions = 1;
-    int64_t num_workgroups = 0;
-    size_t ml_bytes = 0;   // split partial (m, l) array
-    size_t workspace = 0;  // total workspace bytes
+    bool scheduled = true;
+    int64_t num_workgroups = 0;  // direct grid size, or the item bound when scheduled
+    // workspace layout (byte offsets); total = workspace
+    size_t items_off = 0, ml_off = 0, o_off = 0;
+    size_t workspace = 0;
 };
+
+constexpr size_t kHeaderBytes = 256;  // scheduled: item count, queue counter
 
 int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB,
                 int32_t kv_dtype) {
@@ -120,11 +124,21 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     if (p.num_partitions < 1) p.num_partitions = 1;
     p.num_workgroups = units * p.num_partitions;
     if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if (o.schedule < -1 || o.schedule > 1) return PA_ERR_SHAPE;
+    // Scheduled items pack (partition << 16 | KV head) into 32 bits.
+    p.scheduled = o.schedule != -1 && p.num_partitions < 32768 && Hkv < 65536;
+    size_t off = 0;
+    if (p.scheduled) {
+        p.items_off = kHeaderBytes;
+        off = p.items_off + align_up((size_t)p.num_workgroups * 2 * sizeof(int32_t), 256);
+    }
     if (p.num_partitions > 1) {
         const size_t rows = (size_t)S * Hq * p.num_partitions;
-        p.ml_bytes = align_up(rows * 2 * sizeof(float), 256);
-        p.workspace = p.ml_bytes + rows * D * sizeof(float);
+        p.ml_off = off;
+        p.o_off = off + align_up(rows * 2 * sizeof(float), 256);
+        off = p.o_off + rows * D * sizeof(float);
     }
+    p.workspace = off;
     *plan = p;
     return PA_OK;
 }
@@ -179,7 +193,7 @@ int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     plan->partition_tokens = p.partition_tokens;
     plan->num_partitions = p.num_partitions;
     plan->prefetch_tiles = p.depth - 1;
-    plan->reserved = 0;
+    plan->scheduled = p.scheduled ? 1 : 0;
     plan->num_workgroups = p.num_workgroups;
     plan->workspace_bytes = p.workspace;
     return PA_OK;
@@ -215,9 +229,14 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return PA_ERR_ALIGN;
-    if (p.num_partitions > 1) {
+    if (p.workspace > 0) {
         if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+    }
+    int cus = 0;
+    if (p.scheduled) {
+        cus = current_cu_count();
+        if (cus <= 0) return PA_ERR_DEVICE;
     }
     const int64_t esz = fp8 ? 1 : 2;
     pa::DecodeArgs a{};
@@ -227,9 +246,15 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = static_cast<uint16_t*>(out);
+    char* ws = static_cast<char*>(workspace);
     if (p.num_partitions > 1) {
-        a.part_ml = static_cast<float*>(workspace);
-        a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ml_bytes);
+        a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
+        a.part_o = reinterpret_cast<float*>(ws + p.o_off);
+    }
+    if (p.scheduled) {
+        a.item_count = reinterpret_cast<int*>(ws);
+        a.queue = reinterpret_cast<int*>(ws) + 1;
+        a.items = reinterpret_cast<const int2*>(ws + p.items_off);
     }
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
@@ -246,8 +271,23 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, p.waves, p.depth, s)
-                                                : pa::launch_decode_valu(a, head_dim, fp8, p.waves, p.depth, s);
+    hipError_t e;
+    if (p.scheduled) {
+        pa::ScheduleArgs sa{};
+        sa.context_lens = context_lens;
+        sa.items = reinterpret_cast<int2*>(ws + p.items_off);
+        sa.item_count = reinterpret_cast<int*>(ws);
+        sa.queue = a.queue;
+        sa.num_seqs = num_seqs;
+        sa.num_kv_heads = num_kv_heads;
+        sa.partition_tokens = p.partition_tokens;
+        sa.max_context = max_blocks_per_seq * block_size;
+        e = pa::launch_schedule(sa, s);
+        if (e != hipSuccess) return PA_ERR_LAUNCH;
+    }
+    const pa::LaunchShape ls{p.waves, p.depth, cus, p.scheduled ? p.num_workgroups : 0};
+    e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, ls, s)
+                                     : pa::launch_decode_valu(a, head_dim, fp8, ls, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
     if (p.num_partitions > 1) {
         pa::MergeArgs m{};

@@ -65,25 +65,55 @@ struct WorkItem {
     bool active;          // false: nothing to do (empty partition)
 };
 
-__device__ __forceinline__ WorkItem decode_work_item(const DecodeArgs& a) {
+__device__ __forceinline__ WorkItem make_work_item(const DecodeArgs& a, int seq, int kvh, int part) {
     WorkItem w;
-    const int bid = (int)blockIdx.x;
-    const int P = a.num_partitions;
-    w.part = bid % P;
-    const int unit = bid / P;
-    w.kvh = unit % a.num_kv_heads;
-    w.seq = unit / a.num_kv_heads;
-    int ctx = a.context_lens[w.seq];
+    w.seq = seq;
+    w.kvh = kvh;
+    w.part = part;
+    int ctx = a.context_lens[seq];
     const int cap = a.max_blocks_per_seq << a.block_size_log2;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     const int parts_used = (ctx + a.partition_tokens - 1) / a.partition_tokens;
-    w.t_begin = w.part * a.partition_tokens;
+    w.t_begin = part * a.partition_tokens;
     w.t_end = min(w.t_begin + a.partition_tokens, ctx);
     // Partition 0 always runs, so that a zero-length context still gets its
     // (all-zero) output row.
-    w.active = (w.part < parts_used) || (w.part == 0);
-    w.final_out = (P == 1) || (parts_used <= 1);
+    w.active = (part < parts_used) || (part == 0);
+    w.final_out = (a.num_partitions == 1) || (parts_used <= 1);
     return w;
+}
+
+// Direct grid: workgroup b takes item (unit = b / P, part = b % P).
+__device__ __forceinline__ WorkItem decode_work_item(const DecodeArgs& a) {
+    const int bid = (int)blockIdx.x;
+    const int P = a.num_partitions;
+    const int unit = bid / P;
+    return make_work_item(a, unit / a.num_kv_heads, unit % a.num_kv_heads, bid % P);
+}
+
+// Runs `body(item)` for every work item of this workgroup: the one its block
+// index names (direct grid), or, when a schedule was built, items pulled
+// from the device queue until it is empty (persistent grid). `body` must be
+// called by the whole workgroup; a barrier separates consecutive items, so
+// LDS can be reused.
+template <class Body>
+__device__ __forceinline__ void for_each_item(const DecodeArgs& a, Body&& body) {
+    if (a.items == nullptr) {
+        const WorkItem wi = decode_work_item(a);
+        if (wi.active) body(wi);
+        return;
+    }
+    __shared__ int s_next;
+    const int count = *a.item_count;
+    for (;;) {
+        if (threadIdx.x == 0) s_next = atomicAdd(a.queue, 1);
+        __syncthreads();
+        const int it = s_next;
+        __syncthreads();
+        if (it >= count) break;
+        const int2 item = a.items[it];
+        body(make_work_item(a, item.x, item.y & 0xffff, item.y >> 16));
+    }
 }
 
 // Physical block of a token, clamped into the pool so that a bad table entry

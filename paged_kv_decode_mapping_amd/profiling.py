@@ -43,10 +43,10 @@ def _find(d: str, suffix: str) -> str:
 
 
 def _short(name: str) -> str:
-    n = name.split("(")[0]
-    for p in ("void ", "pa::(anonymous namespace)::", "pa::"):
+    n = name
+    for p in ("void ", "(anonymous namespace)::", "pa::"):
         n = n.replace(p, "")
-    return n.strip()
+    return n.split("(")[0].strip()
 
 
 def stats(d: str) -> list:
@@ -91,8 +91,9 @@ def cmd_traffic(a) -> None:
                 return k, v[counter]
         raise KeyError(f"{key_sub} / {counter} not in the counter CSV: {list(cs)}")
 
-    # the copy kernel is the first non-pa kernel in the run
-    copy_name = next(k for k in fetch if "pa_" not in k)
+    # the copy kernel: the non-pa kernel that both reads and writes (a fill
+    # only writes)
+    copy_name = next(k for k in fetch if "pa_" not in k and "Fill" not in k and "copyBuffer" not in k)
     cf = fetch[copy_name]["FETCH_SIZE"][0]
     cw = write[copy_name]["WRITE_SIZE"][0]
     f_scale = a.copy_bytes / cf

@@ -66,7 +66,7 @@ A = 0x10000
 
 def _decode(lib, **kw):
     args = dict(q=A, k=A, v=A, bt=A, cl=A, scale=0.125, out=A, S=4, Hq=8, Hkv=2, D=64, bs=16, MB=7, N=32,
-                kvd=1, ks=1.0, vs=1.0, ws=None, wsb=0, opts=pa._opts(partition_tokens=-1))
+                kvd=1, ks=1.0, vs=1.0, ws=None, wsb=0, opts=pa._opts(partition_tokens=-1, schedule=-1))
     args.update(kw)
     o = args["opts"]
     return lib.pa_decode(args["q"], args["k"], args["v"], args["bt"], args["cl"], args["scale"], args["out"],
@@ -81,9 +81,11 @@ def _decode(lib, **kw):
     (dict(N=0), -2), (dict(q=None), -1), (dict(bt=None), -1), (dict(out=A + 8), -4), (dict(k=A + 2), -4),
     (dict(kvd=2, ks=0.0), -5), (dict(kvd=2, vs=float("nan")), -5), (dict(scale=float("inf")), -2),
     (dict(opts=pa._opts(partition_tokens=24)), -2), (dict(opts=pa._opts(waves=3)), -2),
-    (dict(opts=pa._opts(partition_tokens=32)), -6), (dict(opts=pa._opts(prefetch=4)), -2),
+    (dict(opts=pa._opts(partition_tokens=32, schedule=-1)), -6), (dict(opts=pa._opts(prefetch=4)), -2),
     (dict(opts=pa._opts(prefetch=-1)), -2), (dict(Hq=16, Hkv=2, opts=pa._opts(variant="valu")), -3),
-    (dict(opts=pa._opts(partition_tokens=32), ws=A, wsb=16), -6),
+    (dict(opts=pa._opts(partition_tokens=32, schedule=-1), ws=A, wsb=16), -6),
+    (dict(opts=pa._opts(partition_tokens=-1, schedule=1)), -6), (dict(opts=pa._opts(partition_tokens=-1, schedule=2)), -2),
+    (dict(opts=pa._opts(partition_tokens=-1, schedule=1), ws=A + 16, wsb=1 << 20), -4),
 ])
 def test_decode_rejects_bad_arguments_without_launching(lib, kw, code):
     assert _decode(lib, **kw) == code
@@ -93,18 +95,27 @@ def test_decode_zero_sequences_is_a_no_op(lib):
     assert _decode(lib, S=0, q=None, out=None) == 0
 
 
+def _align(x, a=256):
+    return -(-x // a) * a
+
+
 def test_plan_with_explicit_partitions(lib):
-    p = pa.pa_decode_get_plan(128, 32, 8, 128, 16, 256, partition_tokens=512, variant="valu", waves=4)
-    assert p["num_partitions"] == 8 and p["partition_tokens"] == 512
-    assert p["num_workgroups"] == 128 * 8 * 8
-    rows = 128 * 32 * 8
-    ml = -(-rows * 8 // 256) * 256
-    assert p["workspace_bytes"] == ml + rows * 128 * 4
+    S, Hq, Hkv, D = 128, 32, 8, 128
+    p = pa.pa_decode_get_plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4, schedule=-1)
+    assert p["num_partitions"] == 8 and p["partition_tokens"] == 512 and not p["scheduled"]
+    assert p["num_workgroups"] == S * Hkv * 8
+    rows = S * Hq * 8
+    assert p["workspace_bytes"] == _align(rows * 8) + rows * D * 4
     assert p["variant"] == "valu" and p["prefetch_tiles"] == 2
-    p1 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, prefetch=3)
+    # scheduled (the default): a 256-byte header and the item list come first
+    ps = pa.pa_decode_get_plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4)
+    assert ps["scheduled"] and ps["num_workgroups"] == S * Hkv * 8
+    assert ps["workspace_bytes"] == 256 + _align(S * Hkv * 8 * 8) + _align(rows * 8) + rows * D * 4
+    p1 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, prefetch=3, schedule=-1)
     assert p1["num_partitions"] == 1 and p1["workspace_bytes"] == 0 and p1["prefetch_tiles"] == 3
-    assert p1["variant"] == "mfma"
-    assert p1["partition_tokens"] == 112
+    assert p1["variant"] == "mfma" and p1["partition_tokens"] == 112
+    p1s = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1)
+    assert p1s["workspace_bytes"] == 256 + _align(4 * 2 * 8)
     # a partition longer than the longest possible context is no split
     p2 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=4096)
     assert p2["num_partitions"] == 1

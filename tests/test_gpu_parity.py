@@ -70,20 +70,48 @@ def test_split_and_waves_agree_with_oracle(lib, name, partition, waves, variant)
     ref = _oracle(w)
     d = DeviceWorkload(w)
     prefetch = 1 + (waves + partition) % 3  # every ring depth, spread over the cases
-    note(f"decode {name} partition={partition} waves={waves} variant={variant} prefetch={prefetch}")
-    out = d.decode(partition_tokens=partition, waves=waves, variant=variant, prefetch=prefetch)
+    schedule = 1 if (waves + partition // 16) % 2 else -1  # device work list, or the direct grid
+    note(f"decode {name} partition={partition} waves={waves} variant={variant} prefetch={prefetch} "
+         f"schedule={schedule}")
+    out = d.decode(partition_tokens=partition, waves=waves, variant=variant, prefetch=prefetch,
+                   schedule=schedule)
     torch.cuda.synchronize()
     compare(host_bits(out), ref, *BF16_TOL)
 
 
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_decode_is_deterministic(lib, variant):
+    """Repeat runs are bit-identical, and the device-built schedule (items in
+    an order that depends on atomics) gives the same bits as the direct grid."""
     w = W.make_workload("mixed_batch", **REDUCED["mixed_batch"])
     d = DeviceWorkload(w)
     note(f"determinism mixed_batch {variant}")
-    a = host_bits(d.decode(partition_tokens=512, variant=variant))
-    b = host_bits(d.decode(partition_tokens=512, variant=variant))
+    a = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=1))
+    b = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=1))
+    c = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=-1))
     assert np.array_equal(a, b)
+    assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("schedule", [1, -1])
+def test_full_size_mixed_batch_sampled(lib, schedule):
+    """The mixed continuous batch at its full size (256 sequences, lognormal
+    lengths, shared prefix), in the launch configuration the benchmark uses,
+    checked on a sample of (sequence, KV head) units the oracle computes one
+    by one."""
+    w = W.make_workload("mixed_batch")
+    d = DeviceWorkload(w)
+    note(f"full-size mixed_batch schedule={schedule}")
+    out = host_bits(d.decode(schedule=schedule))
+    rng = np.random.default_rng(3)
+    s = w.spec
+    longest = int(np.argmax(w.context_lens))
+    units = np.unique(np.concatenate([rng.choice(s.num_seqs * s.num_kv_heads, 24, replace=False),
+                                      [longest * s.num_kv_heads, int(np.argmin(w.context_lens)) * s.num_kv_heads]]))
+    ref = oracle.decode_workload(w, units=units)
+    g = s.group
+    got = np.stack([out[u // s.num_kv_heads, (u % s.num_kv_heads) * g:(u % s.num_kv_heads + 1) * g] for u in units])
+    compare(got, ref, *BF16_TOL)
 
 
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
