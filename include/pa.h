@@ -79,10 +79,14 @@ typedef struct pa_decode_opts {
     int32_t prefetch_tiles;   /* 0 = chosen; else 1..3: 16-token tiles each
                                  wavefront keeps in flight ahead of the one it
                                  consumes */
-    int32_t schedule;         /* 0 or 1 = build the work list on the device
-                                 (longest first, no empty workgroups) and run
-                                 a persistent grid over it; -1 = one workgroup
-                                 per (sequence, KV head, partition) */
+    int32_t schedule;         /* 1 = first build the work list on the device
+                                 from context_lens: real (sequence, KV head,
+                                 partition) items only, longest first, so
+                                 workgroups are dispatched in that order; -1 =
+                                 one workgroup per (sequence, KV head,
+                                 partition) in index order, empty ones
+                                 included; 0 = the work list when the plan
+                                 splits contexts, else -1 */
     int32_t reserved;         /* must be 0 */
 } pa_decode_opts;
 
@@ -94,9 +98,9 @@ typedef struct pa_decode_plan {
     int32_t partition_tokens; /* tokens per partition */
     int32_t num_partitions;   /* partitions per (sequence, KV head); 1 = no split */
     int32_t prefetch_tiles;
-    int32_t scheduled;        /* 1 = device-built work list + persistent grid */
-    int64_t num_workgroups;   /* decode kernel grid size (direct grid), or the
-                                 upper bound on work items (scheduled) */
+    int32_t scheduled;        /* 1 = device-built work list */
+    int64_t num_workgroups;   /* decode kernel grid size (with a work list, the
+                                 ones past its end exit at once) */
     size_t workspace_bytes;   /* bytes of workspace pa_decode needs */
 } pa_decode_plan;
 

@@ -15,22 +15,26 @@
 // MFMA with fp32 accumulation (ToPG §2: FP32 accumulation).
 //
 // Layout of one 16-token tile in a wave (lane l, c = l % 16, gq = l / 16):
+//   * K and V rows go HBM -> registers -> LDS with 16-byte non-temporal
+//     buffer loads in which every instruction covers whole 256-byte rows
+//     (bf16, D = 128): the cache is read exactly once, as full lines. Loading
+//     K straight into the MFMA operand layout instead (16 rows x 64 bytes
+//     per instruction) was measured at ~70 % of peak against ~79 % this way.
 //   * S = K Q^T by v_mfma_f32_16x16x32_bf16, D/32 times: the A operand is K
-//     (row = token c, eight d values of chunk gq), loaded straight from HBM
-//     with 16-byte buffer loads; B is Q^T (column = head c), kept in
-//     registers. Lane l receives S[token 4*gq + r][head c], r = 0..3.
+//     (row = token c, eight d values of chunk gq) read back from LDS; B is
+//     Q^T (column = head c), kept in registers. Lane l receives
+//     S[token 4*gq + r][head c], r = 0..3.
 //   * The online softmax of head c needs the tile max over the four lane
 //     groups: two cross-lane exchanges per tile.
 //   * O^T = V^T P^T by v_mfma_f32_16x16x16_bf16, D/16 times: B is P^T
 //     (token 4*gq + r, head c) -- exactly the lane's own four probabilities,
 //     rounded to bf16 -- and A is V^T (row = d, token 4*gq + r), read from
-//     the tile's copy in LDS. V goes HBM -> registers -> LDS with
-//     fully-coalesced 16-byte loads (each instruction covers whole rows) so
-//     that the transpose happens in LDS. Lane l accumulates O[d = 16 j +
-//     4 gq + r][head c], so the softmax rescale of head c stays in-lane.
+//     the LDS copy with gfx950's transposing LDS load. Lane l accumulates
+//     O[d = 16 j + 4 gq + r][head c], so the softmax rescale of head c stays
+//     in-lane.
 //   * fp8 caches: codes are widened to bf16 exactly (every e4m3fn value is a
-//     bf16 value) with v_cvt_scalef32_pk_bf16_fp8; the scales are folded into
-//     the score scale and the output.
+//     bf16 value) with v_cvt_scalef32_pk_bf16_fp8 while staging; the scales
+//     are folded into the score scale and the output.
 //   * Each wave keeps a ring of NB tiles in registers: NB - 1 tiles are in
 //     flight while one is consumed (the same scheme as the VALU kernel).
 #include "pa_epilogue.h"
@@ -42,6 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // 16 fp8 codes -> 16 bf16 (two 8-element halves), exact.
 __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4& hi) {
@@ -57,18 +62,23 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4&
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
+// Occupancy the register allocator is asked to keep: 3 waves per SIMD for the
+// rings of 2 and 3 tiles (<= 168 VGPRs), 2 for the deepest ring.
+template <int NB>
+constexpr int mfma_waves_per_eu() { return NB <= 3 ? 3 : 2; }
+
 template <int D, bool FP8, int NB>
-__global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<NB>())))
+void pa_decode_mfma_kernel(DecodeArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int NQK = D / 32;         // q.K^T MFMAs per tile
     constexpr int NPV = D / 16;         // P.V MFMAs per tile
-    constexpr int NIK = D * ESZ / 64;   // 16-byte K loads per lane per tile
-    constexpr int EPL = 16 / ESZ;       // V elements per 16-byte lane load
-    constexpr int LPR = D / EPL;        // lanes per V row
-    constexpr int RPI = 64 / LPR;       // V rows per load instruction
-    constexpr int NIV = kTile / RPI;    // V loads per lane per tile
+    constexpr int EPL = 16 / ESZ;       // elements per 16-byte lane load
+    constexpr int LPR = D / EPL;        // lanes per row
+    constexpr int RPI = 64 / LPR;       // rows per load instruction
+    constexpr int NI = kTile / RPI;     // loads per lane per tile, for each of K and V
     constexpr int RS = D + 8;           // LDS row stride (bf16 elements): +16 bytes per row
-    static_assert(NIV >= 1 && kTile % RPI == 0, "tile shape");
+    static_assert(NI >= 1 && kTile % RPI == 0, "tile shape");
 
     extern __shared__ float smem[];
     for_each_item(a, [&](const WorkItem& wi) {
@@ -78,16 +88,19 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
         const int c = lane & 15;
         const int gq = lane >> 4;
         const int g = a.group;
-        uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * kTile * RS;
+        uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * 2 * kTile * RS;  // V tile
+        uint16_t* ks = vs + kTile * RS;                                               // K tile
+        const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RS + 4 * (lane & 3);
 
-        // Q^T operands: MFMA j takes d = dq(j) + 0..7 of head c, where dq(j) is
-        // the d offset the lane's K operand of MFMA j holds.
+        // Q^T operands: MFMA j takes d = 32 j + 8 gq + 0..7 of head c, the d
+        // range of the lane's K operand of MFMA j.
         bf16x8 qb[NQK];
 #pragma unroll
         for (int j = 0; j < NQK; ++j) {
-            const int d0 = FP8 ? (64 * (j >> 1) + 16 * gq + 8 * (j & 1)) : (32 * j + 8 * gq);
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (c < g) w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + c) * D + d0);
+            if (c < g)
+                w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + c) * D +
+                                                    32 * j + 8 * gq);
             qb[j] = __builtin_bit_cast(bf16x8, w);
         }
 
@@ -100,66 +113,74 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
         const int span = wi.t_end - wi.t_begin;
         const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
         const uint32_t head_off = (uint32_t)wi.kvh * a.head_bytes;
-        const uint32_t koff = (uint32_t)c * a.slot_bytes + head_off + 16u * (uint32_t)gq;
-        const uint32_t voff = (uint32_t)(lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
+        // per-lane byte offsets inside a tile (the same for K and V), fixed
+        // for the whole item: load i of lane l covers row i * RPI + l / LPR
+        uint32_t roff[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            roff[i] = (uint32_t)(i * RPI + lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
         const int bs_mask = (1 << a.block_size_log2) - 1;
         const float qk = a.qk_scale_log2;
 
-        u32x4 kb[NB][NIK], vb[NB][NIV];  // ring of NB tiles: NB - 1 in flight while one is consumed
+        u32x4 kb[NB][NI], vb[NB][NI];  // ring of NB tiles: NB - 1 in flight while one is consumed
 
-        // Loads for tile t. A tile past the end (the prefetch after the last
-        // one) still issues its loads, against a zero-byte buffer: they return
-        // zeros without touching memory, and every path through the loop keeps
-        // the same number of loads in flight, so the wait before a tile's use
-        // never has to drain the prefetch behind it.
-        auto issue = [&](int t, u32x4 (&kb)[NIK], u32x4 (&vb)[NIV]) {
-            const bool live = t < ntiles;
-            const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
+        // Loads for tile t, through a buffer descriptor that ends at the
+        // tile's last valid row: rows past the context read as zero (their
+        // weight is 0, but 0 * NaN would not be), with no masking code. A tile
+        // past the end (the prefetch after the last one) still issues its
+        // loads, against a zero-byte descriptor: they return zeros without
+        // touching memory, and every path through the loop keeps the same
+        // number of loads in flight, so the wait before a tile's use never
+        // has to drain the prefetch behind it.
+        // Wave w takes tiles w, w + W, w + 2W, ... of the item.
+        const int t_first = wave, t_step = W, t_stop = ntiles;
+
+        auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
+            const bool live = t < t_stop;
+            const int t0 = wi.t_begin + (live ? t : t_stop - 1) * kTile;
             const int64_t blk = physical_block(a, wi.seq, t0);
             const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
-            const uint32_t nbytes = live ? a.block_bytes : 0u;
+            const int valid = min(wi.t_end - t0, kTile);
+            const uint32_t nbytes = live ? row0 + (uint32_t)valid * a.slot_bytes : 0u;
             const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
             const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
 #pragma unroll
-            for (int i = 0; i < NIK; ++i) kb[i] = buf_load_b128(rk, koff + row0 + 64u * i);
+            for (int i = 0; i < NI; ++i) kb[i] = buf_load_b128_stream(rk, roff[i], row0);
 #pragma unroll
-            for (int i = 0; i < NIV; ++i) vb[i] = buf_load_b128(rv, voff + row0 + (uint32_t)(i * RPI) * a.slot_bytes);
+            for (int i = 0; i < NI; ++i) vb[i] = buf_load_b128_stream(rv, roff[i], row0);
         };
 
-        auto consume = [&](int t, const u32x4 (&kb)[NIK], const u32x4 (&vb)[NIV]) {
+        auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
             const int t0 = wi.t_begin + t * kTile;
             const int valid = wi.t_end - t0;
             const bool full = valid >= kTile;
 
-            // V rows -> LDS as bf16 (rows past the context are zeroed: their
-            // weight is 0, but 0 * NaN would not be).
-#pragma unroll
-            for (int i = 0; i < NIV; ++i) {
-                const int row = i * RPI + lane / LPR;
-                u32x4 w = vb[i];
-                if (!full && row >= valid) w = u32x4{0u, 0u, 0u, 0u};
+            // K and V rows -> LDS as bf16 (rows past the context arrived as zeros)
+            auto stage = [&](uint16_t* dst, const u32x4& w, int row) {
                 if constexpr (!FP8) {
-                    *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 8) = w;
+                    *reinterpret_cast<u32x4*>(dst + row * RS + (lane % LPR) * 8) = w;
                 } else {
                     u32x4 lo, hi;
                     fp8x16_to_bf16(w, lo, hi);
-                    *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16) = lo;
-                    *reinterpret_cast<u32x4*>(vs + row * RS + (lane % LPR) * 16 + 8) = hi;
+                    *reinterpret_cast<u32x4*>(dst + row * RS + (lane % LPR) * 16) = lo;
+                    *reinterpret_cast<u32x4*>(dst + row * RS + (lane % LPR) * 16 + 8) = hi;
                 }
+            };
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int row = i * RPI + lane / LPR;
+                stage(ks, kb[i], row);
+                stage(vs, vb[i], row);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
             // S = K Q^T
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
-                bf16x8 ka;
-                if constexpr (!FP8) {
-                    ka = __builtin_bit_cast(bf16x8, kb[j]);
-                } else {
-                    u32x4 lo, hi;
-                    fp8x16_to_bf16(kb[j >> 1], lo, hi);
-                    ka = __builtin_bit_cast(bf16x8, (j & 1) ? hi : lo);
-                }
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j], s, 0, 0, 0);
             }
 
@@ -173,6 +194,9 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
             const float m_new = fmaxf(m, mx);
             const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
             const float alpha = fast_exp2(m - ms);
+            // Rescale only when some head's running max moved (after the first
+            // tiles of a long context it rarely does).
+            const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
             m = m_new;
             bf16x4 pb;
             float psum = 0.0f;
@@ -183,44 +207,47 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
                 psum += (float)b;
             }
             l = fmaf(l, alpha, psum);
+            if (moved) {
 #pragma unroll
-            for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+                for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+            }
 
-            // O^T += V^T P^T
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // O^T += V^T P^T. ds_read_b64_tr_b16: within each 16-lane group,
+            // lane i receives element i % 4 of the 8-byte rows addressed by
+            // lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12. Lane (gq, s) addresses
+            // V[4 gq + s/4][16 j + 4 (s % 4)], so lane (gq, c) receives
+            // V[4 gq + k][16 j + c], k = 0..3: the A operand, one instruction
+            // per MFMA.
 #pragma unroll
             for (int j = 0; j < NPV; ++j) {
-                const uint16_t* src = vs + (4 * gq) * RS + 16 * j + c;
-                const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[RS] << 16);
-                const uint32_t v23 = (uint32_t)src[2 * RS] | ((uint32_t)src[3 * RS] << 16);
-                const bf16x4 va = __builtin_bit_cast(bf16x4, u32x2{v01, v23});
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                typedef __attribute__((address_space(3))) uint16_t lds_u16;
+                lds_s16x4* src = (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_base) + 16 * j);
+                const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));
                 o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
             }
+            // the next tile's staging overwrites this one
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         };
 
-        if (ntiles > 0) {
+        if (t_first < t_stop) {
             // The ring is unrolled so that every buffer index is a constant.
-            // sched_barrier keeps the compiler from sinking the prefetch below
-            // the waits of the tile being consumed.
-            int t = wave;
+            // Each step issues the loads NB - 1 tiles ahead unconditionally
+            // (past the end they are zero-byte no-ops) and consumes one tile
+            // behind a uniform branch, so every path through the loop keeps
+            // the same loads in flight and the waits before a tile's use
+            // leave the prefetch behind it outstanding. sched_barrier keeps
+            // the compiler from sinking the prefetch below those waits.
 #pragma unroll
-            for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
-            bool go = t < ntiles;
-            while (go) {
+            for (int b = 0; b < NB - 1; ++b) issue(t_first + b * t_step, kb[b], vb[b]);
+            for (int t = t_first; t < t_stop; t += NB * t_step) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    if (go) {
-                        issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-                        __builtin_amdgcn_sched_barrier(0);
-                        consume(t, kb[b], vb[b]);
-                        t += W;
-                        go = t < ntiles;
-                    }
+                    issue(t + (b + NB - 1) * t_step, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (t + b * t_step < t_stop) consume(t + b * t_step, kb[b], vb[b]);
                 }
             }
         }
@@ -250,13 +277,11 @@ __global__ __launch_bounds__(512) void pa_decode_mfma_kernel(DecodeArgs a) {
 template <int D, bool FP8, int NB>
 hipError_t launch_d(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
     const dim3 block((unsigned)(64 * ls.waves));
-    const size_t stage = (size_t)ls.waves * kTile * (D + 8) * sizeof(uint16_t);
+    const size_t stage = (size_t)ls.waves * 2 * kTile * (D + 8) * sizeof(uint16_t);
     const size_t comb = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
     const size_t lds = stage > comb ? stage : comb;
-    const auto kernel = pa_decode_mfma_kernel<D, FP8, NB>;
-    const int64_t nwg = grid_size(reinterpret_cast<const void*>(kernel), a, ls, lds);
-    if (nwg <= 0) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), block, lds, s, a);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 

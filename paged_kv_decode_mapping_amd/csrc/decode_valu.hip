@@ -106,7 +106,11 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
 
         const int span = wi.t_end - wi.t_begin;
         const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
-        const uint32_t lane_off = (uint32_t)r_in * a.slot_bytes + (uint32_t)wi.kvh * a.head_bytes + (uint32_t)c * 16u;
+        // per-lane byte offsets inside a tile, fixed for the whole item
+        uint32_t lane_off[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            lane_off[i] = (uint32_t)(i * RPI + r_in) * a.slot_bytes + (uint32_t)wi.kvh * a.head_bytes + (uint32_t)c * 16u;
         const int bs_mask = (1 << a.block_size_log2) - 1;
         const float qk = a.qk_scale_log2;
 
@@ -122,14 +126,17 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
             const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
             const int64_t blk = physical_block(a, wi.seq, t0);
             const uint32_t row0 = (uint32_t)(t0 & bs_mask);
-            const uint32_t nbytes = live ? a.block_bytes : 0u;
+            // the descriptor ends at the tile's last valid row: rows past the
+            // context read as zero, so V needs no masking code
+            const int valid = min(wi.t_end - t0, kTile);
+            const uint32_t nbytes = live ? (row0 + (uint32_t)valid) * a.slot_bytes : 0u;
             const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
             const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
+            const uint32_t soff = row0 * a.slot_bytes;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                const uint32_t off = lane_off + (row0 + (uint32_t)(i * RPI)) * a.slot_bytes;
-                kb[i] = buf_load_b128(rk, off);
-                vb[i] = buf_load_b128(rv, off);
+                kb[i] = buf_load_b128_stream(rk, lane_off[i], soff);
+                vb[i] = buf_load_b128_stream(rv, lane_off[i], soff);
             }
         };
 
@@ -174,10 +181,8 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                u32x4 w = vb[i];
-                if (!full && (i * RPI + r_in) >= valid) w = u32x4{0u, 0u, 0u, 0u};
                 float vf[EPL];
-                unpack<FP8, EPL>(w, vf);
+                unpack<FP8, EPL>(vb[i], vf);
 #pragma unroll
                 for (int h = 0; h < GM; ++h) {
 #pragma unroll
@@ -188,22 +193,20 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
 
         if (ntiles > 0) {
             // The ring is unrolled so that every buffer index is a constant.
-            // sched_barrier keeps the compiler from sinking the prefetch below
-            // the waits of the tile being consumed.
-            int t = wave;
+            // Each step issues the loads NB - 1 tiles ahead unconditionally
+            // (past the end they are zero-byte no-ops) and consumes one tile
+            // behind a uniform branch, so every path through the loop keeps
+            // the same loads in flight and the waits before a tile's use
+            // leave the prefetch behind it outstanding. sched_barrier keeps
+            // the compiler from sinking the prefetch below those waits.
 #pragma unroll
-            for (int b = 0; b < NB - 1; ++b) issue(t + b * W, kb[b], vb[b]);
-            bool go = t < ntiles;
-            while (go) {
+            for (int b = 0; b < NB - 1; ++b) issue(wave + b * W, kb[b], vb[b]);
+            for (int t = wave; t < ntiles; t += NB * W) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    if (go) {
-                        issue(t + (NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-                        __builtin_amdgcn_sched_barrier(0);
-                        consume(t, kb[b], vb[b]);
-                        t += W;
-                        go = t < ntiles;
-                    }
+                    issue(t + (b + NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (t + b * W < ntiles) consume(t + b * W, kb[b], vb[b]);
                 }
             }
         }
@@ -247,10 +250,8 @@ template <int D, bool FP8, int GM, int NB>
 hipError_t launch_k(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
     const dim3 block((unsigned)(64 * ls.waves));
     const size_t lds = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
-    const auto kernel = pa_decode_valu_kernel<D, FP8, GM, NB>;
-    const int64_t nwg = grid_size(reinterpret_cast<const void*>(kernel), a, ls, lds);
-    if (nwg <= 0) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), block, lds, s, a);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
+    hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, NB>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 

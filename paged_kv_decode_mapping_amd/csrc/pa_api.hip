@@ -6,6 +6,7 @@
 //   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
 //   nanoVLLM = «大模型推理优化技术：从nano-vLLM到连续批处理»
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -55,7 +56,7 @@ struct Plan {
     size_t workspace = 0;
 };
 
-constexpr size_t kHeaderBytes = 256;  // scheduled: item count, queue counter
+constexpr size_t kHeaderBytes = 256;  // scheduled: item count
 
 int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB,
                 int32_t kv_dtype) {
@@ -87,6 +88,17 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
         return PA_ERR_SHAPE;
     p.variant = o.variant != PA_VARIANT_AUTO ? o.variant : (g >= 4 ? PA_VARIANT_MFMA : PA_VARIANT_VALU);
     if (p.variant == PA_VARIANT_VALU && g > 4) return PA_ERR_UNSUPPORTED;
+    // Defaults measured on MI355X: the MFMA kernel's tiles are 16 whole K
+    // and V rows (8 KiB per wave for bf16, D = 128), so one tile in flight
+    // per wave already covers the memory latency; the VALU kernel for g = 1
+    // holds fewer bytes per wave and does best with 8 waves, 2 tiles ahead.
+    if (p.variant == PA_VARIANT_MFMA) {
+        p.waves = 4;
+        p.depth = 2;
+    } else {
+        p.waves = g == 1 ? 8 : 4;
+        p.depth = 3;
+    }
     if (o.prefetch_tiles < 0 || o.prefetch_tiles > 3) return PA_ERR_SHAPE;
     if (o.prefetch_tiles > 0) p.depth = o.prefetch_tiles + 1;
     if (o.waves_per_group != 0) {
@@ -125,12 +137,17 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     p.num_workgroups = units * p.num_partitions;
     if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
     if (o.schedule < -1 || o.schedule > 1) return PA_ERR_SHAPE;
-    // Scheduled items pack (partition << 16 | KV head) into 32 bits.
-    p.scheduled = o.schedule != -1 && p.num_partitions < 32768 && Hkv < 65536;
+    // Device work list: by default only when contexts are split. Then most
+    // (sequence, partition) pairs of a ragged batch are empty and the real
+    // ones differ in length, so a compact longest-first list pays for its
+    // pre-pass; an unsplit grid has one workgroup per (sequence, KV head)
+    // and no empty ones. Items pack (partition << 16 | KV head) into 32 bits.
+    const bool want = o.schedule == 1 || (o.schedule == 0 && p.num_partitions > 1);
+    p.scheduled = want && p.num_partitions < 32768 && Hkv < 65536;
     size_t off = 0;
     if (p.scheduled) {
         p.items_off = kHeaderBytes;
-        off = p.items_off + align_up((size_t)p.num_workgroups * 2 * sizeof(int32_t), 256);
+        off = p.items_off + align_up((size_t)p.num_workgroups * 4 * sizeof(int32_t), 256);
     }
     if (p.num_partitions > 1) {
         const size_t rows = (size_t)S * Hq * p.num_partitions;
@@ -233,11 +250,6 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
         if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
     }
-    int cus = 0;
-    if (p.scheduled) {
-        cus = current_cu_count();
-        if (cus <= 0) return PA_ERR_DEVICE;
-    }
     const int64_t esz = fp8 ? 1 : 2;
     pa::DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -253,8 +265,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     }
     if (p.scheduled) {
         a.item_count = reinterpret_cast<int*>(ws);
-        a.queue = reinterpret_cast<int*>(ws) + 1;
-        a.items = reinterpret_cast<const int2*>(ws + p.items_off);
+        a.items = reinterpret_cast<const int4*>(ws + p.items_off);
     }
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
@@ -264,7 +275,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.partition_tokens = p.partition_tokens;
     a.num_partitions = p.num_partitions;
-    a.num_blocks = num_blocks;
+    a.last_block = (int32_t)((num_blocks > INT32_MAX ? (int64_t)INT32_MAX + 1 : num_blocks) - 1);
     a.head_bytes = (uint32_t)(head_dim * esz);
     a.slot_bytes = (uint32_t)((int64_t)num_kv_heads * head_dim * esz);
     a.block_bytes = (uint32_t)((int64_t)block_size * num_kv_heads * head_dim * esz);
@@ -275,17 +286,17 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     if (p.scheduled) {
         pa::ScheduleArgs sa{};
         sa.context_lens = context_lens;
-        sa.items = reinterpret_cast<int2*>(ws + p.items_off);
+        sa.items = reinterpret_cast<int4*>(ws + p.items_off);
         sa.item_count = reinterpret_cast<int*>(ws);
-        sa.queue = a.queue;
         sa.num_seqs = num_seqs;
         sa.num_kv_heads = num_kv_heads;
         sa.partition_tokens = p.partition_tokens;
+        sa.num_partitions = p.num_partitions;
         sa.max_context = max_blocks_per_seq * block_size;
         e = pa::launch_schedule(sa, s);
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
-    const pa::LaunchShape ls{p.waves, p.depth, cus, p.scheduled ? p.num_workgroups : 0};
+    const pa::LaunchShape ls{p.waves, p.depth};
     e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, ls, s)
                                      : pa::launch_decode_valu(a, head_dim, fp8, ls, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;

@@ -69,8 +69,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+// Cache-policy bits of a buffer load on gfx950: bit 1 = nt (non-temporal).
+constexpr int kCachePolicyDefault = 0;
+constexpr int kCachePolicyStream = 2;
+
+// 16-byte buffer load at voff (per-lane, VGPR) + soff (wave-uniform, SGPR).
+// Keeping the uniform part in soff lets per-lane offsets stay loop-invariant,
+// so issuing a tile's loads needs no vector temporaries.
+__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicyDefault);
+}
+
+// A load of data read once (the KV cache in decode): marked non-temporal, so
+// that the caches treat the lines as streaming. On MI355X a plain streaming
+// read reaches ~6.25 TB/s with default loads and ~7.0 TB/s with nt loads.
+__device__ __forceinline__ u32x4 buf_load_b128_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicyStream);
 }
 
 __device__ __forceinline__ u32x2 buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff) {

@@ -91,11 +91,25 @@ __device__ __forceinline__ WorkItem decode_work_item(const DecodeArgs& a) {
     return make_work_item(a, unit / a.num_kv_heads, unit % a.num_kv_heads, bid % P);
 }
 
-// Runs `body(item)` for every work item of this workgroup: the one its block
-// index names (direct grid), or, when a schedule was built, items pulled
-// from the device queue until it is empty (persistent grid). `body` must be
-// called by the whole workgroup; a barrier separates consecutive items, so
-// LDS can be reused.
+__device__ __forceinline__ WorkItem scheduled_item(const int4& r) {
+    WorkItem w;
+    w.seq = r.x;
+    w.kvh = r.y & 0xffff;
+    w.part = r.y >> 16;
+    w.t_begin = r.z;
+    w.t_end = r.w & ~kItemFinal;
+    w.final_out = (r.w & kItemFinal) != 0;
+    w.active = true;
+    return w;
+}
+
+// Runs `body(item)` for this workgroup's work item: with no schedule, the
+// (sequence, KV head, partition) its block index names; with a schedule, the
+// block index's entry of the device-built list. That list is compact and
+// longest first, so workgroups are dispatched in that order and those past
+// its end (the grid is sized for the most items there can be) exit at once,
+// after every real item has been dispatched. `body` must be called by the
+// whole workgroup.
 template <class Body>
 __device__ __forceinline__ void for_each_item(const DecodeArgs& a, Body&& body) {
     if (a.items == nullptr) {
@@ -103,26 +117,22 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, Body&& body) 
         if (wi.active) body(wi);
         return;
     }
-    __shared__ int s_next;
+    const int b = (int)blockIdx.x;
     const int count = *a.item_count;
-    for (;;) {
-        if (threadIdx.x == 0) s_next = atomicAdd(a.queue, 1);
-        __syncthreads();
-        const int it = s_next;
-        __syncthreads();
-        if (it >= count) break;
-        const int2 item = a.items[it];
-        body(make_work_item(a, item.x, item.y & 0xffff, item.y >> 16));
-    }
+    const int4 rec = a.items[b];  // in bounds: the list has room for the whole grid
+    if (b >= count) return;
+    body(scheduled_item(rec));
 }
 
 // Physical block of a token, clamped into the pool so that a bad table entry
-// cannot address memory outside it.
+// cannot address memory outside it. The clamp is 32-bit (table entries are
+// int32) so it stays in scalar registers: a 64-bit compare has no scalar form
+// on gfx9 and would borrow vector registers inside the load pipeline.
 __device__ __forceinline__ int64_t physical_block(const DecodeArgs& a, int seq, int token) {
-    int64_t b = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + (token >> a.block_size_log2)];
+    int b = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + (token >> a.block_size_log2)];
     b = b < 0 ? 0 : b;
-    b = b >= a.num_blocks ? a.num_blocks - 1 : b;
-    return b;
+    b = b > a.last_block ? a.last_block : b;
+    return (int64_t)b;
 }
 
 }  // namespace pa

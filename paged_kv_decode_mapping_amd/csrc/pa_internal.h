@@ -22,24 +22,25 @@ struct DecodeArgs {
     int32_t num_seqs, num_q_heads, num_kv_heads, group;
     int32_t block_size_log2, max_blocks_per_seq;
     int32_t partition_tokens, num_partitions;
-    int64_t num_blocks;
+    int32_t last_block;            // min(num_blocks, 2^31) - 1: the largest usable block id
     uint32_t block_bytes;          // bytes of one physical block
     uint32_t slot_bytes;           // bytes of one token row (all KV heads)
     uint32_t head_bytes;           // bytes of one KV head's row
     float qk_scale_log2;           // scale * k_scale * log2(e)
     float v_scale;                 // 1 for bf16
     // Device schedule (null = direct grid, one workgroup per item):
-    const int2* items;             // (seq, part << 16 | kv head), longest first
+    const int4* items;             // see ScheduleArgs, longest first
     const int* item_count;         // number of valid items
-    int* queue;                    // next item to hand out (zeroed by the scheduler)
 };
+
+// A scheduled work item: (seq, part << 16 | kv head, t_begin, t_end | kItemFinal).
+constexpr int kItemFinal = 1 << 30;  // the item stores the final output (no merge)
 
 struct ScheduleArgs {
     const int32_t* context_lens;
-    int2* items;
+    int4* items;
     int* item_count;
-    int* queue;
-    int32_t num_seqs, num_kv_heads, partition_tokens;
+    int32_t num_seqs, num_kv_heads, partition_tokens, num_partitions;
     int32_t max_context;           // max_blocks_per_seq * block_size
 };
 
@@ -68,22 +69,7 @@ struct CacheWriteArgs {
 struct LaunchShape {
     int waves;          // wavefronts per workgroup
     int depth;          // tiles a wave keeps in its register ring (2..4)
-    int num_cus;        // compute units of the device
-    int64_t max_items;  // persistent grid: upper bound on scheduled items (0 = direct grid)
 };
-
-// Workgroups to launch: one per (sequence, KV head, partition) for a direct
-// grid; for a scheduled (persistent) grid, as many as can be resident at
-// once (occupancy x compute units), but no more than there can be items.
-inline int64_t grid_size(const void* kernel, const DecodeArgs& a, const LaunchShape& ls, size_t lds) {
-    if (a.items == nullptr) return (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * ls.waves, lds) != hipSuccess ||
-        per_cu <= 0)
-        per_cu = 1;
-    const int64_t n = (int64_t)per_cu * ls.num_cus;
-    return n < ls.max_items ? n : ls.max_items;
-}
 
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s);

@@ -75,6 +75,12 @@ def _decode(lib, **kw):
                          ctypes.byref(o) if o is not None else None, None)
 
 
+def _reserved(v):
+    o = pa._opts(partition_tokens=-1, schedule=-1)
+    o.reserved = v
+    return o
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(D=96), -3), (dict(D=256), -3), (dict(Hq=6, Hkv=4), -2), (dict(Hq=64, Hkv=2), -3),
     (dict(bs=8), -3), (dict(bs=24), -3), (dict(kvd=7), -5), (dict(MB=0), -2), (dict(S=-1), -2),
@@ -86,6 +92,7 @@ def _decode(lib, **kw):
     (dict(opts=pa._opts(partition_tokens=32, schedule=-1), ws=A, wsb=16), -6),
     (dict(opts=pa._opts(partition_tokens=-1, schedule=1)), -6), (dict(opts=pa._opts(partition_tokens=-1, schedule=2)), -2),
     (dict(opts=pa._opts(partition_tokens=-1, schedule=1), ws=A + 16, wsb=1 << 20), -4),
+    (dict(opts=_reserved(1)), -2), (dict(opts=_reserved(-1)), -2),
 ])
 def test_decode_rejects_bad_arguments_without_launching(lib, kw, code):
     assert _decode(lib, **kw) == code
@@ -107,15 +114,18 @@ def test_plan_with_explicit_partitions(lib):
     rows = S * Hq * 8
     assert p["workspace_bytes"] == _align(rows * 8) + rows * D * 4
     assert p["variant"] == "valu" and p["prefetch_tiles"] == 2
-    # scheduled (the default): a 256-byte header and the item list come first
+    # scheduled (the default when contexts are split): a 256-byte header and
+    # the item list come first
     ps = pa.pa_decode_get_plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4)
     assert ps["scheduled"] and ps["num_workgroups"] == S * Hkv * 8
-    assert ps["workspace_bytes"] == 256 + _align(S * Hkv * 8 * 8) + _align(rows * 8) + rows * D * 4
+    assert ps["workspace_bytes"] == 256 + _align(S * Hkv * 8 * 16) + _align(rows * 8) + rows * D * 4
     p1 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, prefetch=3, schedule=-1)
     assert p1["num_partitions"] == 1 and p1["workspace_bytes"] == 0 and p1["prefetch_tiles"] == 3
     assert p1["variant"] == "mfma" and p1["partition_tokens"] == 112
-    p1s = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1)
-    assert p1s["workspace_bytes"] == 256 + _align(4 * 2 * 8)
+    p1d = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1)
+    assert not p1d["scheduled"] and p1d["workspace_bytes"] == 0
+    p1s = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, schedule=1)
+    assert p1s["scheduled"] and p1s["workspace_bytes"] == 256 + _align(4 * 2 * 16)
     # a partition longer than the longest possible context is no split
     p2 = pa.pa_decode_get_plan(4, 8, 2, 64, 16, 7, partition_tokens=4096)
     assert p2["num_partitions"] == 1

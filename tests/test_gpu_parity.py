@@ -277,3 +277,22 @@ def test_fp8_decode_reads_every_code_exactly(lib, variant):
             nan = np.isnan(ref)
             assert np.array_equal(np.isnan(v), nan)
             assert np.array_equal(v[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_many_short_items_per_workgroup(lib, variant):
+    """Hundreds of short and empty contexts: every persistent workgroup runs
+    many items back to back (item lookahead, queue tickets, LDS reuse), and
+    the schedule must still give the direct grid's bits."""
+    rng = np.random.default_rng(21)
+    ctx = rng.integers(0, 48, size=600).tolist()
+    name = "llama7b_mha" if variant == "valu" else "mixed_batch"
+    w = W.make_workload(name, num_seqs=len(ctx), context=("list", ctx), shared_prefix_tokens=0)
+    ref = _oracle(w)
+    d = DeviceWorkload(w)
+    for part in (-1, 16):
+        note(f"many short items {variant} partition={part}")
+        a = host_bits(d.decode(variant=variant, partition_tokens=part, schedule=1))
+        b = host_bits(d.decode(variant=variant, partition_tokens=part, schedule=-1))
+        compare(a, ref, *BF16_TOL)
+        assert np.array_equal(a, b)
