@@ -95,6 +95,151 @@ def cpu_baseline(w, kv: str, kq=None, vq=None, budget_s: float = 12.0) -> dict:
                       f"float64 gather + softmax(qK^T)V, same byte model"}
 
 
+def bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b: int, k_scale: float, v_scale: float,
+                kq=None, vq=None) -> int:
+    """Time pa_decode_multi: the last --qlen cached tokens of every sequence are
+    its queries (speculative verification of qlen - 1 draft tokens)."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    from paged_kv_decode_mapping_amd import workloads as W
+    s = w.spec
+    qlens = np.minimum(np.full(s.num_seqs, args.qlen), w.context_lens)
+    mq = W.make_multi_query(w, qlens)
+    dev = k_cache.device
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    qs = torch.from_numpy(mq.query_start).to(dev)
+    maxq = int(qlens.max())
+    kvd = pa.PA_KV_BF16 if kv_b == 2 else pa.PA_KV_FP8_E4M3FN
+    need = pa.pa_decode_multi_workspace_size(s.num_seqs, mq.num_tokens, maxq, s.num_q_heads, s.num_kv_heads,
+                                             s.head_dim, s.block_size, w.max_blocks_per_seq, kvd, args.partition)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def run():
+        pa.pa_decode_multi(q, k_cache, v_cache, tables, ctx, qs, w.scale, maxq, out, k_scale=k_scale,
+                           v_scale=v_scale, workspace=ws, partition_tokens=args.partition)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    avg = float(ms.mean())
+    cl = w.context_lens.astype(np.int64)
+    nblk = (cl + s.block_size - 1) // s.block_size
+    # K and V of every context once, q in and out for every query row, tables and offsets
+    nbytes = int((2 * cl * s.num_kv_heads * s.head_dim * kv_b).sum() + 2 * mq.num_tokens * s.num_q_heads * s.head_dim * 2
+                 + 4 * nblk.sum() + 4 * s.num_seqs + 4 * (s.num_seqs + 1))
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    log(f"multi: {mq.num_tokens} query tokens (qlen {args.qlen}), avg {avg * 1e3:.1f} us = {achieved:.0f} GB/s")
+    base = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kvd_o = oracle.KV_BF16 if kv_b == 2 else oracle.KV_FP8_E4M3FN
+        kc = w.k_cache if kq is None else kq
+        vc = w.v_cache if vq is None else vq
+        units_all = np.random.default_rng(5).permutation(s.num_seqs * s.num_kv_heads)
+        done, t_total, ob = 0, 0.0, 0
+        while done < len(units_all) and t_total < 12.0:
+            u = units_all[done:done + 64]
+            t1 = time.perf_counter()
+            oracle.multi_decode(mq.q, kc, vc, w.block_tables, w.context_lens, mq.query_start, w.scale, units=u,
+                                kv_dtype=kvd_o, k_scale=k_scale, v_scale=v_scale)
+            t_total += time.perf_counter() - t1
+            seqs = u // s.num_kv_heads
+            ob += int((2 * cl[seqs] * s.head_dim * kv_b + 4 * qlens[seqs] * s.group * s.head_dim).sum())
+            done += len(u)
+        base = {"value": round(ob / t_total / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+                "kind": "oracle", "sample": f"{done} of {len(units_all)} (sequence, KV head) units, {t_total:.1f} s"}
+        log(f"cpu baseline {base}")
+    res = {
+        "metric": "multi-token paged attention achieved HBM GB/s + query tokens/s",
+        "value": round(nbytes * args.steps / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.kv, "data": "synthetic",
+        "config": {"workload": f"{s.name} with {args.qlen} query tokens per sequence", "num_seqs": s.num_seqs,
+                   "query_tokens": mq.num_tokens, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+                   "head_dim": s.head_dim, "block_size": s.block_size},
+        "query_tokens_per_s": round(mq.num_tokens / (avg * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_decode_multi"},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_copy_blocks(args, w, k_cache, v_cache, kv_b: int, kq=None, vq=None) -> int:
+    """Time pa_copy_blocks: each call copies --pairs whole blocks of K and V
+    (src and dst drawn without replacement from a fresh permutation of the
+    pool per call, so no call finds its blocks in a cache)."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    s = w.spec
+    n = args.pairs
+    N = w.num_blocks
+    if 2 * n > N:
+        raise SystemExit(f"--pairs {n} needs a pool of at least {2 * n} blocks (have {N})")
+    rng = np.random.default_rng(77)
+    calls = args.warmup + args.steps
+    maps = [torch.from_numpy(np.ascontiguousarray(rng.permutation(N)[:2 * n].reshape(2, n).T)).to(k_cache.device)
+            for _ in range(calls)]
+    block_bytes = s.block_size * s.num_kv_heads * s.head_dim * kv_b
+    moved = 4 * n * block_bytes  # K and V, read once and written once
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        pa.pa_copy_blocks(k_cache, v_cache, maps[i])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pa.pa_copy_blocks(k_cache, v_cache, maps[args.warmup + i])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    avg = float(ms.mean())
+    achieved = moved / (avg * 1e-3) / 1e9
+    log(f"copy_blocks: {n} pairs x {block_bytes} B, avg {avg * 1e3:.1f} us = {achieved:.0f} GB/s")
+    base = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kc = w.k_cache if kq is None else kq
+        vc = w.v_cache if vq is None else vq
+        kc, vc = np.array(kc), np.array(vc)  # private copies: the oracle copies in place
+        pairs = maps[0].cpu().numpy()[: min(n, 256)]
+        t1 = time.perf_counter()
+        oracle.copy_blocks(kc, vc, pairs)
+        dt = time.perf_counter() - t1
+        base = {"value": round(4 * len(pairs) * block_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": f"{len(pairs)} of {n} pairs of one call, {dt:.2f} s, element-wise copy"}
+        log(f"cpu baseline {base}")
+    res = {
+        "metric": "paged KV block copy achieved HBM GB/s (read + write)",
+        "value": round(moved * args.steps / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.kv, "data": "synthetic",
+        "config": {"workload": f"{s.name} pool: {n} block pairs per call, {block_bytes} B per block and cache",
+                   "num_blocks": N, "block_size": s.block_size, "num_kv_heads": s.num_kv_heads,
+                   "head_dim": s.head_dim, "pairs": n},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_copy_blocks"},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +254,12 @@ def main() -> int:
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
     ap.add_argument("--prefetch", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
+    ap.add_argument("--op", choices=["step", "copy_blocks", "multi"], default="step",
+                    help="step: cache write + decode (the default measurement); copy_blocks: time "
+                         "pa_copy_blocks on the workload's pool; multi: time pa_decode_multi with "
+                         "--qlen query tokens per sequence")
+    ap.add_argument("--qlen", type=int, default=4, help="query tokens per sequence for --op multi")
+    ap.add_argument("--pairs", type=int, default=1024, help="block pairs per pa_copy_blocks call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy this many MiB device-to-device once (a plain copy kernel "
                          "of known size, the reference for hardware byte counters)")
@@ -162,6 +313,10 @@ def main() -> int:
         if not args.no_cpu_baseline:
             kq, vq = kc8.cpu().numpy(), vc8.cpu().numpy()
     kv_b = 2 if args.kv == "bf16" else 1
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, w, k_cache, v_cache, kv_b, kq, vq)
+    if args.op == "multi":
+        return bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b, k_scale, v_scale, kq, vq)
     plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
                                  w.max_blocks_per_seq, pa.PA_KV_BF16 if args.kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
                                  partition_tokens=args.partition, variant=args.variant, waves=args.waves,

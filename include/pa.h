@@ -5,7 +5,7 @@
  * "device" is a device address on the current HIP device; every call is
  * asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
  * default stream) and returns after the launches are queued. The library
- * allocates nothing and keeps no state between calls: the caller owns every
+ * allocates no device memory and keeps no state between calls: the caller owns every
  * buffer, including the split-K workspace.
  *
  * Pages cited (titles as printed at the top of each page):
@@ -36,7 +36,11 @@
  * is read back from the device. Device-side contents (slot ids, block ids,
  * context lengths) are preconditions: the kernels clamp block ids into the
  * pool and ignore out-of-pool slots so that a bad table cannot fault the GPU,
- * but the results are then unspecified.
+ * but the results are then unspecified. pa_check_cache_write_inputs and
+ * pa_check_decode_inputs verify them (synchronising); with the environment
+ * variable PA_DEBUG_VALIDATE set to anything but "0", pa_cache_write and
+ * pa_decode run those checks first and return PA_ERR_PRECONDITION instead of
+ * launching.
  */
 #ifndef PA_H
 #define PA_H
@@ -57,6 +61,7 @@ extern "C" {
 #define PA_ERR_WORKSPACE (-6)   /* workspace missing or smaller than pa_decode_workspace_size */
 #define PA_ERR_LAUNCH (-7)      /* the HIP runtime rejected a launch */
 #define PA_ERR_DEVICE (-8)      /* the current device could not be queried */
+#define PA_ERR_PRECONDITION (-9) /* a device-side input breaks a precondition (checked calls only) */
 
 /* KV-cache element types. */
 #define PA_KV_BF16 1
@@ -133,6 +138,25 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                    int32_t kv_dtype, float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_copy_blocks -- duplicate physical blocks, the copy step of copy-on-write
+ * (Tutorial §4.2, PagedKVCache supports copy-on-write for beam search;
+ * Tutorial §4.3 "Prefix Caching" shares blocks between sequences): for each
+ * pair (src, dst) of block_mapping, block dst of k_cache and of v_cache
+ * becomes a byte-for-byte copy of block src (every row and KV head).
+ *
+ *   k_cache, v_cache  device, [num_blocks, block_size, num_kv_heads, head_dim]
+ *                     of kv_dtype
+ *   block_mapping     device, [num_pairs][2] int64 (src, dst); a pair with a
+ *                     negative or out-of-pool id is skipped
+ * Preconditions (not checked): destinations distinct, and no block is both
+ * a source and a destination in one call (pairs are copied concurrently).
+ * num_pairs <= 65535; num_pairs == 0 returns PA_OK with no launch.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int32_t kv_dtype, void* stream);
+
+/*
  * pa_decode -- one decode step of paged attention: every sequence's single
  * query token attends over its context_lens[i] cached tokens, reached
  * through its block-table row (Tutorial §4.2, PagedKVCache.get_kv;
@@ -160,7 +184,8 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
  *                    and the split-K partials; scratch, overwritten by each
  *                    call
  *   opts             NULL or tuning options
- * Supported: head_dim in {64, 128}; g in [1, 16]; block_size a power of
+ * Supported: head_dim in {64, 128}; g in [1, 1024] (above 16 the
+ * multi-row kernel of pa_decode_multi runs); block_size a power of
  * two in [16, 1024]; block_size * num_kv_heads * head_dim * element size
  * < 2^31 bytes. Calls that share a workspace must be ordered on one stream.
  */
@@ -172,6 +197,50 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               int32_t kv_dtype, float k_scale, float v_scale,
               void* workspace, size_t workspace_bytes,
               const pa_decode_opts* opts, void* stream);
+
+/*
+ * pa_decode_multi -- paged attention for several query tokens per sequence,
+ * each attending causally over the paged context: the target model's pass
+ * that verifies K draft tokens at once (Tutorial §5.1, speculative
+ * decoding) and a prefill chunk over an already cached prefix (Tutorial
+ * §6.2, chunked prefill). Sequence i has context_lens[i] = L cached tokens,
+ * the last n_i = query_start[i+1] - query_start[i] of which are its query
+ * tokens, already written with pa_cache_write. Query r of sequence i (row
+ * query_start[i] + r of q and out) is the token at position L - n_i + r; for
+ * query head h, with g = num_q_heads / num_kv_heads and kh = h / g,
+ *     s_j = scale * sum_d q[row,h,d] * K_j[kh,d]      for j <= L - n_i + r
+ *     out[row,h] = sum_j softmax(s)_j * V_j[kh,:]
+ * (K_j, V_j and fp8 scaling as in pa_decode). n_i = 1 for every sequence is
+ * exactly pa_decode's operation.
+ *
+ *   q, out          device, [num_query_tokens, num_q_heads, head_dim] bfloat16
+ *   query_start     device, [num_seqs + 1] int32, non-decreasing, from 0 to
+ *                   num_query_tokens
+ *   max_query_len   host, >= every n_i (rows past it are not computed)
+ *   partition_tokens 0 = chosen by the library, -1 = never split, > 0 =
+ *                   split contexts into partitions of this many tokens
+ *                   (multiple of 16) merged by log-sum-exp
+ *   workspace       device, >= pa_decode_multi_workspace_size(...) bytes,
+ *                   256-byte aligned (may be NULL when that size is 0)
+ * Other arguments as in pa_decode. Preconditions (not checked, see
+ * pa_check_decode_inputs): n_i <= context_lens[i]; a query with no visible
+ * token gets a zero output row. g may be anything up to 1024 here (and in
+ * pa_decode, which routes g > 16 to the same kernel).
+ */
+int pa_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* query_start, float scale, void* out,
+                    int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                    int32_t kv_dtype, float k_scale, float v_scale,
+                    void* workspace, size_t workspace_bytes, int32_t partition_tokens, void* stream);
+
+/* Bytes of workspace pa_decode_multi needs (0 when none, or for invalid sizes). */
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                                      int32_t partition_tokens);
 
 /*
  * pa_decode_get_plan -- the launch plan pa_decode would use for these sizes
@@ -187,6 +256,26 @@ int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t kv_dtype, const pa_decode_opts* opts);
+
+/*
+ * pa_check_cache_write_inputs -- check the device-side preconditions of
+ * pa_cache_write: every slot is negative (skipped) or in
+ * [0, num_blocks * block_size), and no slot appears twice (Tutorial §4.2,
+ * PagedKVCache: each appended token gets its own row).
+ * pa_check_decode_inputs -- check those of pa_decode: every context length
+ * is in [0, max_blocks_per_seq * block_size] and the table entries covering
+ * it (the first ceil(ctx / block_size) of the row) are in [0, num_blocks).
+ *
+ * Device pointers, as in the hot-path calls. Both wait for `stream` and copy
+ * the index arrays to host memory (no device allocation): debugging aids,
+ * not for the decode loop. Return PA_OK, PA_ERR_PRECONDITION, PA_ERR_NULL,
+ * PA_ERR_SHAPE, or PA_ERR_LAUNCH if the copy fails.
+ */
+int pa_check_cache_write_inputs(const int64_t* slot_mapping, int64_t num_tokens, int32_t block_size,
+                                int64_t num_blocks, void* stream);
+int pa_check_decode_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                           void* stream);
 
 /* Host-side reference of the kernels' fp8 encoder (same source as the
  * device code): n float32 inputs, already divided by the scale, to e4m3fn

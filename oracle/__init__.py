@@ -62,6 +62,12 @@ def _load():
                                             P, P, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
                                             P, i64, P, ctypes.c_int]
         lib.oracle_decode_units.restype = ctypes.c_int
+        lib.oracle_multi_units.argtypes = [P, P, P, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                           P, P, P, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                                           P, i64, P, ctypes.c_int]
+        lib.oracle_multi_units.restype = ctypes.c_int
+        lib.oracle_copy_blocks.argtypes = [P, P, P, i64, i64, i64, i64, i64, i64]
+        lib.oracle_copy_blocks.restype = i64
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -170,6 +176,53 @@ def decode_workload(w, *, units: Optional[Sequence[int]] = None, kv_dtype: int =
     return decode_units(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, units,
                         w.spec.num_q_heads, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
                         threads=threads)
+
+
+def multi_decode(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, *,
+                 units: Optional[Sequence[int]] = None, kv_dtype: int = KV_BF16, k_scale: float = 1.0,
+                 v_scale: float = 1.0, threads: int = 0) -> np.ndarray:
+    """Multi-token paged attention -> float64 [T_q, Hq, D]: the last
+    query_start[i+1] - query_start[i] of sequence i's context_lens[i] tokens
+    attend causally. Rows of units not requested stay NaN."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    Tq, Hq, D = q.shape
+    N, bs, Hkv, D2 = k_cache.shape
+    assert D2 == D and Hq % Hkv == 0
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    S = ctx.shape[0]
+    assert qs.shape == (S + 1,) and qs[0] == 0 and qs[-1] == Tq and np.all(np.diff(qs) >= 0)
+    MB = tables.shape[1]
+    if units is None:
+        units = np.arange(S * Hkv)
+    units = np.ascontiguousarray(np.asarray(units, dtype=np.int64))
+    out = np.full((Tq, Hq, D), np.nan, dtype=np.float64)
+    kc = np.ascontiguousarray(k_cache)
+    vc = np.ascontiguousarray(v_cache)
+    rc = lib.oracle_multi_units(_ptr(q), _ptr(kc), _ptr(vc), kv_dtype, k_scale, v_scale, _ptr(tables),
+                                _ptr(ctx), _ptr(qs), S, Hq, Hkv, D, bs, N, MB, float(scale), _ptr(units),
+                                len(units), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError("block id outside the pool, context longer than its table row, "
+                         "or more query tokens than context")
+    return out
+
+
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> int:
+    """In-place block copy of both caches ([N, bs, Hkv, D], uint16 bf16 bits or
+    uint8 fp8 codes) for (src, dst) pairs; negative ids are skipped."""
+    lib = _load()
+    pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+    assert k_cache.shape == v_cache.shape and k_cache.dtype == v_cache.dtype
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    N, bs, Hkv, D = k_cache.shape
+    n = lib.oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pr), pr.shape[0], N, bs, Hkv, D,
+                               k_cache.dtype.itemsize)
+    if n < 0:
+        raise ValueError("block id outside the pool or a repeated destination")
+    return int(n)
 
 
 def quantize_pool(bits: np.ndarray, scale: float) -> np.ndarray:

@@ -19,6 +19,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 
 PA_OK = 0
+PA_ERR_PRECONDITION = -9
 PA_KV_BF16 = 1
 PA_KV_FP8_E4M3FN = 2
 PA_VARIANT_AUTO = 0
@@ -71,6 +72,17 @@ def load_library(path: Optional[str] = None):
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_fp8_e4m3fn_encode_host.argtypes = [P, P, i64]
     lib.pa_fp8_e4m3fn_encode_host.restype = None
+    lib.pa_decode_multi.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, i32, i32, i32, i64,
+                                    i32, f32, f32, P, sz, i32, P]
+    lib.pa_decode_multi.restype = ctypes.c_int
+    lib.pa_decode_multi_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_multi_workspace_size.restype = sz
+    lib.pa_copy_blocks.argtypes = [P, P, P, i64, i32, i32, i32, i64, i32, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_check_cache_write_inputs.argtypes = [P, i64, i32, i64, P]
+    lib.pa_check_cache_write_inputs.restype = ctypes.c_int
+    lib.pa_check_decode_inputs.argtypes = [P, P, i32, i32, i32, i64, P]
+    lib.pa_check_decode_inputs.restype = ctypes.c_int
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.pa_strerror.restype = ctypes.c_char_p
     lib.pa_version.restype = ctypes.c_int
@@ -142,6 +154,78 @@ def pa_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v
         raise PAError(st, "pa_cache_write")
 
 
+def pa_decode_multi(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+                    max_query_len: int, out=None, *, k_scale: float = 1.0, v_scale: float = 1.0,
+                    workspace=None, partition_tokens: int = 0, stream=None):
+    """Multi-token paged attention: q [T_q, Hq, D] bf16, query_start [S + 1]
+    int32; the last query_start[i+1] - query_start[i] of sequence i's
+    context_lens[i] cached tokens attend causally. Returns out [T_q, Hq, D]."""
+    import torch
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_cache, "k_cache", None, 4)
+    _check(v_cache, "v_cache", None, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    _check(query_start, "query_start", torch.int32, 1)
+    kvd = _kv_dtype(k_cache)
+    if _kv_dtype(v_cache) != kvd or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache differ")
+    Tq, Hq, D = q.shape
+    N, bs, Hkv, D2 = k_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or block_tables.shape[0] != S or query_start.shape != (S + 1,):
+        raise ValueError("shape mismatch")
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out shape")
+    need = lib.pa_decode_multi_workspace_size(S, Tq, int(max_query_len), Hq, Hkv, D, bs, MB, kvd,
+                                              int(partition_tokens))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pa_decode_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                             context_lens.data_ptr(), query_start.data_ptr(), float(scale), out.data_ptr(), S, Tq,
+                             int(max_query_len), Hq, Hkv, D, bs, MB, N, kvd, float(k_scale), float(v_scale),
+                             ws_ptr, ws_bytes, int(partition_tokens), _stream_ptr(stream))
+    if st != PA_OK:
+        raise PAError(st, "pa_decode_multi")
+    return out
+
+
+def pa_decode_multi_workspace_size(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads,
+                                   head_dim, block_size, max_blocks_per_seq, kv_dtype=PA_KV_BF16,
+                                   partition_tokens=0) -> int:
+    return int(load_library().pa_decode_multi_workspace_size(num_seqs, num_query_tokens, max_query_len,
+                                                             num_q_heads, num_kv_heads, head_dim, block_size,
+                                                             max_blocks_per_seq, kv_dtype, partition_tokens))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
+    """Copy whole physical blocks of both caches [N, bs, Hkv, D] for (src, dst)
+    pairs block_mapping [n, 2] int64 (copy-on-write's copy)."""
+    import torch
+    lib = load_library()
+    _check(k_cache, "k_cache", None, 4)
+    _check(v_cache, "v_cache", None, 4)
+    _check(block_mapping, "block_mapping", torch.int64, 2)
+    kvd = _kv_dtype(k_cache)
+    if _kv_dtype(v_cache) != kvd or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache differ")
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n, 2]")
+    N, bs, Hkv, D = k_cache.shape
+    st = lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
+                            block_mapping.shape[0], Hkv, D, bs, N, kvd, _stream_ptr(stream))
+    if st != PA_OK:
+        raise PAError(st, "pa_copy_blocks")
+
+
 def pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                        kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0,
                        schedule=0) -> dict:
@@ -210,6 +294,38 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, bloc
     return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                        block_size, max_blocks_per_seq, kv_dtype,
                                                        ctypes.byref(o)))
+
+
+def pa_check_cache_write_inputs(slot_mapping, num_blocks: int, block_size: int, stream=None) -> int:
+    """Check pa_cache_write's device-side preconditions (slots distinct, each
+    negative or inside the pool). Synchronises. Returns PA_OK or
+    PA_ERR_PRECONDITION; raises on argument errors."""
+    import torch
+    lib = load_library()
+    _check(slot_mapping, "slot_mapping", torch.int64, 1)
+    st = lib.pa_check_cache_write_inputs(slot_mapping.data_ptr(), slot_mapping.numel(), int(block_size),
+                                         int(num_blocks), _stream_ptr(stream))
+    if st not in (PA_OK, PA_ERR_PRECONDITION):
+        raise PAError(st, "pa_check_cache_write_inputs")
+    return st
+
+
+def pa_check_decode_inputs(block_tables, context_lens, num_blocks: int, block_size: int, stream=None) -> int:
+    """Check pa_decode's device-side preconditions (lengths within the table
+    row, covering table entries inside the pool). Synchronises. Returns PA_OK
+    or PA_ERR_PRECONDITION; raises on argument errors."""
+    import torch
+    lib = load_library()
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    S, MB = block_tables.shape
+    if context_lens.shape != (S,):
+        raise ValueError("shape mismatch")
+    st = lib.pa_check_decode_inputs(block_tables.data_ptr(), context_lens.data_ptr(), S, int(block_size), MB,
+                                    int(num_blocks), _stream_ptr(stream))
+    if st not in (PA_OK, PA_ERR_PRECONDITION):
+        raise PAError(st, "pa_check_decode_inputs")
+    return st
 
 
 def fp8_encode_host(x) -> "numpy.ndarray":

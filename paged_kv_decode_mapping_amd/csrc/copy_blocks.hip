@@ -1,0 +1,55 @@
+// copy_blocks.hip -- duplicate physical blocks of the paged caches: the copy
+// step of copy-on-write.
+//
+// Tutorial «大模型推理优化与加速完全教程» §4.2 lists copy-on-write among
+// PagedKVCache's features (beam search forks share blocks), and §4.3
+// "Prefix Caching" shares a prefix's blocks between sequences. Before one
+// sharer may append into a shared block, the block is duplicated into a
+// free one and that sharer's table entry is repointed. This kernel does the
+// duplication: for each (src, dst) pair, block dst of K and of V becomes a
+// byte-for-byte copy of block src (all rows, all KV heads).
+//
+// Workgroup (x, p) copies 16-byte chunks x*256 + t, x*256 + t + stride, ...
+// of pair p's block in both caches: plain coalesced streaming copies (the
+// data is read once and written once, so the loads and stores are marked
+// non-temporal). Pairs with a negative or out-of-pool id are skipped.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kCopyThreads = 256;
+
+__global__ __launch_bounds__(kCopyThreads) void pa_copy_blocks_kernel(CopyBlocksArgs a) {
+    const int64_t p = blockIdx.y;
+    const int64_t src = a.pairs[2 * p];
+    const int64_t dst = a.pairs[2 * p + 1];
+    if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks) return;
+    const int64_t chunks = a.block_bytes / 16;
+    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k_cache + src * a.block_bytes);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_cache + src * a.block_bytes);
+    u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + dst * a.block_bytes);
+    u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + dst * a.block_bytes);
+    const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < chunks; i += stride) {
+        const u32x4 k = __builtin_nontemporal_load(ks + i);
+        const u32x4 v = __builtin_nontemporal_load(vs + i);
+        __builtin_nontemporal_store(k, kd + i);
+        __builtin_nontemporal_store(v, vd + i);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
+    const int64_t chunks = a.block_bytes / 16;
+    // up to 8 workgroups per block pair, each thread moving >= 1 chunk of K and of V
+    int64_t gx = (chunks + kCopyThreads - 1) / kCopyThreads;
+    if (gx > 8) gx = 8;
+    const dim3 grid((unsigned)gx, (unsigned)a.num_pairs);
+    hipLaunchKernelGGL(pa_copy_blocks_kernel, grid, dim3(kCopyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pa

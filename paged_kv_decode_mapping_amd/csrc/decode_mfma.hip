@@ -62,10 +62,10 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4&
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
-// Occupancy the register allocator is asked to keep: 3 waves per SIMD for the
-// rings of 2 and 3 tiles (<= 168 VGPRs), 2 for the deepest ring.
+// Occupancy the register allocator is asked to keep: 4 waves per SIMD (<= 128
+// VGPRs) for the ring of 2 tiles, 3 (<= 168) for 3 tiles, 2 for 4 tiles.
 template <int NB>
-constexpr int mfma_waves_per_eu() { return NB <= 3 ? 3 : 2; }
+constexpr int mfma_waves_per_eu() { return NB <= 2 ? 4 : (NB == 3 ? 3 : 2); }
 
 template <int D, bool FP8, int NB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<NB>())))
@@ -93,16 +93,20 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RS + 4 * (lane & 3);
 
         // Q^T operands: MFMA j takes d = 32 j + 8 gq + 0..7 of head c, the d
-        // range of the lane's K operand of MFMA j.
-        bf16x8 qb[NQK];
-#pragma unroll
-        for (int j = 0; j < NQK; ++j) {
+        // range of the lane's K operand of MFMA j. The group's q rows (zero
+        // rows past g) sit in LDS after the staging tiles and are read per
+        // tile, which keeps 16 registers per lane free for the load ring.
+        uint16_t* qs = reinterpret_cast<uint16_t*>(smem) + W * 2 * kTile * RS;
+        for (int i = (int)threadIdx.x; i < kTile * (D / 8); i += (int)blockDim.x) {
+            const int h = i / (D / 8);
+            const int d8 = i - h * (D / 8);
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (c < g)
-                w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + c) * D +
-                                                    32 * j + 8 * gq);
-            qb[j] = __builtin_bit_cast(bf16x8, w);
+            if (h < g)
+                w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + h) * D + 8 * d8);
+            *reinterpret_cast<u32x4*>(qs + h * RS + 8 * d8) = w;
         }
+        __syncthreads();
+        const uint16_t* q_row = qs + c * RS + 8 * gq;
 
         float m = -INFINITY;  // running max of head c (log2 units), same in all four lane groups
         float l = 0.0f;       // running sum over this lane's tokens
@@ -113,12 +117,11 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         const int span = wi.t_end - wi.t_begin;
         const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
         const uint32_t head_off = (uint32_t)wi.kvh * a.head_bytes;
-        // per-lane byte offsets inside a tile (the same for K and V), fixed
-        // for the whole item: load i of lane l covers row i * RPI + l / LPR
-        uint32_t roff[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            roff[i] = (uint32_t)(i * RPI + lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
+        // per-lane byte offset inside a tile (the same for K and V), fixed for
+        // the whole item: load i of lane l covers row i * RPI + l / LPR; the
+        // i * RPI rows go into the wave-uniform offset
+        const uint32_t roff = (uint32_t)(lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
+        const uint32_t rstep = (uint32_t)RPI * a.slot_bytes;
         const int bs_mask = (1 << a.block_size_log2) - 1;
         const float qk = a.qk_scale_log2;
 
@@ -135,19 +138,18 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         // Wave w takes tiles w, w + W, w + 2W, ... of the item.
         const int t_first = wave, t_step = W, t_stop = ntiles;
 
-        auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
+        auto issue = [&](int t, int64_t blk, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
             const bool live = t < t_stop;
             const int t0 = wi.t_begin + (live ? t : t_stop - 1) * kTile;
-            const int64_t blk = physical_block(a, wi.seq, t0);
             const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
             const int valid = min(wi.t_end - t0, kTile);
             const uint32_t nbytes = live ? row0 + (uint32_t)valid * a.slot_bytes : 0u;
             const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
             const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) kb[i] = buf_load_b128_stream(rk, roff[i], row0);
+            for (int i = 0; i < NI; ++i) kb[i] = buf_load_b128_stream(rk, roff, row0 + i * rstep);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) vb[i] = buf_load_b128_stream(rv, roff[i], row0);
+            for (int i = 0; i < NI; ++i) vb[i] = buf_load_b128_stream(rv, roff, row0 + i * rstep);
         };
 
         auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
@@ -181,7 +183,8 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
                 const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j], s, 0, 0, 0);
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
             }
 
             // online softmax for head c over tokens 4*gq + r
@@ -240,12 +243,24 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             // the same loads in flight and the waits before a tile's use
             // leave the prefetch behind it outstanding. sched_barrier keeps
             // the compiler from sinking the prefetch below those waits.
+            // The table entry of each issued tile was fetched one step earlier.
+            const TableReader tab = make_table_reader(a, wi, t_stop - 1);
+            uint32_t entry = table_fetch(tab, t_first);
 #pragma unroll
-            for (int b = 0; b < NB - 1; ++b) issue(t_first + b * t_step, kb[b], vb[b]);
+            for (int b = 0; b < NB - 1; ++b) {
+                const int64_t blk = table_block(tab, entry);
+                entry = table_fetch(tab, t_first + (b + 1) * t_step);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(t_first + b * t_step, blk, kb[b], vb[b]);
+            }
             for (int t = t_first; t < t_stop; t += NB * t_step) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    issue(t + (b + NB - 1) * t_step, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                    const int ti = t + (b + NB - 1) * t_step;
+                    const int64_t blk = table_block(tab, entry);
+                    entry = table_fetch(tab, ti + t_step);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue(ti, blk, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
                     __builtin_amdgcn_sched_barrier(0);
                     if (t + b * t_step < t_stop) consume(t + b * t_step, kb[b], vb[b]);
                 }
@@ -277,7 +292,7 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
 template <int D, bool FP8, int NB>
 hipError_t launch_d(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
     const dim3 block((unsigned)(64 * ls.waves));
-    const size_t stage = (size_t)ls.waves * 2 * kTile * (D + 8) * sizeof(uint16_t);
+    const size_t stage = ((size_t)ls.waves * 2 + 1) * kTile * (D + 8) * sizeof(uint16_t);
     const size_t comb = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
     const size_t lds = stage > comb ? stage : comb;
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));

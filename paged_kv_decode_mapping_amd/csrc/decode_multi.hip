@@ -1,0 +1,398 @@
+// decode_multi.hip -- paged attention for several query rows per KV head:
+// multi-token queries (speculative verification, chunked prefill) and GQA
+// groups wider than one 16-row matrix tile (MQA).
+//
+// Pages cited (titles as printed at the top of each page):
+//   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
+//   ToPG     = «ToPG框架解析：大模型推理性能优化与三阶段流水线设计»
+//
+// What it computes. Sequence i has context_lens[i] = L cached tokens; its
+// last n = query_start[i+1] - query_start[i] are its query tokens (already
+// written to the cache). Query r sits at position p = L - n + r and, for
+// each query head h, attends over positions 0..p (causal) of KV head h / g:
+// the target model's single verification pass over K draft tokens of
+// Tutorial §5.1 (speculative decoding), a prefill chunk over its cached
+// prefix as in Tutorial §6.2 (chunked prefill), and, with n = 1, the decode
+// step of Tutorial §4.4 (GroupedQueryAttention) for any group size, MQA
+// included. Gather through the block table as in Tutorial §4.2 (get_kv).
+//
+// Rows. The (query token r, head hh) pairs of one (sequence, KV head) are
+// rows rho = r * g + hh; every wave of a workgroup owns one 16-row tile of
+// them (W waves: 16 W rows), so the online-softmax state of a row never
+// leaves its lanes and a workgroup needs no combine step. Rows are the
+// columns of the same MFMA tiles the decode kernel uses:
+//   S = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q^T rows
+//               of this wave from LDS;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, A = V^T by the transposing LDS
+//               read, B = the lane's own probabilities (bf16).
+// Lane (c, gq) holds S[token 4 gq + r][row c]: the causal mask compares the
+// token with the position of row c.
+//
+// Tiles. The workgroup walks its token range in 16-token tiles; all waves
+// use every tile, so the tile is loaded once, cooperatively (each lane one
+// or more 16-byte chunks of K and of V), and staged in LDS. Each lane keeps
+// a ring of NB tiles of its chunks in registers (NB - 1 in flight), and the
+// LDS copy is double-buffered, so one workgroup barrier per tile orders
+// both the staging before the reads and the reads before the next overwrite.
+// fp8 codes are widened to bf16 while staging (exact); the scales are folded
+// into the score scale and the output (ToPG §2: fp32 accumulation; ToPG §3:
+// fp8 KV).
+//
+// Split-K. A workgroup covers one partition of at most P tokens; with more
+// than one partition it stores unnormalised partial states (m, l, o) per row
+// and pa_multi_merge_kernel combines them by log-sum-exp.
+#include "pa_epilogue.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void fp8x16_to_bf16_m(const u32x4& w, u32x4& lo, u32x4& hi) {
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+        r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    }
+    lo = u32x4{r[0], r[1], r[2], r[3]};
+    hi = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+// Work item of a workgroup: (sequence, KV head, row block, partition).
+struct MultiItem {
+    int seq, kvh, rb, part;
+    int L;        // context length (clamped to the table row)
+    int q0, n;    // first query row and number of query tokens
+};
+
+template <int D, bool FP8, int W, int NB>
+__global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr int NQK = D / 32;
+    constexpr int NPV = D / 16;
+    constexpr int EPL = 16 / ESZ;            // elements per 16-byte chunk
+    constexpr int LPR = D / EPL;             // chunks per token row
+    constexpr int CHUNKS = kTile * LPR;      // chunks per tile (of K, and of V)
+    constexpr int NI = (CHUNKS + 64 * W - 1) / (64 * W);  // chunks per lane
+    constexpr int RS = D + 8;                // LDS row stride, bf16 elements
+    static_assert(NB % 2 == 0, "the LDS buffer of a ring slot is its parity");
+
+    extern __shared__ float smem[];
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);  // [16 W][RS] query rows
+    uint16_t* kbuf = qs + 16 * W * RS;                  // [2][16][RS]
+    uint16_t* vbuf = kbuf + 2 * kTile * RS;             // [2][16][RS]
+
+    // ---- the work item
+    int bid = (int)blockIdx.x;
+    MultiItem it;
+    it.part = bid % a.num_partitions;
+    bid /= a.num_partitions;
+    it.rb = bid % a.row_blocks;
+    bid /= a.row_blocks;
+    it.kvh = bid % a.num_kv_heads;
+    it.seq = bid / a.num_kv_heads;
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    int L = a.context_lens[it.seq];
+    it.L = L < 0 ? 0 : (L > cap ? cap : L);
+    if (a.query_start != nullptr) {
+        it.q0 = a.query_start[it.seq];
+        int n = a.query_start[it.seq + 1] - it.q0;
+        n = n > a.max_query_len ? a.max_query_len : n;
+        // rows outside [0, num_query_rows) are never touched, whatever query_start holds
+        if (it.q0 < 0 || it.q0 > a.num_query_rows) n = 0;
+        else if (n > a.num_query_rows - it.q0) n = a.num_query_rows - it.q0;
+        it.n = n < 0 ? 0 : n;
+    } else {
+        it.q0 = it.seq;
+        it.n = 1;
+    }
+    const int g = a.group;
+    const int rows = it.n * g;
+    const int row0 = it.rb * 16 * W;
+    if (row0 >= rows) return;
+    // the last position any row of this block attends to
+    const int last_row = min(rows, row0 + 16 * W) - 1;
+    const int pos_max = it.L - it.n + last_row / g;
+    const int t_begin = it.part * a.partition_tokens;
+    const int t_end = min(min(t_begin + a.partition_tokens, pos_max + 1), it.L);
+    if (it.part > 0 && t_begin >= t_end) return;  // nothing of this block here (partition 0 always stores)
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = (int)(threadIdx.x & 63);
+    const int c = lane & 15;
+    const int gq = lane >> 4;
+
+    // ---- query rows of this block -> LDS (zero rows past the block's rows)
+    for (int i = (int)threadIdx.x; i < 16 * W * (D / 8); i += 64 * W) {
+        const int rr = i / (D / 8);
+        const int d8 = i - rr * (D / 8);
+        const int rho = row0 + rr;
+        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        if (rho < rows) {
+            const int r = rho / g, hh = rho - (rho / g) * g;
+            w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh) * D + 8 * d8);
+        }
+        *reinterpret_cast<u32x4*>(qs + rr * RS + 8 * d8) = w;
+    }
+
+    // this lane's row (column c of the wave's tile) and its causal limit
+    const int my_rho = row0 + wave * 16 + c;
+    const bool my_valid = my_rho < rows;
+    const int my_pos = my_valid ? it.L - it.n + my_rho / g : -1;  // sees tokens <= my_pos
+    const uint16_t* q_row = qs + (wave * 16 + c) * RS + 8 * gq;
+
+    float m = -INFINITY, l = 0.0f;
+    f32x4 o[NPV];
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int span = t_end - t_begin;
+    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
+    const uint32_t head_off = (uint32_t)it.kvh * a.head_bytes;
+    const int bs_mask = (1 << a.block_size_log2) - 1;
+    const float qk = a.qk_scale_log2;
+
+    // chunk i of this lane: id k = tid + 64 W i -> token row k / LPR, chunk k % LPR
+    uint32_t coff[NI];
+    bool cown[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k = (int)threadIdx.x + 64 * W * i;
+        cown[i] = k < CHUNKS;
+        const int kk = cown[i] ? k : 0;
+        // a lane past the tile's chunks reads past every descriptor (zeros)
+        coff[i] = cown[i] ? (uint32_t)(kk / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(kk % LPR) : 0x7fffffffu;
+    }
+
+    u32x4 kb[NB][NI], vb[NB][NI];
+
+    __syncthreads();  // query rows in LDS
+
+    if (ntiles > 0) {
+        const TableReader tab = make_table_reader(a.block_tables, a.max_blocks_per_seq, a.block_size_log2,
+                                                  a.last_block, it.seq, t_begin, ntiles - 1);
+
+        auto issue = [&](int t, int64_t blk, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+            const bool live = t < ntiles;
+            const int t0 = t_begin + (live ? t : ntiles - 1) * kTile;
+            const uint32_t rowb = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
+            const int valid = min(t_end - t0, kTile);
+            const uint32_t nbytes = live ? rowb + (uint32_t)valid * a.slot_bytes : 0u;
+            const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
+            const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) kr[i] = buf_load_b128_stream(rk, coff[i], rowb);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vr[i] = buf_load_b128_stream(rv, coff[i], rowb);
+        };
+
+        auto stage = [&](uint16_t* dst, const u32x4& w, int k) {
+            const int row = k / LPR, ch = k % LPR;
+            if constexpr (!FP8) {
+                *reinterpret_cast<u32x4*>(dst + row * RS + ch * 8) = w;
+            } else {
+                u32x4 lo, hi;
+                fp8x16_to_bf16_m(w, lo, hi);
+                *reinterpret_cast<u32x4*>(dst + row * RS + ch * 16) = lo;
+                *reinterpret_cast<u32x4*>(dst + row * RS + ch * 16 + 8) = hi;
+            }
+        };
+
+        auto consume = [&](int t, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], int buf) {
+            uint16_t* ks = kbuf + buf * kTile * RS;
+            uint16_t* vs = vbuf + buf * kTile * RS;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                if (cown[i]) {
+                    const int k = (int)threadIdx.x + 64 * W * i;
+                    stage(ks, kr[i], k);
+                    stage(vs, vr[i], k);
+                }
+            }
+            __syncthreads();  // the tile is in LDS; the other buffer's readers are done
+
+            const int t0 = t_begin + t * kTile;
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NQK; ++j) {
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
+            }
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = t0 + 4 * gq + r;
+                x[r] = (tok > my_pos || tok >= t_end) ? -INFINITY : s[r] * qk;
+            }
+            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            mx = fmaxf(mx, xor_shfl(mx, 16));
+            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float m_new = fmaxf(m, mx);
+            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m - ms);
+            const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
+            m = m_new;
+            bf16x4 pb;
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
+                pb[r] = b;
+                psum += (float)b;
+            }
+            l = fmaf(l, alpha, psum);
+            if (moved) {
+#pragma unroll
+                for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+            }
+            // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c]
+            const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RS + 4 * (lane & 3);
+#pragma unroll
+            for (int j = 0; j < NPV; ++j) {
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                typedef __attribute__((address_space(3))) uint16_t lds_u16;
+                lds_s16x4* src = (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_base) + 16 * j);
+                const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
+            }
+        };
+
+        uint32_t entry = table_fetch(tab, 0);
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b) {
+            const int64_t blk = table_block(tab, entry);
+            entry = table_fetch(tab, b + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(b, blk, kb[b], vb[b]);
+        }
+        for (int t = 0; t < ntiles; t += NB) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int ti = t + b + NB - 1;
+                const int64_t blk = table_block(tab, entry);
+                entry = table_fetch(tab, ti + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(ti, blk, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (t + b < ntiles) consume(t + b, kb[b], vb[b], b & 1);  // uniform over the workgroup
+            }
+        }
+    }
+
+    // ---- store this lane's row (the four lane groups hold disjoint tokens)
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    if (!my_valid) return;
+    const int r = my_rho / g, hh = my_rho - (my_rho / g) * g;
+    const int64_t row = (int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh;
+    if (a.num_partitions == 1) {
+        const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[j][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[j][1] * inv) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[j][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[j][3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(a.out + row * D + 16 * j + 4 * gq) = u32x2{lo, hi};
+        }
+    } else {
+        const int64_t prow = row * a.num_partitions + it.part;
+#pragma unroll
+        for (int j = 0; j < NPV; ++j)
+            *reinterpret_cast<f32x4*>(a.part_o + prow * D + 16 * j + 4 * gq) = o[j] * a.v_scale;
+        if (gq == 0) {
+            a.part_ml[prow * 2] = m;
+            a.part_ml[prow * 2 + 1] = l;
+        }
+    }
+}
+
+// One wave per (query row, query head): log-sum-exp merge of the partitions
+// that hold tokens the row attends to (positions 0..p).
+template <int D>
+__global__ __launch_bounds__(256) void pa_multi_merge_kernel(MultiArgs a) {
+    const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int lane = (int)(threadIdx.x & 63);
+    const int64_t total = (int64_t)a.num_query_rows * a.num_q_heads;
+    if (wid >= total) return;
+    const int qrow = (int)(wid / a.num_q_heads);
+    // the sequence of this query row: the last i with query_start[i] <= qrow
+    int seq, q0, n;
+    if (a.query_start != nullptr) {
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.query_start[mid] <= qrow) lo = mid;
+            else hi = mid - 1;
+        }
+        seq = lo;
+        q0 = a.query_start[seq];
+        n = a.query_start[seq + 1] - q0;
+        n = n > a.max_query_len ? a.max_query_len : n;
+        if (q0 < 0 || q0 > a.num_query_rows) n = 0;
+        else if (n > a.num_query_rows - q0) n = a.num_query_rows - q0;
+        n = n < 0 ? 0 : n;
+    } else {
+        seq = qrow;
+        q0 = qrow;
+        n = 1;
+    }
+    const int r = qrow - q0;
+    if (r < 0 || r >= n) return;  // not a row of this sequence's queries (malformed query_start)
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    int L = a.context_lens[seq];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int pos = L - n + r;
+    const int np = pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
+    const float* ml = a.part_ml + wid * a.num_partitions * 2;
+    const float* po = a.part_o + wid * a.num_partitions * D;
+    float M = -INFINITY;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+    for (int d = lane; d < D; d += 64) {
+        float Lsum = 0.0f, O = 0.0f;
+        if (M != -INFINITY) {
+            for (int p = 0; p < np; ++p) {
+                const float f = state_weight(ml[2 * p], M);
+                Lsum += ml[2 * p + 1] * f;
+                O += po[(int64_t)p * D + d] * f;
+            }
+        }
+        a.out[wid * D + d] = f32_to_bf16_rne(Lsum > 0.0f ? O / Lsum : 0.0f);
+    }
+}
+
+template <int D, bool FP8, int W>
+hipError_t launch_w(const MultiArgs& a, hipStream_t s) {
+    constexpr int NB = W == 1 ? 2 : 4;
+    const size_t lds = ((size_t)16 * W + 4 * kTile) * (D + 8) * sizeof(uint16_t);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.row_blocks * a.num_partitions));
+    hipLaunchKernelGGL((pa_multi_kernel<D, FP8, W, NB>), grid, dim3(64 * W), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_df(const MultiArgs& a, int waves, hipStream_t s) {
+    if (waves <= 1) return launch_w<D, FP8, 1>(a, s);
+    if (waves == 2) return launch_w<D, FP8, 2>(a, s);
+    return launch_w<D, FP8, 4>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, hipStream_t s) {
+    hipError_t e;
+    if (head_dim == 64) e = fp8 ? launch_df<64, true>(a, waves, s) : launch_df<64, false>(a, waves, s);
+    else e = fp8 ? launch_df<128, true>(a, waves, s) : launch_df<128, false>(a, waves, s);
+    if (e != hipSuccess || a.num_partitions == 1) return e;
+    const int64_t waves_total = (int64_t)a.num_query_rows * a.num_q_heads;
+    const dim3 grid((unsigned)((waves_total * 64 + 255) / 256));
+    if (head_dim == 64) hipLaunchKernelGGL(pa_multi_merge_kernel<64>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(pa_multi_merge_kernel<128>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pa

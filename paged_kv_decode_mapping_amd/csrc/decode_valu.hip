@@ -25,7 +25,7 @@
 //     l, o) over the tokens it sees, so the tile loop needs no cross-row
 //     exchange; the RPI states are combined once, after the loop.
 //   * The block id of a 16-token tile is wave-uniform (block_size >= 16),
-//     fetched with a scalar load, and becomes the base of a buffer resource
+//     fetched one tile ahead, and becomes the base of a buffer resource
 //     limited to that block.
 //   * Each wave keeps a ring of NB tiles in registers: the loads of tile
 //     t + (NB - 1) W are issued before tile t is consumed.
@@ -121,10 +121,9 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
         // zeros without touching memory, and every path through the loop keeps
         // the same number of loads in flight, so the wait before a tile's use
         // never has to drain the prefetch behind it.
-        auto issue = [&](int t, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
+        auto issue = [&](int t, int64_t blk, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
             const bool live = t < ntiles;
             const int t0 = wi.t_begin + (live ? t : ntiles - 1) * kTile;
-            const int64_t blk = physical_block(a, wi.seq, t0);
             const uint32_t row0 = (uint32_t)(t0 & bs_mask);
             // the descriptor ends at the tile's last valid row: rows past the
             // context read as zero, so V needs no masking code
@@ -199,12 +198,24 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
             // the same loads in flight and the waits before a tile's use
             // leave the prefetch behind it outstanding. sched_barrier keeps
             // the compiler from sinking the prefetch below those waits.
+            // The table entry of each issued tile was fetched one step earlier.
+            const TableReader tab = make_table_reader(a, wi, ntiles - 1);
+            uint32_t entry = table_fetch(tab, wave);
 #pragma unroll
-            for (int b = 0; b < NB - 1; ++b) issue(wave + b * W, kb[b], vb[b]);
+            for (int b = 0; b < NB - 1; ++b) {
+                const int64_t blk = table_block(tab, entry);
+                entry = table_fetch(tab, wave + (b + 1) * W);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(wave + b * W, blk, kb[b], vb[b]);
+            }
             for (int t = wave; t < ntiles; t += NB * W) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    issue(t + (b + NB - 1) * W, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+                    const int ti = t + (b + NB - 1) * W;
+                    const int64_t blk = table_block(tab, entry);
+                    entry = table_fetch(tab, ti + W);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue(ti, blk, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
                     __builtin_amdgcn_sched_barrier(0);
                     if (t + b * W < ntiles) consume(t + b * W, kb[b], vb[b]);
                 }

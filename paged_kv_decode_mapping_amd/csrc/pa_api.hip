@@ -1,6 +1,6 @@
 // pa_api.hip -- the C ABI of libpa: argument checks, launch planning and
 // kernel dispatch. Host code only; nothing here reads device memory or
-// synchronises.
+// synchronises (unless PA_DEBUG_VALIDATE asks for the checks of validate.hip).
 //
 // Pages cited (titles as printed at the top of each page):
 //   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
@@ -50,6 +50,8 @@ struct Plan {
     int partition_tokens = 0;
     int num_partitions = 1;
     bool scheduled = true;
+    bool multi = false;          // the multi-row kernel (more than 16 query rows per KV head)
+    int row_blocks = 1;          // multi: blocks of 16 * waves rows per (sequence, KV head)
     int64_t num_workgroups = 0;  // direct grid size, or the item bound when scheduled
     // workspace layout (byte offsets); total = workspace
     size_t items_off = 0, ml_off = 0, o_off = 0;
@@ -65,11 +67,77 @@ int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32
     if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
     if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
-    if (g > 16) return PA_ERR_UNSUPPORTED;
+    if (g > 1024) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(bs) || bs < pa::kTile || bs > 1024) return PA_ERR_UNSUPPORTED;
     const int64_t esz = kv_dtype == PA_KV_BF16 ? 2 : 1;
     if ((int64_t)bs * Hkv * D * esz >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
     if ((int64_t)MB * bs >= (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+// Tokens per partition for `units` independent workgroup groups over
+// contexts of at most `cap` tokens: enough workgroups to fill the chip
+// several times over, but no split while whole contexts already give that
+// and stay short. partition_tokens: 0 = choose, -1 = never split, > 0 =
+// forced (a multiple of the tile).
+int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int64_t* P_out) {
+    const int64_t cap16 = align_up((size_t)cap, pa::kTile);
+    int64_t P;
+    if (partition_tokens > 0) {
+        if (partition_tokens % pa::kTile) return PA_ERR_SHAPE;
+        P = partition_tokens;
+    } else if (partition_tokens < 0) {
+        P = cap16;
+    } else {
+        const int cus = current_cu_count();
+        if (cus <= 0) return PA_ERR_DEVICE;
+        if (cap <= 4096 && units >= 2 * cus) {
+            P = cap16;
+        } else {
+            P = 4096;
+            while (P > 512 && units * ((cap + P - 1) / P) < 4 * cus) P /= 2;
+        }
+    }
+    if (P >= cap16) P = cap16;
+    *P_out = P;
+    return PA_OK;
+}
+
+// Plan of the multi-row kernel: Tq query rows in all, at most maxq per
+// sequence, g = Hq / Hkv heads per KV head, so at most maxq * g rows per
+// (sequence, KV head); one wave per 16 of them, up to 4 waves a workgroup.
+int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+                    int32_t MB, int32_t partition_tokens, Plan* plan) {
+    if (Tq < 0 || maxq < 0) return PA_ERR_SHAPE;
+    Plan p;
+    p.variant = PA_VARIANT_MFMA;
+    p.multi = true;
+    p.scheduled = false;
+    const int g = Hq / Hkv;
+    const int64_t rows = (int64_t)(maxq > 0 ? maxq : 1) * g;
+    p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    p.depth = p.waves == 1 ? 2 : 4;  // register ring of the cooperative tile loads
+    const int64_t rb = (rows + 16 * p.waves - 1) / (16 * p.waves);
+    if (rb >= (int64_t(1) << 20)) return PA_ERR_UNSUPPORTED;
+    p.row_blocks = (int)rb;
+    const int64_t cap = (int64_t)MB * bs;
+    int64_t P = 0;
+    const int st = choose_partition((int64_t)S * Hkv * rb, cap, partition_tokens, &P);
+    if (st != PA_OK) return st;
+    p.partition_tokens = (int)P;
+    p.num_partitions = (int)((cap + P - 1) / P);
+    if (p.num_partitions < 1) p.num_partitions = 1;
+    p.num_workgroups = (int64_t)S * Hkv * rb * p.num_partitions;
+    if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    size_t off = 0;
+    if (p.num_partitions > 1) {
+        const size_t prow = (size_t)Tq * Hq * p.num_partitions;
+        p.ml_off = 0;
+        p.o_off = align_up(prow * 2 * sizeof(float), 256);
+        off = p.o_off + prow * D * sizeof(float);
+    }
+    p.workspace = off;
+    *plan = p;
     return PA_OK;
 }
 
@@ -88,6 +156,15 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
         return PA_ERR_SHAPE;
     p.variant = o.variant != PA_VARIANT_AUTO ? o.variant : (g >= 4 ? PA_VARIANT_MFMA : PA_VARIANT_VALU);
     if (p.variant == PA_VARIANT_VALU && g > 4) return PA_ERR_UNSUPPORTED;
+    if (o.prefetch_tiles < 0 || o.prefetch_tiles > 3) return PA_ERR_SHAPE;
+    if (o.schedule < -1 || o.schedule > 1) return PA_ERR_SHAPE;
+    if (o.waves_per_group != 0 && o.waves_per_group != 1 && o.waves_per_group != 2 &&
+        o.waves_per_group != 4 && o.waves_per_group != 8)
+        return PA_ERR_SHAPE;
+    // More query heads per KV head than one 16-row tile holds (MQA): the
+    // multi-row kernel, one wave per 16 heads (waves, prefetch and schedule
+    // options do not apply to it).
+    if (g > 16) return make_multi_plan(S, S, 1, Hq, Hkv, D, bs, MB, o.partition_tokens, plan);
     // Defaults measured on MI355X: the MFMA kernel's tiles are 16 whole K
     // and V rows (8 KiB per wave for bf16, D = 128), so one tile in flight
     // per wave already covers the memory latency; the VALU kernel for g = 1
@@ -110,27 +187,10 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     // The epilogue stages W * g * (D + 2) floats in LDS; stay within 64 KiB.
     while (p.waves > 1 && (size_t)p.waves * g * (D + 2) * sizeof(float) > 65536) p.waves /= 2;
     const int64_t cap = (int64_t)MB * bs;  // longest context the tables can hold
-    const int64_t cap16 = align_up((size_t)cap, pa::kTile);
     const int64_t units = (int64_t)S * Hkv;
-    int64_t P;
-    if (o.partition_tokens > 0) {
-        if (o.partition_tokens % pa::kTile) return PA_ERR_SHAPE;
-        P = o.partition_tokens;
-    } else if (o.partition_tokens < 0) {
-        P = cap16;
-    } else {
-        const int cus = current_cu_count();
-        if (cus <= 0) return PA_ERR_DEVICE;
-        // Enough workgroups to fill the chip several times over, but no split
-        // while whole contexts already give that and stay short.
-        if (cap <= 4096 && units >= 2 * cus) {
-            P = cap16;
-        } else {
-            P = 4096;
-            while (P > 512 && units * ((cap + P - 1) / P) < 4 * cus) P /= 2;
-        }
-    }
-    if (P >= cap16) P = cap16;
+    int64_t P = 0;
+    st = choose_partition(units, cap, o.partition_tokens, &P);
+    if (st != PA_OK) return st;
     p.partition_tokens = (int)P;
     p.num_partitions = (int)((cap + P - 1) / P);
     if (p.num_partitions < 1) p.num_partitions = 1;
@@ -160,6 +220,48 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     return PA_OK;
 }
 
+// Launch the multi-row kernel for a plan made by make_multi_plan.
+int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+              float scale, void* out, int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv,
+              int32_t D, int32_t bs, int32_t MB, int64_t num_blocks, int32_t kv_dtype, float k_scale,
+              float v_scale, void* workspace, void* stream) {
+    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
+    const int64_t esz = fp8 ? 1 : 2;
+    pa::MultiArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start = query_start;
+    a.out = static_cast<uint16_t*>(out);
+    if (p.num_partitions > 1) {
+        char* ws = static_cast<char*>(workspace);
+        a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
+        a.part_o = reinterpret_cast<float*>(ws + p.o_off);
+    }
+    a.num_seqs = S;
+    a.num_query_rows = Tq;
+    a.max_query_len = maxq;
+    a.num_q_heads = Hq;
+    a.num_kv_heads = Hkv;
+    a.group = Hq / Hkv;
+    a.block_size_log2 = log2i(bs);
+    a.max_blocks_per_seq = MB;
+    a.partition_tokens = p.partition_tokens;
+    a.num_partitions = p.num_partitions;
+    a.row_blocks = p.row_blocks;
+    a.last_block = (int32_t)((num_blocks > INT32_MAX ? (int64_t)INT32_MAX + 1 : num_blocks) - 1);
+    a.head_bytes = (uint32_t)(D * esz);
+    a.slot_bytes = (uint32_t)((int64_t)Hkv * D * esz);
+    a.block_bytes = (uint32_t)((int64_t)bs * Hkv * D * esz);
+    a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    const hipError_t e = pa::launch_multi(a, D, fp8, p.waves, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +282,10 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0) return PA_ERR_ALIGN;
     if (num_tokens * num_kv_heads * (head_dim / 8) >= (int64_t(1) << 40)) return PA_ERR_SHAPE;
+    if (pa::debug_validate_enabled()) {
+        const int vs = pa_check_cache_write_inputs(slot_mapping, num_tokens, block_size, num_blocks, stream);
+        if (vs != PA_OK) return vs;
+    }
     pa::CacheWriteArgs a{};
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
@@ -194,6 +300,29 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
     a.v_scale = kv_dtype == PA_KV_FP8_E4M3FN ? v_scale : 1.0f;
     const hipError_t e =
         pa::launch_cache_write(a, kv_dtype == PA_KV_FP8_E4M3FN, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int32_t kv_dtype, void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_UNSUPPORTED;
+    if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_mapping) & 7u) != 0) return PA_ERR_ALIGN;
+    pa::CopyBlocksArgs a{};
+    a.k_cache = static_cast<uint8_t*>(k_cache);
+    a.v_cache = static_cast<uint8_t*>(v_cache);
+    a.pairs = block_mapping;
+    a.num_pairs = num_pairs;
+    a.num_blocks = num_blocks;
+    a.block_bytes = (int64_t)block_size * num_kv_heads * head_dim * (kv_dtype == PA_KV_BF16 ? 2 : 1);
+    const hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -250,6 +379,15 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
         if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
     }
+    if (pa::debug_validate_enabled()) {
+        const int vs = pa_check_decode_inputs(block_tables, context_lens, num_seqs, block_size,
+                                              max_blocks_per_seq, num_blocks, stream);
+        if (vs != PA_OK) return vs;
+    }
+    if (p.multi)
+        return run_multi(p, q, k_cache, v_cache, block_tables, context_lens, nullptr, scale, out, num_seqs,
+                         num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                         num_blocks, kv_dtype, k_scale, v_scale, workspace, stream);
     const int64_t esz = fp8 ? 1 : 2;
     pa::DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -318,6 +456,56 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     return PA_OK;
 }
 
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                                      int32_t partition_tokens) {
+    if (check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype) != PA_OK)
+        return 0;
+    Plan p;
+    if (make_multi_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, partition_tokens, &p) != PA_OK)
+        return 0;
+    return p.workspace;
+}
+
+int pa_decode_multi(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
+                    int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int64_t num_blocks, int32_t kv_dtype, float k_scale, float v_scale, void* workspace,
+                    size_t workspace_bytes, int32_t partition_tokens, void* stream) {
+    int st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype);
+    if (st != PA_OK) return st;
+    if (num_query_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
+    if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_SHAPE;
+    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
+    if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+        return PA_ERR_DTYPE;
+    Plan p;
+    st = make_multi_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                         block_size, max_blocks_per_seq, partition_tokens, &p);
+    if (st != PA_OK) return st;
+    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(query_start) & 3u))
+        return PA_ERR_ALIGN;
+    if (p.workspace > 0) {
+        if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+    }
+    if (pa::debug_validate_enabled()) {
+        const int vs = pa_check_decode_inputs(block_tables, context_lens, num_seqs, block_size,
+                                              max_blocks_per_seq, num_blocks, stream);
+        if (vs != PA_OK) return vs;
+    }
+    return run_multi(p, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out, num_seqs,
+                     num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, kv_dtype, k_scale, v_scale, workspace, stream);
+}
+
 void pa_fp8_e4m3fn_encode_host(const float* x, uint8_t* codes, int64_t n) {
     if (!x || !codes) return;
     for (int64_t i = 0; i < n; ++i) codes[i] = pa::fp8_e4m3fn_encode(x[i]);
@@ -334,6 +522,7 @@ const char* pa_strerror(int status) {
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
         case PA_ERR_DEVICE: return "the current HIP device could not be queried";
+        case PA_ERR_PRECONDITION: return "a device-side input violates a precondition (slots, tables or lengths)";
         default: return "unknown status";
     }
 }

@@ -124,14 +124,52 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, Body&& body) 
     body(scheduled_item(rec));
 }
 
-// Physical block of a token, clamped into the pool so that a bad table entry
-// cannot address memory outside it. The clamp is 32-bit (table entries are
-// int32) so it stays in scalar registers: a 64-bit compare has no scalar form
-// on gfx9 and would borrow vector registers inside the load pipeline.
-__device__ __forceinline__ int64_t physical_block(const DecodeArgs& a, int seq, int token) {
-    int b = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + (token >> a.block_size_log2)];
+// Block-table reads for a wave's sequence of tiles, one tile ahead. The
+// entry of the next tile a wave will issue is fetched with a vector (buffer)
+// load while the current tile's loads go out. Vector loads complete in issue
+// order, so when the entry is needed one step later the wait for it only
+// covers loads issued before the tile in flight; a scalar load would share
+// its counter with the LDS traffic of the tile being consumed, and since
+// scalar loads may complete out of order the compiler has to wait for all of
+// it before the next issue.
+struct TableReader {
+    __amdgpu_buffer_rsrc_t rsrc;  // this sequence's table row
+    int t_begin;                  // first token of the item
+    int last_tile;                // entries past the item's last tile read its entry
+    int block_size_log2;
+    int last_block;
+};
+
+__device__ __forceinline__ TableReader make_table_reader(const int32_t* block_tables, int max_blocks_per_seq,
+                                                         int block_size_log2, int last_block, int seq,
+                                                         int t_begin, int last_tile) {
+    TableReader r;
+    r.rsrc = make_rsrc(block_tables + (int64_t)seq * max_blocks_per_seq, (uint32_t)max_blocks_per_seq * 4u);
+    r.t_begin = t_begin;
+    r.last_tile = last_tile;
+    r.block_size_log2 = block_size_log2;
+    r.last_block = last_block;
+    return r;
+}
+
+__device__ __forceinline__ TableReader make_table_reader(const DecodeArgs& a, const WorkItem& wi, int last_tile) {
+    return make_table_reader(a.block_tables, a.max_blocks_per_seq, a.block_size_log2, a.last_block, wi.seq,
+                             wi.t_begin, last_tile);
+}
+
+// Start fetching the table entry of tile t (an index within the item).
+__device__ __forceinline__ uint32_t table_fetch(const TableReader& r, int t) {
+    const int tok = r.t_begin + min(t, r.last_tile) * kTile;
+    return __builtin_amdgcn_raw_buffer_load_b32(r.rsrc, (uint32_t)(tok >> r.block_size_log2) << 2, 0, 0);
+}
+
+// The physical block of a fetched entry, clamped into the pool so that a bad
+// table entry cannot address memory outside it. The clamp is 32-bit (table
+// entries are int32) so it stays in scalar registers.
+__device__ __forceinline__ int64_t table_block(const TableReader& r, uint32_t entry) {
+    int b = __builtin_amdgcn_readfirstlane((int)entry);
     b = b < 0 ? 0 : b;
-    b = b > a.last_block ? a.last_block : b;
+    b = b > r.last_block ? r.last_block : b;
     return (int64_t)b;
 }
 

@@ -65,6 +65,37 @@ struct CacheWriteArgs {
     float k_scale, v_scale;        // fp8 only
 };
 
+// Arguments of the multi-row kernel (several query tokens per sequence,
+// or more than 16 query heads per KV head), passed by value.
+struct MultiArgs {
+    const uint16_t* q;             // [num_query_rows, Hq, D] bf16
+    const uint8_t* k_cache;        // [N, bs, Hkv, D] bf16 or e4m3fn
+    const uint8_t* v_cache;
+    const int32_t* block_tables;   // [S, MB]
+    const int32_t* context_lens;   // [S]
+    const int32_t* query_start;    // [S + 1]; null = one query token per sequence (row = seq)
+    uint16_t* out;                 // [num_query_rows, Hq, D] bf16
+    float* part_ml;                // [num_query_rows, Hq, P, 2], split only
+    float* part_o;                 // [num_query_rows, Hq, P, D], split only
+    int32_t num_seqs, num_query_rows, max_query_len;
+    int32_t num_q_heads, num_kv_heads, group;
+    int32_t block_size_log2, max_blocks_per_seq;
+    int32_t partition_tokens, num_partitions;
+    int32_t row_blocks;            // blocks of 16 * waves rows per (sequence, KV head)
+    int32_t last_block;
+    uint32_t block_bytes, slot_bytes, head_bytes;
+    float qk_scale_log2, v_scale;
+};
+
+struct CopyBlocksArgs {
+    uint8_t* k_cache;              // [N, bs, Hkv, D]
+    uint8_t* v_cache;
+    const int64_t* pairs;          // [num_pairs][2] (src, dst)
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_bytes;           // bs * Hkv * D * element size (a multiple of 16)
+};
+
 // How a decode kernel is launched.
 struct LaunchShape {
     int waves;          // wavefronts per workgroup
@@ -77,5 +108,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, const
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+// the multi-row kernel, then (split) its merge
+hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, hipStream_t s);
+
+// PA_DEBUG_VALIDATE set (and not "0"): the hot-path calls first run the
+// precondition checks of validate.hip.
+bool debug_validate_enabled();
 
 }  // namespace pa

@@ -26,12 +26,20 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+# The sources that decide what pa_decode launches and what its kernels do:
+# the launch plan, the decode kernels, the work-list and merge kernels and
+# the headers they include. Other kernels (cache write, block copy, the
+# multi-token kernel) and the host-side checks do not change its traffic.
+DECODE_SOURCES = ("pa_api.hip", "decode_mfma.hip", "decode_valu.hip", "schedule.hip", "merge.hip",
+                  "pa_epilogue.h", "pa_device.h", "pa_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_decode_mapping_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in DECODE_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

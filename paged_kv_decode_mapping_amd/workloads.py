@@ -312,3 +312,35 @@ def make_workload(name_or_spec, *, seed: Optional[int] = None, num_seqs: Optiona
 def reduced(name: str, num_seqs: int, context: Sequence[int], **kw) -> Workload:
     """Same structure as a named workload at a size the oracle finishes in seconds."""
     return make_workload(name, num_seqs=num_seqs, context=("list", list(context)), **kw)
+
+
+@dataclasses.dataclass
+class MultiQuery:
+    """Query tokens for multi-token paged attention over a generated workload:
+    sequence i's last q_lens[i] cached tokens are its queries (draft tokens
+    being verified, or a prefill chunk whose K/V are already written)."""
+
+    q: np.ndarray             # uint16 [T_q, Hq, D] bf16 bits, sequence-major
+    query_start: np.ndarray   # int32 [S + 1], query_start[i+1] - query_start[i] = q_lens[i]
+    q_lens: np.ndarray        # int32 [S]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+
+def make_multi_query(w: Workload, q_lens, *, seed: Optional[int] = None) -> MultiQuery:
+    """Draw N(0,1) bf16 query rows for q_lens[i] query tokens of each sequence of
+    `w` (each at most that sequence's context length). Seeded, one stream."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    s = w.spec
+    if q_lens.shape != (s.num_seqs,):
+        raise ValueError("one query length per sequence")
+    if np.any(q_lens < 0) or np.any(q_lens > w.context_lens):
+        raise ValueError("query lengths must lie in [0, context length]")
+    rng = np.random.default_rng(s.seed + 7919 if seed is None else seed)
+    T = int(q_lens.sum())
+    q = _to_bf16_bits(rng.standard_normal((T, s.num_q_heads, s.head_dim), dtype=np.float32))
+    qs = np.zeros(s.num_seqs + 1, dtype=np.int64)
+    qs[1:] = np.cumsum(q_lens)
+    return MultiQuery(q=q, query_start=qs.astype(np.int32), q_lens=q_lens.astype(np.int32))

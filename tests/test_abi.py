@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = pa.strerror(code)
         assert s and s != "unknown status"
     assert pa.strerror(-99) == "unknown status"
@@ -82,7 +82,7 @@ def _reserved(v):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(D=96), -3), (dict(D=256), -3), (dict(Hq=6, Hkv=4), -2), (dict(Hq=64, Hkv=2), -3),
+    (dict(D=96), -3), (dict(D=256), -3), (dict(Hq=6, Hkv=4), -2), (dict(Hq=2050, Hkv=2), -3), (dict(Hq=64, Hkv=2, opts=pa._opts(variant="valu")), -3),
     (dict(bs=8), -3), (dict(bs=24), -3), (dict(kvd=7), -5), (dict(MB=0), -2), (dict(S=-1), -2),
     (dict(N=0), -2), (dict(q=None), -1), (dict(bt=None), -1), (dict(out=A + 8), -4), (dict(k=A + 2), -4),
     (dict(kvd=2, ks=0.0), -5), (dict(kvd=2, vs=float("nan")), -5), (dict(scale=float("inf")), -2),
@@ -149,3 +149,51 @@ def test_cache_write_rejects_bad_arguments(lib, kw, code):
 
 def test_cache_write_zero_tokens_is_a_no_op(lib):
     assert _cw(lib, T=0, k=None, v=None, slots=None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 4, 16, 32), -1), ((A, -1, 16, 32), -2), ((A, 4, 0, 32), -2), ((A, 4, 16, 0), -2),
+    ((None, 0, 16, 32), 0),
+])
+def test_cache_write_check_argument_errors(lib, args, code):
+    """The precondition check validates its own arguments before touching the device."""
+    assert lib.pa_check_cache_write_inputs(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, A, 4, 16, 7, 32), -1), ((A, None, 4, 16, 7, 32), -1), ((A, A, -1, 16, 7, 32), -2),
+    ((A, A, 4, 16, 0, 32), -2), ((A, A, 4, 16, 7, 0), -2), ((None, None, 0, 16, 7, 32), 0),
+])
+def test_decode_check_argument_errors(lib, args, code):
+    assert lib.pa_check_decode_inputs(*args, None) == code
+
+
+def _multi(lib, **kw):
+    args = dict(q=A, k=A, v=A, bt=A, cl=A, qs=A, scale=0.125, out=A, S=4, Tq=10, maxq=4, Hq=8, Hkv=2, D=64,
+                bs=16, MB=7, N=32, kvd=1, ks=1.0, vs=1.0, ws=None, wsb=0, part=-1)
+    args.update(kw)
+    return lib.pa_decode_multi(args["q"], args["k"], args["v"], args["bt"], args["cl"], args["qs"], args["scale"],
+                               args["out"], args["S"], args["Tq"], args["maxq"], args["Hq"], args["Hkv"], args["D"],
+                               args["bs"], args["MB"], args["N"], args["kvd"], args["ks"], args["vs"], args["ws"],
+                               args["wsb"], args["part"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), -3), (dict(Hq=6, Hkv=4), -2), (dict(Tq=-1), -2), (dict(maxq=-2), -2), (dict(qs=None), -1),
+    (dict(out=A + 8), -4), (dict(qs=A + 2), -4), (dict(kvd=2, ks=0.0), -5), (dict(part=24), -2),
+    (dict(part=32), -6), (dict(part=32, ws=A + 16, wsb=1 << 24), -4), (dict(bs=8), -3), (dict(N=0), -2),
+])
+def test_multi_rejects_bad_arguments_without_launching(lib, kw, code):
+    assert _multi(lib, **kw) == code
+
+
+def test_multi_nothing_to_do_is_a_no_op(lib):
+    assert _multi(lib, S=0, q=None, out=None) == 0
+    assert _multi(lib, Tq=0, q=None, out=None) == 0
+
+
+def test_multi_workspace_size(lib):
+    assert pa.pa_decode_multi_workspace_size(4, 10, 4, 8, 2, 64, 16, 7, partition_tokens=-1) == 0
+    n = pa.pa_decode_multi_workspace_size(4, 10, 4, 8, 2, 64, 16, 7, partition_tokens=32)
+    P = -(-7 * 16 // 32)
+    assert n == _align(10 * 8 * P * 2 * 4) + 10 * 8 * P * 64 * 4

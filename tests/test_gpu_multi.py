@@ -1,0 +1,131 @@
+"""GPU parity of multi-token paged attention (pa_decode_multi) and of
+pa_decode with more than 16 query heads per KV head (MQA), against the
+float64 oracle, through the C ABI. Tolerances as for decode: max |err|
+1e-2, mean 1e-3 with bf16 KV; 5e-2 / 5e-3 with fp8 KV (same cache codes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_mapping_amd as pa
+from paged_kv_decode_mapping_amd import workloads as W
+
+from _gpu_util import DeviceWorkload, compare, host_bits, note
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = (1e-2, 1e-3)
+FP8_TOL = (5e-2, 5e-3)
+
+
+@pytest.fixture(scope="module")
+def lib(gpu):
+    return pa.load_library()
+
+
+CASES = {
+    # name: (workload kwargs, query lengths)
+    "tiny_mixed_lengths": ("tiny", dict(), [1, 5, 16, 4]),
+    "spec_verify_70b": ("llama70b_gqa", dict(num_seqs=3, context=("list", [4096, 1234, 17])), [4, 4, 4]),
+    "spec_verify_mixed": ("mixed_batch", dict(num_seqs=6, context=("list", [16, 100, 511, 900, 3000, 77])),
+                          [8, 1, 8, 5, 8, 0]),
+    "chunk_prefill": ("mixed_batch", dict(num_seqs=3, context=("list", [600, 1500, 100])), [100, 37, 100]),
+    "long_bs128": ("long_splitk", dict(num_seqs=2, context=("list", [5000, 2049])), [16, 3]),
+    "mha_multi": ("llama7b_mha", dict(num_seqs=3, context=("list", [512, 1000, 33])), [6, 2, 33]),
+}
+
+
+def _run(name, partition=0, kv="bf16"):
+    base, kw, qlens = CASES[name]
+    w = W.make_workload(base, **kw)
+    mq = W.make_multi_query(w, qlens)
+    kc, vc, ks, vs = w.k_cache, w.v_cache, 1.0, 1.0
+    kvd = oracle.KV_BF16
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd = oracle.KV_FP8_E4M3FN
+    ref = oracle.multi_decode(mq.q, kc, vc, w.block_tables, w.context_lens, mq.query_start, w.scale,
+                              kv_dtype=kvd, k_scale=ks, v_scale=vs)
+    d = DeviceWorkload(w, kc, vc)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    qs = torch.from_numpy(mq.query_start).cuda()
+    note(f"multi {name} kv={kv} partition={partition} qlens={qlens}")
+    out = pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, qs, w.scale,
+                             int(max(qlens)), k_scale=ks, v_scale=vs, partition_tokens=partition)
+    torch.cuda.synchronize()
+    return host_bits(out), ref
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("partition", [0, -1, 512])
+def test_multi_matches_oracle(lib, name, partition):
+    got, ref = _run(name, partition)
+    compare(got, ref, *BF16_TOL)
+
+
+@pytest.mark.parametrize("name", ["spec_verify_mixed", "long_bs128"])
+def test_multi_fp8_matches_oracle(lib, name):
+    got, ref = _run(name, 0, "fp8")
+    compare(got, ref, *FP8_TOL)
+
+
+def test_multi_small_partitions_and_ragged_tiles(lib):
+    """Partitions of one tile: every query row merges many partials, rows
+    whose position ends inside a tile mask the rest of it."""
+    got, ref = _run("tiny_mixed_lengths", 16)
+    compare(got, ref, *BF16_TOL)
+    got, ref = _run("chunk_prefill", 48)
+    compare(got, ref, *BF16_TOL)
+
+
+def test_multi_one_token_equals_decode_oracle(lib):
+    """With one query token per sequence the operation is decode."""
+    w = W.make_workload("mixed_batch", num_seqs=5, context=("list", [1, 16, 17, 700, 2049]))
+    mq = W.make_multi_query(w, [1] * 5)
+    d = DeviceWorkload(w)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    note("multi n=1")
+    out = pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                             torch.from_numpy(mq.query_start).cuda(), w.scale, 1)
+    ref = oracle.decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale)
+    compare(host_bits(out), ref, *BF16_TOL)
+
+
+def test_multi_last_row_of_full_context_equals_decode_bits(lib):
+    """Query r = n - 1 sees the whole context; r = 0 with n = L sees one
+    token, so its output is that token's V row exactly."""
+    w = W.make_workload("tiny")
+    L = w.context_lens.astype(int)
+    mq = W.make_multi_query(w, L.tolist())  # every cached token is a query
+    d = DeviceWorkload(w)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    note("multi n=L")
+    got = host_bits(pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                                       torch.from_numpy(mq.query_start).cuda(), w.scale, int(L.max())))
+    torch.cuda.synchronize()
+    g = w.spec.group
+    for i in range(w.spec.num_seqs):
+        row0 = int(mq.query_start[i])
+        b = w.block_tables[i, 0]
+        for h in range(w.spec.num_q_heads):
+            assert np.array_equal(got[row0, h], w.v_cache[b, 0, h // g])
+    ref = oracle.multi_decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq.query_start, w.scale)
+    compare(got, ref, *BF16_TOL)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 1, 128), (64, 1, 64), (64, 2, 128), (48, 2, 128)])
+@pytest.mark.parametrize("partition", [0, -1, 256])
+def test_decode_mqa_wide_groups(lib, Hq, Hkv, D, partition):
+    """pa_decode with g > 16 (MQA): routed to the multi-row kernel."""
+    w = W.make_workload("mixed_batch", num_seqs=5, context=("list", [1, 16, 300, 1000, 2100]),
+                        num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D)
+    ref = oracle.decode_workload(w)
+    d = DeviceWorkload(w)
+    note(f"mqa Hq={Hq} Hkv={Hkv} D={D} partition={partition}")
+    plan = pa.pa_decode_get_plan(w.spec.num_seqs, Hq, Hkv, D, 16, w.max_blocks_per_seq, partition_tokens=partition)
+    assert plan["variant"] == "mfma"
+    got = host_bits(d.decode(partition_tokens=partition))
+    torch.cuda.synchronize()
+    compare(got, ref, *BF16_TOL)

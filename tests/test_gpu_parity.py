@@ -296,3 +296,71 @@ def test_many_short_items_per_workgroup(lib, variant):
         b = host_bits(d.decode(variant=variant, partition_tokens=part, schedule=-1))
         compare(a, ref, *BF16_TOL)
         assert np.array_equal(a, b)
+
+
+def _copy_case(rng, N, n, extra_bad=True):
+    """n (src, dst) pairs: distinct destinations, no block both a source and a
+    destination; plus padding and out-of-pool pairs that must be skipped."""
+    ids = rng.permutation(N)
+    pairs = [[int(ids[i]), int(ids[n + i])] for i in range(n)]
+    if extra_bad:
+        pairs += [[-1, int(ids[2 * n])], [int(ids[2 * n + 1]), -5], [N + 3, int(ids[2 * n + 2])],
+                  [int(ids[2 * n + 3]), N]]
+    return np.array(pairs, np.int64)
+
+
+@pytest.mark.parametrize("name,kv", [("tiny", "bf16"), ("mixed_batch", "bf16"), ("mixed_batch", "fp8"),
+                                     ("long_splitk", "bf16")])
+def test_copy_blocks_bit_exact(lib, name, kv):
+    """Every byte of both caches equals the oracle's copy (skipped pairs and
+    untouched blocks included)."""
+    rng = np.random.default_rng(21)
+    w = W.make_workload(name, **REDUCED[name])
+    kc, vc = w.k_cache, w.v_cache
+    if kv == "fp8":
+        kc = oracle.quantize_pool(kc, 0.05)
+        vc = oracle.quantize_pool(vc, 0.07)
+    N = w.num_blocks
+    n = min(40, (N - 4) // 2)
+    pairs = _copy_case(rng, N, n)
+    ek, ev = kc.copy(), vc.copy()
+    oracle.copy_blocks(ek, ev, pairs[(pairs >= 0).all(1) & (pairs < N).all(1)])
+    d = DeviceWorkload(w, kc, vc)
+    note(f"copy_blocks {name} {kv} pairs={len(pairs)}")
+    pa.pa_copy_blocks(d.k_cache, d.v_cache, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    gk = d.k_cache.cpu().numpy() if d.fp8 else host_bits(d.k_cache)
+    gv = d.v_cache.cpu().numpy() if d.fp8 else host_bits(d.v_cache)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+
+
+def test_copy_blocks_then_decode_through_copies(lib):
+    """Copy-on-write round trip on the device: copy every block the batch
+    uses to free blocks, repoint the tables, decode: the output bits equal
+    the decode through the originals."""
+    w = W.make_workload("mixed_batch", **REDUCED["mixed_batch"])
+    d = DeviceWorkload(w)
+    note("copy_blocks then decode")
+    before = host_bits(d.decode())
+    tb = w.block_tables.copy()
+    nblk = [(int(c) + 15) // 16 for c in w.context_lens]
+    every = {int(tb[i, j]) for i in range(len(nblk)) for j in range(nblk[i])}
+    taken = every | {int(w.poison_block)} | set((w.slot_mapping // w.spec.block_size).tolist())
+    free = [b for b in range(w.num_blocks) if b not in taken]
+    # the sequences whose blocks fit in the free ones
+    chosen, used = [], []
+    for i in range(len(nblk)):
+        new = [int(b) for b in dict.fromkeys(tb[i, :nblk[i]].tolist()) if int(b) not in used]
+        if len(used) + len(new) <= len(free):
+            chosen.append(i)
+            used += new
+    assert len(chosen) >= 3, chosen
+    remap = dict(zip(used, free))
+    pa.pa_copy_blocks(d.k_cache, d.v_cache, torch.tensor([[u, remap[u]] for u in used], dtype=torch.int64).cuda())
+    for i in chosen:
+        for j in range(nblk[i]):
+            tb[i, j] = remap[int(tb[i, j])]
+    d.block_tables = torch.from_numpy(tb).cuda()
+    after = host_bits(d.decode())
+    torch.cuda.synchronize()
+    assert np.array_equal(before, after)

@@ -1,0 +1,113 @@
+"""GPU tests of the opt-in precondition checks (pa_check_cache_write_inputs,
+pa_check_decode_inputs, and the PA_DEBUG_VALIDATE switch of the hot-path
+calls). The inputs that break a precondition are index arrays only; nothing
+here launches a kernel on them: a check that fails returns before launching.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_mapping_amd as pa
+from paged_kv_decode_mapping_amd import workloads as W
+
+from _gpu_util import DeviceWorkload, host_bits, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib(gpu):
+    return pa.load_library()
+
+
+@pytest.fixture
+def debug_validate():
+    old = os.environ.get("PA_DEBUG_VALIDATE")
+    os.environ["PA_DEBUG_VALIDATE"] = "1"
+    yield
+    if old is None:
+        del os.environ["PA_DEBUG_VALIDATE"]
+    else:
+        os.environ["PA_DEBUG_VALIDATE"] = old
+
+
+SMALL = {
+    "tiny": dict(),
+    "mixed_batch": dict(num_seqs=10, context=("list", [16, 100, 511, 512, 513, 900, 3000, 40, 8192, 77])),
+    "long_splitk": dict(num_seqs=2, context=("list", [5000, 2049])),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_generated_workloads_pass(lib, name):
+    w = W.make_workload(name, **SMALL[name])
+    d = DeviceWorkload(w)
+    note(f"checks accept {name}")
+    bs = w.spec.block_size
+    assert pa.pa_check_cache_write_inputs(d.slot_mapping, w.num_blocks, bs) == pa.PA_OK
+    assert pa.pa_check_decode_inputs(d.block_tables, d.context_lens, w.num_blocks, bs) == pa.PA_OK
+
+
+def test_bad_slots_are_reported(lib):
+    N, bs = 32, 16
+    cases = {
+        "duplicate": [3, 17, 3, -1],
+        "past the pool": [0, 1, N * bs, 5],
+    }
+    for what, slots in cases.items():
+        note(f"slot check: {what}")
+        t = torch.tensor(slots, dtype=torch.int64, device="cuda")
+        assert pa.pa_check_cache_write_inputs(t, N, bs) == pa.PA_ERR_PRECONDITION, what
+    ok = torch.tensor([-1, -7, 0, N * bs - 1, 200], dtype=torch.int64, device="cuda")
+    assert pa.pa_check_cache_write_inputs(ok, N, bs) == pa.PA_OK
+
+
+def test_bad_tables_and_lengths_are_reported(lib):
+    N, bs = 32, 16
+    good = np.array([[0, 1, 2, 3], [4, 5, -1, 99], [6, 7, 8, 9]], dtype=np.int32)
+    ctx = np.array([64, 32, 1], dtype=np.int32)  # row 1 never reads its bad tail entries
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    note("decode check: valid tables")
+    assert pa.pa_check_decode_inputs(t(good), t(ctx), N, bs) == pa.PA_OK
+    bad_tables = good.copy()
+    bad_tables[1, 1] = N  # covers tokens 16..31 of a 32-token context
+    neg_tables = good.copy()
+    neg_tables[0, 3] = -2
+    for what, tab, c in [("entry past the pool", bad_tables, ctx), ("negative entry", neg_tables, ctx),
+                         ("context past the row", good, np.array([65, 32, 1], np.int32)),
+                         ("negative context", good, np.array([64, -1, 1], np.int32))]:
+        note(f"decode check: {what}")
+        assert pa.pa_check_decode_inputs(t(tab), t(c), N, bs) == pa.PA_ERR_PRECONDITION, what
+
+
+def test_debug_switch_stops_hot_path_calls(lib, debug_validate):
+    w = W.make_workload("tiny")
+    d = DeviceWorkload(w)
+    note("PA_DEBUG_VALIDATE: valid inputs still run")
+    out = d.decode()
+    torch.cuda.synchronize()
+    ref_bits = host_bits(out)
+    # a table entry outside the pool: the call must refuse before launching
+    bad = w.block_tables.copy()
+    bad[0, 0] = w.num_blocks + 5
+    d.block_tables = torch.from_numpy(bad).cuda()
+    sentinel = torch.full_like(out, 7.0)
+    note("PA_DEBUG_VALIDATE: bad table refused")
+    with pytest.raises(pa.PAError) as e:
+        d.decode(out=sentinel)
+    assert e.value.status == pa.PA_ERR_PRECONDITION
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)  # nothing was launched
+    # a duplicated slot in the cache write
+    slots = w.slot_mapping.copy()
+    slots[1] = slots[0]
+    kc = d.k_cache.clone()
+    note("PA_DEBUG_VALIDATE: duplicate slot refused")
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_cache_write(d.new_k, d.new_v, torch.from_numpy(slots).cuda(), d.k_cache, d.v_cache)
+    assert e.value.status == pa.PA_ERR_PRECONDITION
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(torch.int16), d.k_cache.view(torch.int16))
+    assert ref_bits.shape == (w.spec.num_seqs, w.spec.num_q_heads, w.spec.head_dim)

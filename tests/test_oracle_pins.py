@@ -277,6 +277,129 @@ def test_cache_write_rejects_out_of_pool_slot():
         oracle.cache_write(w.new_k, w.new_v, slots, w.k_cache.copy(), w.v_cache.copy())
 
 
+# ---------------------------------------------------------------- multi-token
+
+MULTI_CASES = [  # (Hq, Hkv, D, bs, ctx, q_lens)
+    (8, 2, 64, 16, [1, 17, 64, 100], [1, 5, 16, 4]),
+    (4, 4, 32, 4, [3, 8, 9, 30], [3, 2, 0, 7]),
+    (8, 1, 16, 8, [5, 16, 33], [5, 1, 33]),
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs,ctx,qlens", MULTI_CASES)
+def test_multi_matches_torch_sdpa_with_bottom_right_causal_mask(Hq, Hkv, D, bs, ctx, qlens):
+    """Pin: torch scaled_dot_product_attention in float64 on the dense K/V of
+    each sequence, with an explicit boolean mask that lets query r (position
+    L - n + r) see positions 0..L - n + r."""
+    rng = np.random.default_rng(41)
+    _, kc, vc, tables, ctx_a, dense = _identity_paged(ctx, Hq, Hkv, D, bs, rng)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = _bits(rng.standard_normal((int(qs[-1]), Hq, D)))
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.multi_decode(q, kc, vc, tables, ctx_a, qs, scale)
+    g = Hq // Hkv
+    for i, (k, v) in enumerate(dense):
+        n, L = qlens[i], ctx[i]
+        if n == 0:
+            continue
+        qt = torch.from_numpy(bf16_f32(q[qs[i]:qs[i + 1]]).astype(np.float64)).permute(1, 0, 2)  # [Hq, n, D]
+        kt = torch.from_numpy(bf16_f32(k).astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, 0)
+        vt = torch.from_numpy(bf16_f32(v).astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, 0)
+        mask = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(got[qs[i]:qs[i + 1]], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_multi_row_equals_decode_of_the_truncated_context():
+    """Pin (invariant, against the decode oracle): query r of a sequence gives
+    exactly the single-token decode of that query over the first L - n + r + 1
+    tokens; with one query token per sequence the whole result is the decode."""
+    w = W.make_workload("tiny", poison=True)
+    qlens = [1, 9, 30, 17]
+    mq = W.make_multi_query(w, qlens)
+    got = oracle.multi_decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq.query_start, w.scale)
+    for i, n in enumerate(qlens):
+        L = int(w.context_lens[i])
+        for r in range(n):
+            row = int(mq.query_start[i]) + r
+            one_q = np.repeat(mq.q[row][None], w.spec.num_seqs, axis=0)
+            trunc = w.context_lens.copy()
+            trunc[:] = 0
+            trunc[i] = L - n + r + 1
+            ref = oracle.decode(one_q, w.k_cache, w.v_cache, w.block_tables, trunc, w.scale)
+            assert np.array_equal(got[row], ref[i])
+    mq1 = W.make_multi_query(w, [1] * w.spec.num_seqs)
+    got1 = oracle.multi_decode(mq1.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq1.query_start,
+                               w.scale)
+    ref1 = oracle.decode(mq1.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale)
+    assert np.array_equal(got1, ref1)
+
+
+def test_multi_rejects_more_queries_than_context():
+    w = W.make_workload("tiny")
+    qs = np.array([0, 2, 2, 2, 2], np.int32)  # sequence 0 has one cached token
+    q = np.zeros((2, 8, 64), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.multi_decode(q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, qs, w.scale)
+
+
+# ---------------------------------------------------------------- block copy
+
+def _copy_pairs(rng, N, n):
+    ids = rng.permutation(N)
+    pairs = np.stack([ids[:n], ids[n:2 * n]], axis=1).astype(np.int64)
+    return pairs
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint8])
+def test_copy_blocks_matches_numpy_block_assignment(dtype):
+    """Pin: numpy's block-level fancy-index assignment cache[dst] = cache[src]
+    (the right side is gathered before the store, so it reads the pre-call
+    state), including a chain where a destination is also a source and
+    padding pairs; every other block is untouched."""
+    rng = np.random.default_rng(11)
+    N, bs, Hkv, D = 40, 16, 2, 64
+    hi = 65535 if dtype == np.uint16 else 255
+    kc = rng.integers(0, hi, (N, bs, Hkv, D), dtype=dtype)
+    vc = rng.integers(0, hi, (N, bs, Hkv, D), dtype=dtype)
+    pairs = np.concatenate([_copy_pairs(rng, N, 9), [[-1, 3], [4, -1], [7, 30], [30, 31]]]).astype(np.int64)
+    pairs = pairs[np.unique(pairs[:, 1], return_index=True)[1]]  # distinct destinations
+    ek, ev = kc.copy(), vc.copy()
+    keep = (pairs >= 0).all(axis=1)
+    ek[pairs[keep, 1]] = kc[pairs[keep, 0]]
+    ev[pairs[keep, 1]] = vc[pairs[keep, 0]]
+    n = oracle.copy_blocks(kc, vc, pairs)
+    assert n == int(keep.sum())
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
+
+
+def test_copy_blocks_then_repointed_table_decodes_the_same():
+    """Pin (invariant): after copying every block a sequence uses to fresh
+    blocks and repointing its table there, the decode is bit-identical."""
+    w = W.make_workload("tiny", poison=False)
+    base = oracle.decode_workload(w)
+    kc, vc, tb = w.k_cache.copy(), w.v_cache.copy(), w.block_tables.copy()
+    used = sorted({int(tb[i, j]) for i, c in enumerate(w.context_lens) for j in range((c + 15) // 16)})
+    free = [b for b in range(w.num_blocks) if b not in used][:len(used)]
+    assert len(free) == len(used)
+    oracle.copy_blocks(kc, vc, np.array(list(zip(used, free)), np.int64))
+    remap = dict(zip(used, free))
+    for i, c in enumerate(w.context_lens):
+        for j in range((c + 15) // 16):
+            tb[i, j] = remap[int(tb[i, j])]
+    got = oracle.decode(w.q, kc, vc, tb, w.context_lens, w.scale)
+    assert np.array_equal(got, base)
+
+
+def test_copy_blocks_rejects_bad_pairs():
+    kc = np.zeros((4, 2, 1, 8), np.uint16)
+    vc = np.zeros_like(kc)
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(kc, vc, [[0, 4]])
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(kc, vc, [[0, 2], [1, 2]])
+
+
 # ---------------------------------------------------------------- fp8 codec
 
 def test_e4m3fn_decode_all_codes_match_torch():
