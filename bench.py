@@ -95,6 +95,62 @@ def cpu_baseline(w, kv: str, kq=None, vq=None, budget_s: float = 12.0) -> dict:
                       f"float64 gather + softmax(qK^T)V, same byte model"}
 
 
+def bench_graph(args, w, q, k_cache, v_cache, tables, ctx, new_k, new_v, slots, k_scale, v_scale, plan,
+                kv_b: int) -> int:
+    """Time the step (cache write + decode) captured once in a HIP graph and
+    replayed, next to the same step launched eagerly through the binding."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    s = w.spec
+    dev = q.device
+    ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        pa.pa_cache_write(new_k, new_v, slots, k_cache, v_cache, k_scale, v_scale)
+        pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
+                     workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
+                     prefetch=args.prefetch, schedule=args.schedule)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(args.warmup, 1)):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    eager = timed(step, args.steps)
+    replay = timed(graph.replay, args.steps)
+    dec_b = decode_bytes(w, kv_b)
+    wr_b = write_bytes(w, kv_b)
+    log(f"graph: eager step {eager * 1e6:.1f} us, replay {replay * 1e6:.1f} us")
+    res = {
+        "metric": "paged decode step (cache write + decode) from a HIP graph: achieved HBM GB/s",
+        "value": round((dec_b + wr_b) / replay / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(replay * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.kv, "data": "synthetic",
+        "config": {"workload": f"{s.name}: {s.description}", "num_seqs": s.num_seqs, "plan": plan},
+        "eager_us_per_step": round(eager * 1e6, 2), "graph_us_per_step": round(replay * 1e6, 2),
+        "decode_tokens_per_s": round(s.num_seqs / replay, 1),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b: int, k_scale: float, v_scale: float,
                 kq=None, vq=None) -> int:
     """Time pa_decode_multi: the last --qlen cached tokens of every sequence are
@@ -254,10 +310,11 @@ def main() -> int:
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
     ap.add_argument("--prefetch", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
-    ap.add_argument("--op", choices=["step", "copy_blocks", "multi"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "multi", "graph"], default="step",
                     help="step: cache write + decode (the default measurement); copy_blocks: time "
                          "pa_copy_blocks on the workload's pool; multi: time pa_decode_multi with "
-                         "--qlen query tokens per sequence")
+                         "--qlen query tokens per sequence; graph: the step captured in a HIP graph, "
+                         "replayed (eager step time reported beside it)")
     ap.add_argument("--qlen", type=int, default=4, help="query tokens per sequence for --op multi")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs per pa_copy_blocks call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -325,6 +382,10 @@ def main() -> int:
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+
+    if args.op == "graph":
+        return bench_graph(args, w, q, k_cache, v_cache, tables, ctx, new_k, new_v, slots, k_scale, v_scale,
+                           plan, kv_b)
 
     def step(ev=None):
         if ev is not None:

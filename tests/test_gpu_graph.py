@@ -1,0 +1,120 @@
+"""GPU tests: the write + decode step captured in a HIP graph (through
+torch.cuda.CUDAGraph) at a bucketed batch size, replayed with new inputs.
+
+The library calls allocate nothing and never synchronise, so a caller can
+capture them. Batches smaller than the bucket are padded: padding sequences
+have context length 0 (zero output) and slot -1 (nothing written). Every
+replay is checked against the same step run eagerly on a second copy of the
+caches (bit-identical outputs and caches), with eager work and
+synchronisations between the replays, and one replay against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_mapping_amd as pa
+from paged_kv_decode_mapping_amd import workloads as W
+
+from _gpu_util import compare, dev_bf16, host_bits, note
+
+pytestmark = pytest.mark.gpu
+
+BUCKET = 16
+
+
+@pytest.fixture(scope="module")
+def lib(gpu):
+    return pa.load_library()
+
+
+def _step_inputs(w, n_real, step):
+    """Padded inputs of one decode step for the first n_real sequences of w:
+    contexts shortened by a step-dependent amount, new tokens to fresh slots."""
+    s = w.spec
+    S = BUCKET
+    ctx = np.zeros(S, np.int32)
+    ctx[:n_real] = np.maximum(w.context_lens[:n_real] - step * 7, 0)
+    tables = np.full((S, w.max_blocks_per_seq), w.poison_block, np.int32)
+    tables[:n_real] = w.block_tables[:n_real]
+    q = np.zeros((S, s.num_q_heads, s.head_dim), np.uint16)
+    q[:n_real] = W.make_multi_query(w, [1] * s.num_seqs, seed=500 + step).q[:n_real]
+    slots = np.full(S, -1, np.int64)
+    slots[:n_real] = w.slot_mapping[:n_real] + step  # stays in the fresh blocks
+    nk = np.zeros((S, s.num_kv_heads, s.head_dim), np.uint16)
+    nv = np.zeros_like(nk)
+    nk[:n_real] = np.roll(w.new_k, step, axis=0)[:n_real]
+    nv[:n_real] = np.roll(w.new_v, -step, axis=0)[:n_real]
+    return ctx, tables, q, slots, nk, nv
+
+
+@pytest.mark.parametrize("partition", [-1, 64])
+def test_captured_step_replays_match_eager(lib, partition):
+    w = W.make_workload("mixed_batch", num_seqs=12,
+                        context=("list", [16, 100, 511, 512, 513, 900, 1000, 40, 2000, 77, 300, 1]))
+    s = w.spec
+    n_real = 10
+    dev = torch.device("cuda")
+    kc_g, vc_g = dev_bf16(w.k_cache), dev_bf16(w.v_cache)   # the graph's caches
+    kc_e, vc_e = kc_g.clone(), vc_g.clone()                 # the eager reference's caches
+    S, MB = BUCKET, w.max_blocks_per_seq
+    st_q = torch.zeros((S, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device=dev)
+    st_ctx = torch.zeros(S, dtype=torch.int32, device=dev)
+    st_tab = torch.zeros((S, MB), dtype=torch.int32, device=dev)
+    st_slots = torch.full((S,), -1, dtype=torch.int64, device=dev)
+    st_nk = torch.zeros((S, s.num_kv_heads, s.head_dim), dtype=torch.bfloat16, device=dev)
+    st_nv = torch.zeros_like(st_nk)
+    st_out = torch.zeros_like(st_q)
+    need = pa.pa_decode_workspace_size(S, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, MB,
+                                       partition_tokens=partition)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def load(step):
+        ctx, tables, q, slots, nk, nv = _step_inputs(w, n_real, step)
+        st_ctx.copy_(torch.from_numpy(ctx))
+        st_tab.copy_(torch.from_numpy(tables))
+        st_q.copy_(dev_bf16(q))
+        st_slots.copy_(torch.from_numpy(slots))
+        st_nk.copy_(dev_bf16(nk))
+        st_nv.copy_(dev_bf16(nv))
+        return ctx, tables, q, slots, nk, nv
+
+    def step_on(kc, vc, out):
+        pa.pa_cache_write(st_nk, st_nv, st_slots, kc, vc)
+        pa.pa_decode(st_q, kc, vc, st_tab, st_ctx, w.scale, out, workspace=ws, partition_tokens=partition)
+
+    # warm up on a side stream (as torch asks before capture), on scratch caches
+    load(0)
+    kc_w, vc_w = kc_g.clone(), vc_g.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_on(kc_w, vc_w, torch.empty_like(st_out))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del kc_w, vc_w
+
+    note(f"graph capture partition={partition}")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step_on(kc_g, vc_g, st_out)
+    torch.cuda.synchronize()
+
+    for step in range(4):
+        ctx, tables, q, slots, nk, nv = load(step)
+        note(f"graph replay {step} partition={partition}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host_bits(st_out)
+        # the same step eagerly, on the reference caches
+        out_e = torch.empty_like(st_out)
+        step_on(kc_e, vc_e, out_e)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, host_bits(out_e)), f"replay {step}"
+        assert torch.equal(kc_g.view(torch.int16), kc_e.view(torch.int16))
+        assert torch.equal(vc_g.view(torch.int16), vc_e.view(torch.int16))
+        assert np.all(got[n_real:] == 0)  # padding sequences
+        if step == 2:
+            kh, vh = host_bits(kc_g), host_bits(vc_g)
+            ref = oracle.decode(q, kh, vh, tables, ctx, w.scale)
+            compare(got, ref, 1e-2, 1e-3)
