@@ -95,6 +95,45 @@ def cpu_baseline(w, kv: str, kq=None, vq=None, budget_s: float = 12.0) -> dict:
                       f"float64 gather + softmax(qK^T)V, same byte model"}
 
 
+def bench_stream(args, dev) -> int:
+    """Streaming-read reference on the same GPU: the library's probe kernel
+    reads a 4 GiB buffer once with 16-byte loads, with the default cache
+    policy and with the non-temporal one the decode kernels use."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    nbytes = 4 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for nt in (False, True):
+        for _ in range(max(args.warmup, 1)):
+            pa.pa_probe_stream_read(x, sink, nt)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            pa.pa_probe_stream_read(x, sink, nt)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        rates["nontemporal" if nt else "default"] = nbytes / (ms.mean() * 1e-3) / 1e9
+        log(f"stream read ({'non-temporal' if nt else 'default'} loads): {nbytes} B, avg {ms.mean() * 1e3:.1f} us "
+            f"= {rates['nontemporal' if nt else 'default']:.0f} GB/s")
+    best = max(rates.values())
+    res = {"metric": "streaming read of 4 GiB by pa_probe_stream_read (the practical read ceiling)",
+           "value": round(best, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(nbytes / best / 1e6, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": "one read of a 4 GiB buffer, 16-byte loads"},
+           "rates_gbps": {k: round(v, 1) for k, v in rates.items()},
+           "roofline": {"bound": "hbm", "achieved": round(best, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(best / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_probe_read_kernel"},
+           "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_graph(args, w, q, k_cache, v_cache, tables, ctx, new_k, new_v, slots, k_scale, v_scale, plan,
                 kv_b: int) -> int:
     """Time the step (cache write + decode) captured once in a HIP graph and
@@ -310,11 +349,12 @@ def main() -> int:
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
     ap.add_argument("--prefetch", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
-    ap.add_argument("--op", choices=["step", "copy_blocks", "multi", "graph"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "multi", "graph", "stream"], default="step",
                     help="step: cache write + decode (the default measurement); copy_blocks: time "
                          "pa_copy_blocks on the workload's pool; multi: time pa_decode_multi with "
                          "--qlen query tokens per sequence; graph: the step captured in a HIP graph, "
-                         "replayed (eager step time reported beside it)")
+                         "replayed (eager step time reported beside it); stream: the streaming-read "
+                         "reference: the library's probe kernel reading 4 GiB once, the practical read ceiling")
     ap.add_argument("--qlen", type=int, default=4, help="query tokens per sequence for --op multi")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs per pa_copy_blocks call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -336,6 +376,8 @@ def main() -> int:
         return 1
     pa.load_library()
     dev = torch.device("cuda:0")
+    if args.op == "stream":
+        return bench_stream(args, dev)
     log(f"generating workload {args.workload} ({args.kv} KV)")
     t0 = time.time()
     w = W.make_workload(args.workload)

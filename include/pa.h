@@ -150,7 +150,7 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
  *                     negative or out-of-pool id is skipped
  * Preconditions (not checked): destinations distinct, and no block is both
  * a source and a destination in one call (pairs are copied concurrently).
- * num_pairs <= 65535; num_pairs == 0 returns PA_OK with no launch.
+ * num_pairs < 2^31; num_pairs == 0 returns PA_OK with no launch.
  */
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
@@ -276,6 +276,17 @@ int pa_check_cache_write_inputs(const int64_t* slot_mapping, int64_t num_tokens,
 int pa_check_decode_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                            void* stream);
+
+/*
+ * pa_probe_stream_read -- read `bytes` bytes of device memory once with
+ * 16-byte loads (default cache policy, or non-temporal like the decode
+ * kernels' KV loads when `nontemporal` is nonzero). A measurement aid: the
+ * read bandwidth a kernel of this library reaches on the current GPU, the
+ * practical ceiling next to the published HBM peak. `sink` (device, >= 256
+ * uint32) is written only in a case the data never produces in practice.
+ * bytes must be a multiple of 16; buf 16-byte aligned.
+ */
+int pa_probe_stream_read(const void* buf, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
 
 /* Host-side reference of the kernels' fp8 encoder (same source as the
  * device code): n float32 inputs, already divided by the scale, to e4m3fn

@@ -77,6 +77,8 @@ def load_library(path: Optional[str] = None):
     lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_decode_multi_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.pa_decode_multi_workspace_size.restype = sz
+    lib.pa_probe_stream_read.argtypes = [P, i64, i32, P, P]
+    lib.pa_probe_stream_read.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [P, P, P, i64, i32, i32, i32, i64, i32, P]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_check_cache_write_inputs.argtypes = [P, i64, i32, i64, P]
@@ -326,6 +328,20 @@ def pa_check_decode_inputs(block_tables, context_lens, num_blocks: int, block_si
     if st not in (PA_OK, PA_ERR_PRECONDITION):
         raise PAError(st, "pa_check_decode_inputs")
     return st
+
+
+def pa_probe_stream_read(buf, sink, nontemporal: bool = True, stream=None) -> None:
+    """Read every byte of the device tensor `buf` once (a streaming-read
+    reference kernel); `sink` is a device int32/uint32 tensor of >= 256 entries."""
+    lib = load_library()
+    _check(buf, "buf")
+    _check(sink, "sink")
+    if sink.numel() < 256 or sink.element_size() != 4:
+        raise ValueError("sink must hold at least 256 32-bit words")
+    st = lib.pa_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), 1 if nontemporal else 0,
+                                  sink.data_ptr(), _stream_ptr(stream))
+    if st != PA_OK:
+        raise PAError(st, "pa_probe_stream_read")
 
 
 def fp8_encode_host(x) -> "numpy.ndarray":

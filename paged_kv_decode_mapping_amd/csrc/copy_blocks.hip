@@ -9,10 +9,11 @@
 // duplication: for each (src, dst) pair, block dst of K and of V becomes a
 // byte-for-byte copy of block src (all rows, all KV heads).
 //
-// Workgroup (x, p) copies 16-byte chunks x*256 + t, x*256 + t + stride, ...
-// of pair p's block in both caches: plain coalesced streaming copies (the
-// data is read once and written once, so the loads and stores are marked
-// non-temporal). Pairs with a negative or out-of-pool id are skipped.
+// Workgroup p copies pair p's block in both caches: each thread moves
+// 16-byte chunks t, t + 256, ..., issuing kUnroll loads of K and of V before
+// their stores so that enough bytes are in flight. The data is read once and
+// written once, so loads and stores are marked non-temporal. Pairs with a
+// negative or out-of-pool id are skipped.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -20,9 +21,10 @@ namespace pa {
 namespace {
 
 constexpr int kCopyThreads = 256;
+constexpr int kUnroll = 8;
 
 __global__ __launch_bounds__(kCopyThreads) void pa_copy_blocks_kernel(CopyBlocksArgs a) {
-    const int64_t p = blockIdx.y;
+    const int64_t p = blockIdx.x;
     const int64_t src = a.pairs[2 * p];
     const int64_t dst = a.pairs[2 * p + 1];
     if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks) return;
@@ -31,24 +33,31 @@ __global__ __launch_bounds__(kCopyThreads) void pa_copy_blocks_kernel(CopyBlocks
     const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_cache + src * a.block_bytes);
     u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + dst * a.block_bytes);
     u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + dst * a.block_bytes);
-    const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < chunks; i += stride) {
-        const u32x4 k = __builtin_nontemporal_load(ks + i);
-        const u32x4 v = __builtin_nontemporal_load(vs + i);
-        __builtin_nontemporal_store(k, kd + i);
-        __builtin_nontemporal_store(v, vd + i);
+    for (int64_t base = threadIdx.x; base < chunks; base += (int64_t)kUnroll * kCopyThreads) {
+        u32x4 k[kUnroll], v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kCopyThreads;
+            if (i < chunks) {
+                k[u] = __builtin_nontemporal_load(ks + i);
+                v[u] = __builtin_nontemporal_load(vs + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kCopyThreads;
+            if (i < chunks) {
+                __builtin_nontemporal_store(k[u], kd + i);
+                __builtin_nontemporal_store(v[u], vd + i);
+            }
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
-    const int64_t chunks = a.block_bytes / 16;
-    // up to 8 workgroups per block pair, each thread moving >= 1 chunk of K and of V
-    int64_t gx = (chunks + kCopyThreads - 1) / kCopyThreads;
-    if (gx > 8) gx = 8;
-    const dim3 grid((unsigned)gx, (unsigned)a.num_pairs);
-    hipLaunchKernelGGL(pa_copy_blocks_kernel, grid, dim3(kCopyThreads), 0, s, a);
+    hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3((unsigned)a.num_pairs), dim3(kCopyThreads), 0, s, a);
     return hipGetLastError();
 }
 

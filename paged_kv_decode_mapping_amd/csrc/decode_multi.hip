@@ -18,8 +18,8 @@
 //
 // Rows. The (query token r, head hh) pairs of one (sequence, KV head) are
 // rows rho = r * g + hh; every wave of a workgroup owns one 16-row tile of
-// them (W waves: 16 W rows), so the online-softmax state of a row never
-// leaves its lanes and a workgroup needs no combine step. Rows are the
+// them (W = 1, 2, 4 or 8 waves: 16 W rows), so the online-softmax state of
+// a row never leaves its lanes and a workgroup needs no combine step. Rows are the
 // columns of the same MFMA tiles the decode kernel uses:
 //   S = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q^T rows
 //               of this wave from LDS;
@@ -41,6 +41,12 @@
 // Split-K. A workgroup covers one partition of at most P tokens; with more
 // than one partition it stores unnormalised partial states (m, l, o) per row
 // and pa_multi_merge_kernel combines them by log-sum-exp.
+//
+// Order. With a work list (the decode path's longest-first list of
+// (sequence, KV head, partition) items) workgroups take items in that order,
+// so the longest contexts start first; one cooperative tile stream per
+// workgroup makes a long item slow, and a long item started last would
+// stretch the whole launch.
 #include "pa_epilogue.h"
 
 namespace pa {
@@ -90,12 +96,23 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     // ---- the work item
     int bid = (int)blockIdx.x;
     MultiItem it;
-    it.part = bid % a.num_partitions;
-    bid /= a.num_partitions;
-    it.rb = bid % a.row_blocks;
-    bid /= a.row_blocks;
-    it.kvh = bid % a.num_kv_heads;
-    it.seq = bid / a.num_kv_heads;
+    if (a.items != nullptr) {
+        const int idx = bid / a.row_blocks;
+        it.rb = bid - idx * a.row_blocks;
+        const int count = *a.item_count;
+        const int4 rec = a.items[idx];  // in bounds: the list has room for the whole grid
+        if (idx >= count) return;
+        it.seq = rec.x;
+        it.kvh = rec.y & 0xffff;
+        it.part = rec.y >> 16;
+    } else {
+        it.part = bid % a.num_partitions;
+        bid /= a.num_partitions;
+        it.rb = bid % a.row_blocks;
+        bid /= a.row_blocks;
+        it.kvh = bid % a.num_kv_heads;
+        it.seq = bid / a.num_kv_heads;
+    }
     const int cap = a.max_blocks_per_seq << a.block_size_log2;
     int L = a.context_lens[it.seq];
     it.L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -378,7 +395,8 @@ template <int D, bool FP8>
 hipError_t launch_df(const MultiArgs& a, int waves, hipStream_t s) {
     if (waves <= 1) return launch_w<D, FP8, 1>(a, s);
     if (waves == 2) return launch_w<D, FP8, 2>(a, s);
-    return launch_w<D, FP8, 4>(a, s);
+    if (waves == 4) return launch_w<D, FP8, 4>(a, s);
+    return launch_w<D, FP8, 8>(a, s);
 }
 
 }  // namespace

@@ -105,7 +105,8 @@ int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int64
 
 // Plan of the multi-row kernel: Tq query rows in all, at most maxq per
 // sequence, g = Hq / Hkv heads per KV head, so at most maxq * g rows per
-// (sequence, KV head); one wave per 16 of them, up to 4 waves a workgroup.
+// (sequence, KV head); one wave per 16 of them, up to 8 waves a workgroup
+// (more rows take more workgroups, each reading the K/V again).
 int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
                     int32_t MB, int32_t partition_tokens, Plan* plan) {
     if (Tq < 0 || maxq < 0) return PA_ERR_SHAPE;
@@ -115,7 +116,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     p.scheduled = false;
     const int g = Hq / Hkv;
     const int64_t rows = (int64_t)(maxq > 0 ? maxq : 1) * g;
-    p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : (rows <= 64 ? 4 : 8));
     p.depth = p.waves == 1 ? 2 : 4;  // register ring of the cooperative tile loads
     const int64_t rb = (rows + 16 * p.waves - 1) / (16 * p.waves);
     if (rb >= (int64_t(1) << 20)) return PA_ERR_UNSUPPORTED;
@@ -129,11 +130,21 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     if (p.num_partitions < 1) p.num_partitions = 1;
     p.num_workgroups = (int64_t)S * Hkv * rb * p.num_partitions;
     if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    // Split contexts (long or ragged ones): take items longest first from the
+    // device work list. A workgroup here is one cooperative tile stream, so a
+    // long item started last would stretch the launch (measured: 8 queries
+    // per sequence on a ragged batch, 531 -> 384 us). Unsplit, the direct
+    // grid keeps the KV heads of a sequence adjacent, which measured faster.
+    p.scheduled = p.num_partitions > 1 && p.num_partitions < 32768 && Hkv < 65536;
     size_t off = 0;
+    if (p.scheduled) {
+        p.items_off = kHeaderBytes;
+        off = p.items_off + align_up((size_t)S * Hkv * p.num_partitions * 4 * sizeof(int32_t), 256);
+    }
     if (p.num_partitions > 1) {
         const size_t prow = (size_t)Tq * Hq * p.num_partitions;
-        p.ml_off = 0;
-        p.o_off = align_up(prow * 2 * sizeof(float), 256);
+        p.ml_off = off;
+        p.o_off = off + align_up(prow * 2 * sizeof(float), 256);
         off = p.o_off + prow * D * sizeof(float);
     }
     p.workspace = off;
@@ -258,7 +269,23 @@ int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_c
     a.block_bytes = (uint32_t)((int64_t)bs * Hkv * D * esz);
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
-    const hipError_t e = pa::launch_multi(a, D, fp8, p.waves, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.scheduled) {
+        char* ws = static_cast<char*>(workspace);
+        pa::ScheduleArgs sa{};
+        sa.context_lens = context_lens;
+        sa.items = reinterpret_cast<int4*>(ws + p.items_off);
+        sa.item_count = reinterpret_cast<int*>(ws);
+        sa.num_seqs = S;
+        sa.num_kv_heads = Hkv;
+        sa.partition_tokens = p.partition_tokens;
+        sa.num_partitions = p.num_partitions;
+        sa.max_context = MB * bs;
+        if (pa::launch_schedule(sa, s) != hipSuccess) return PA_ERR_LAUNCH;
+        a.items = sa.items;
+        a.item_count = sa.item_count;
+    }
+    const hipError_t e = pa::launch_multi(a, D, fp8, p.waves, s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -310,7 +337,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
     if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_UNSUPPORTED;
-    if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;
+    if (num_pairs >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
     if (num_pairs == 0) return PA_OK;
     if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
     if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
@@ -504,6 +531,17 @@ int pa_decode_multi(const void* q, const void* k_cache, const void* v_cache, con
     return run_multi(p, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out, num_seqs,
                      num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_blocks_per_seq, num_blocks, kv_dtype, k_scale, v_scale, workspace, stream);
+}
+
+int pa_probe_stream_read(const void* buf, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream) {
+    if (bytes < 0 || (bytes & 15) != 0) return PA_ERR_SHAPE;
+    if (bytes == 0) return PA_OK;
+    if (!buf || !sink) return PA_ERR_NULL;
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return PA_ERR_ALIGN;
+    const int cus = current_cu_count();
+    if (cus <= 0) return PA_ERR_DEVICE;
+    const hipError_t e = pa::launch_probe_read(buf, bytes, nontemporal != 0, sink, cus, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 void pa_fp8_e4m3fn_encode_host(const float* x, uint8_t* codes, int64_t n) {

@@ -85,6 +85,11 @@ struct MultiArgs {
     int32_t last_block;
     uint32_t block_bytes, slot_bytes, head_bytes;
     float qk_scale_log2, v_scale;
+    // Device work list (null = direct grid): the decode work list of
+    // (sequence, KV head, partition) items, longest first; workgroup b takes
+    // item b / row_blocks, row block b % row_blocks.
+    const int4* items;
+    const int* item_count;
 };
 
 struct CopyBlocksArgs {
@@ -109,6 +114,9 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+// streaming-read reference kernel (probe.hip)
+hipError_t launch_probe_read(const void* buf, int64_t bytes, bool nontemporal, uint32_t* sink, int cus,
+                             hipStream_t s);
 // the multi-row kernel, then (split) its merge
 hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, hipStream_t s);
 

@@ -193,7 +193,38 @@ def test_multi_nothing_to_do_is_a_no_op(lib):
 
 
 def test_multi_workspace_size(lib):
-    assert pa.pa_decode_multi_workspace_size(4, 10, 4, 8, 2, 64, 16, 7, partition_tokens=-1) == 0
-    n = pa.pa_decode_multi_workspace_size(4, 10, 4, 8, 2, 64, 16, 7, partition_tokens=32)
+    """Unsplit: nothing. Split: header (item count) + the work list of
+    (sequence, KV head, partition) items, then the split-K partials."""
+    S, Tq, Hq, Hkv, D = 4, 10, 8, 2, 64
+    assert pa.pa_decode_multi_workspace_size(S, Tq, 4, Hq, Hkv, D, 16, 7, partition_tokens=-1) == 0
+    n = pa.pa_decode_multi_workspace_size(S, Tq, 4, Hq, Hkv, D, 16, 7, partition_tokens=32)
     P = -(-7 * 16 // 32)
-    assert n == _align(10 * 8 * P * 2 * 4) + 10 * 8 * P * 64 * 4
+    assert n == 256 + _align(S * Hkv * P * 16) + _align(Tq * Hq * P * 2 * 4) + Tq * Hq * P * D * 4
+
+
+def _copy(lib, **kw):
+    args = dict(k=A, v=A, m=A, n=4, Hkv=2, D=64, bs=16, N=32, kvd=1)
+    args.update(kw)
+    return lib.pa_copy_blocks(args["k"], args["v"], args["m"], args["n"], args["Hkv"], args["D"], args["bs"],
+                              args["N"], args["kvd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(kvd=5), -5), (dict(D=32), -3),
+    (dict(bs=24), -3), (dict(k=None), -1), (dict(m=None), -1), (dict(v=A + 4), -4), (dict(m=A + 4), -4),
+    (dict(n=1 << 31), -3),
+])
+def test_copy_blocks_rejects_bad_arguments(lib, kw, code):
+    assert _copy(lib, **kw) == code
+
+
+def test_copy_blocks_zero_pairs_is_a_no_op(lib):
+    assert _copy(lib, n=0, k=None, v=None, m=None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A, 24, 1, A), -2), ((A, -16, 1, A), -2), ((None, 32, 1, A), -1), ((A, 32, 0, None), -1),
+    ((A + 8, 32, 1, A), -4), ((A, 32, 1, A + 2), -4), ((None, 0, 1, None), 0),
+])
+def test_probe_rejects_bad_arguments(lib, args, code):
+    assert lib.pa_probe_stream_read(*args, None) == code

@@ -111,3 +111,15 @@ def test_debug_switch_stops_hot_path_calls(lib, debug_validate):
     torch.cuda.synchronize()
     assert torch.equal(kc.view(torch.int16), d.k_cache.view(torch.int16))
     assert ref_bits.shape == (w.spec.num_seqs, w.spec.num_q_heads, w.spec.head_dim)
+
+
+def test_stream_probe_reads_without_writing(lib):
+    """The streaming-read reference kernel runs over a buffer with a ragged
+    tail and leaves its sink untouched (its data never matches the magic)."""
+    x = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    note("stream probe")
+    for nt in (False, True):
+        pa.pa_probe_stream_read(x, sink, nt)
+    torch.cuda.synchronize()
+    assert torch.all(sink == 0)
