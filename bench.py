@@ -52,9 +52,10 @@ def write_bytes(w, kv_bytes: int) -> int:
     return int(T * s.num_kv_heads * s.head_dim * (2 * 2 + 2 * kv_bytes) + 8 * T)
 
 
-def load_traffic(workload: str, kv: str):
+def load_traffic(workload: str, kv: str, plan: dict):
     """HBM traffic per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources."""
+    summary, if it was taken on the current kernel sources with the same
+    launch plan."""
     p = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}_{kv}.json")
     if not os.path.exists(p):
         return None
@@ -63,7 +64,7 @@ def load_traffic(workload: str, kv: str):
     except Exception:
         return None
     from paged_kv_decode_mapping_amd.profiling import kernel_source_hash
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash() or d.get("plan") != plan:
         return None
     return d.get("bytes_per_launch")
 
@@ -503,7 +504,7 @@ def main() -> int:
         base = cpu_baseline(w, args.kv, kq, vq)
         log(f"cpu baseline {base}")
 
-    traffic = load_traffic(args.workload, args.kv)
+    traffic = load_traffic(args.workload, args.kv, plan)
     tok_s = s.num_seqs / (ms_per_step * 1e-3)
     res = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + decode tokens/s",

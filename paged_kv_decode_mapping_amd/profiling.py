@@ -26,12 +26,18 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-# The sources that decide what pa_decode launches and what its kernels do:
-# the launch plan, the decode kernels, the work-list and merge kernels and
-# the headers they include. Other kernels (cache write, block copy, the
-# multi-token kernel) and the host-side checks do not change its traffic.
-DECODE_SOURCES = ("pa_api.hip", "decode_mfma.hip", "decode_valu.hip", "schedule.hip", "merge.hip",
-                  "pa_epilogue.h", "pa_device.h", "pa_internal.h")
+# What decides the decode kernels' traffic: their sources, the headers they
+# include, and the argument blocks they receive. The launch plan (waves,
+# tiles in flight, partitions) is stored next to the figure and compared
+# separately, so host-side changes elsewhere do not invalidate it.
+DECODE_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "schedule.hip", "merge.hip", "pa_epilogue.h",
+                  "pa_device.h")
+DECODE_STRUCTS = ("DecodeArgs", "ScheduleArgs", "MergeArgs", "LaunchShape")
+
+
+def _struct_text(src: str, name: str) -> str:
+    i = src.index("struct " + name + " {")
+    return src[i:src.index("};", i) + 2]
 
 
 def kernel_source_hash() -> str:
@@ -40,7 +46,30 @@ def kernel_source_hash() -> str:
     for f in DECODE_SOURCES:
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
+    internal = open(os.path.join(csrc, "pa_internal.h")).read()
+    for name in DECODE_STRUCTS:
+        h.update(_struct_text(internal, name).encode())
     return h.hexdigest()[:16]
+
+
+def decode_plan(workload: str, kv: str) -> dict:
+    """The launch plan pa_decode uses for a named workload on this GPU."""
+    import paged_kv_decode_mapping_amd as pa
+    from paged_kv_decode_mapping_amd import workloads as W
+    s = W.SPECS[workload]
+    ctx = s.context
+    cap = {"const": lambda: ctx[1], "uniform": lambda: ctx[2], "lognormal": lambda: ctx[4],
+           "list": lambda: max(ctx[1])}[ctx[0]]()
+    mb = -(-int(cap) // s.block_size)
+    return pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, mb,
+                                 pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN)
+
+
+def _plan_or_none(workload: str, kv: str):
+    try:
+        return decode_plan(workload, kv)
+    except Exception:  # unknown workload, or no GPU to plan for: the figure is then never reported
+        return None
 
 
 def _find(d: str, suffix: str) -> str:
@@ -114,7 +143,8 @@ def cmd_traffic(a) -> None:
            "copy_kernel": _short(copy_name), "copy_bytes": a.copy_bytes,
            "fetch_counter_per_copy_byte": cf / a.copy_bytes, "write_counter_per_copy_byte": cw / a.copy_bytes,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
-           "dispatches": len(dfetch), "kernel_source_hash": kernel_source_hash(), "command": a.cmd}
+           "dispatches": len(dfetch), "kernel_source_hash": kernel_source_hash(),
+           "plan": _plan_or_none(a.workload, a.kv), "command": a.cmd}
     json.dump(res, open(a.out, "w"), indent=1)
     print(json.dumps(res, indent=1))
 

@@ -48,3 +48,4 @@ def test_traffic_scaling(tmp_path):
     assert r["fetch_bytes_per_launch"] == 2100.0 * 1024
     assert r["write_bytes_per_launch"] == 12.0 * 1024
     assert r["kernel_source_hash"] == profiling.kernel_source_hash()
+    assert r["plan"] is None  # unknown workload: no plan, so bench.py never reports this figure
