@@ -255,6 +255,29 @@ def test_decode_fp8_matches_oracle(lib, name, variant):
     compare(host_bits(out), ref, *BF16_TOL)
 
 
+@pytest.mark.parametrize("prefetch", [1, 2])
+def test_fp8_decode_edge_contexts_and_pairs(lib, prefetch):
+    """The fp8 MFMA kernel consumes a wave's tiles in pairs: contexts that
+    leave a wave an odd number of tiles (the pair's second tile empty),
+    partial tiles, one-tile partitions and empty contexts."""
+    ctx = [0, 1, 15, 16, 17, 32, 48, 63, 64, 65, 200, 257]
+    w = W.make_workload("tiny", num_seqs=len(ctx), context=("list", ctx))
+    ks, vs = 0.02, 0.03
+    kq = oracle.quantize_pool(w.k_cache, ks)
+    vq = oracle.quantize_pool(w.v_cache, vs)
+    ref = _oracle(w, kv_dtype=oracle.KV_FP8_E4M3FN, k_cache=kq, v_cache=vq, k_scale=ks, v_scale=vs)
+    d = DeviceWorkload(w, kq, vq)
+    for part in (-1, 16, 48):
+        for waves in (1, 4):
+            note(f"fp8 edges prefetch={prefetch} partition={part} waves={waves}")
+            got = host_bits(d.decode(k_scale=ks, v_scale=vs, variant="mfma", prefetch=prefetch,
+                                     partition_tokens=part, waves=waves))
+            torch.cuda.synchronize()
+            compare(got, ref, *FP8_TOL)
+            compare(got, ref, *BF16_TOL)
+            assert np.all(got[0] == 0)
+
+
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_fp8_decode_reads_every_code_exactly(lib, variant):
     """ctx = 1 with V rows holding all 256 codes: out = code * v_scale exactly
