@@ -92,6 +92,11 @@ typedef struct pa_decode_opts {
                                  partition) in index order, empty ones
                                  included; 0 = the work list when the plan
                                  splits contexts, else -1 */
+    int32_t heads_per_tile;   /* MFMA kernel: 0 = chosen (2 for bf16 caches
+                                 when g is 5..8 and num_kv_heads is even,
+                                 else 1); else 1, 2 or 4 adjacent KV heads
+                                 sharing one 16-row matrix tile
+                                 (g * heads_per_tile <= 16) */
     int32_t reserved;         /* must be 0 */
 } pa_decode_opts;
 
@@ -107,6 +112,7 @@ typedef struct pa_decode_plan {
     int64_t num_workgroups;   /* decode kernel grid size (with a work list, the
                                  ones past its end exit at once) */
     size_t workspace_bytes;   /* bytes of workspace pa_decode needs */
+    int32_t heads_per_tile;   /* KV heads per matrix tile (1 for the VALU kernel) */
 } pa_decode_plan;
 
 /*

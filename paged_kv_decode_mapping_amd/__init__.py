@@ -39,14 +39,16 @@ class PAError(RuntimeError):
 class pa_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("waves_per_group", ctypes.c_int32), ("prefetch_tiles", ctypes.c_int32),
-                ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class pa_decode_plan(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
                 ("partition_tokens", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("prefetch_tiles", ctypes.c_int32), ("scheduled", ctypes.c_int32),
-                ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+                ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("heads_per_tile", ctypes.c_int32)]
 
 
 def load_library(path: Optional[str] = None):
@@ -98,9 +100,9 @@ def strerror(status: int) -> str:
 
 
 def _opts(partition_tokens: int = 0, variant="auto", waves: int = 0, prefetch: int = 0,
-          schedule: int = 0) -> pa_decode_opts:
+          schedule: int = 0, heads_per_tile: int = 0) -> pa_decode_opts:
     v = _VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    return pa_decode_opts(int(partition_tokens), v, int(waves), int(prefetch), int(schedule), 0)
+    return pa_decode_opts(int(partition_tokens), v, int(waves), int(prefetch), int(schedule), int(heads_per_tile), 0)
 
 
 def _kv_dtype(t) -> int:
@@ -230,9 +232,9 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
 
 def pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                        kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0,
-                       schedule=0) -> dict:
+                       schedule=0, heads_per_tile=0) -> dict:
     lib = load_library()
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
     p = pa_decode_plan()
     st = lib.pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, kv_dtype, ctypes.byref(o), ctypes.byref(p))
@@ -242,12 +244,13 @@ def pa_decode_get_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size
             "partition_tokens": p.partition_tokens, "num_partitions": p.num_partitions,
             "prefetch_tiles": p.prefetch_tiles, "scheduled": bool(p.scheduled),
             "num_workgroups": p.num_workgroups,
-            "workspace_bytes": p.workspace_bytes}
+            "workspace_bytes": p.workspace_bytes, "heads_per_tile": p.heads_per_tile}
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
               k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, partition_tokens: int = 0,
-              variant="auto", waves: int = 0, prefetch: int = 0, schedule: int = 0, stream=None):
+              variant="auto", waves: int = 0, prefetch: int = 0, schedule: int = 0, heads_per_tile: int = 0,
+              stream=None):
     """Decode step: q [S, Hq, D] bf16 attends through block_tables [S, MB] int32 and
     context_lens [S] int32 over the paged caches [N, bs, Hkv, D]. Returns out [S, Hq, D] bf16.
 
@@ -274,7 +277,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
         _check(out, "out", torch.bfloat16, 3)
         if out.shape != q.shape:
             raise ValueError("out shape")
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
     need = lib.pa_decode_workspace_size(S, Hq, Hkv, D, bs, MB, kvd, ctypes.byref(o))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -291,8 +294,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                              kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0,
-                             schedule=0) -> int:
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule)
+                             schedule=0, heads_per_tile=0) -> int:
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
     return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                        block_size, max_blocks_per_seq, kv_dtype,
                                                        ctypes.byref(o)))

@@ -63,22 +63,32 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4&
 }
 
 // Occupancy the register allocator is asked to keep: 4 waves per SIMD (<= 128
-// VGPRs) for the ring of 2 tiles, 3 (<= 168) for 3 tiles, 2 for 4 tiles.
-template <int NB>
-constexpr int mfma_waves_per_eu() { return NB <= 2 ? 4 : (NB == 3 ? 3 : 2); }
+// VGPRs) for the ring of 2 tiles, 3 (<= 168) for 3 tiles, 2 for 4 tiles; the
+// bf16 kernel with packed heads keeps a per-head P.V path for non-finite V
+// (about 35 more registers) and gets one wave per SIMD less.
+template <int NB, int HP, bool FP8>
+constexpr int mfma_waves_per_eu() {
+    const int base = NB <= 2 ? 4 : (NB == 3 ? 3 : 2);
+    return (HP > 1 && !FP8 && base > 2) ? base - 1 : base;
+}
 
-template <int D, bool FP8, int NB>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<NB>())))
+template <int D, bool FP8, int NB, int HP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<NB, HP, FP8>())))
 void pa_decode_mfma_kernel(DecodeArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int NQK = D / 32;         // q.K^T MFMAs per tile
     constexpr int NPV = D / 16;         // P.V MFMAs per tile
     constexpr int EPL = 16 / ESZ;       // elements per 16-byte lane load
-    constexpr int LPR = D / EPL;        // lanes per row
-    constexpr int RPI = 64 / LPR;       // rows per load instruction
-    constexpr int NI = kTile / RPI;     // loads per lane per tile, for each of K and V
+    constexpr int LPR = D / EPL;        // lanes per KV head row
+    // A tile is 16 MFMA rows: TPH tokens of each of HP adjacent KV heads
+    // (row = head * TPH + token); their rows are HP * D contiguous elements
+    // in the cache, so each token contributes one contiguous chunk.
+    constexpr int TPH = kTile / HP;     // tokens per tile
+    constexpr int LPC = HP * LPR;       // lanes per token chunk (HP heads)
+    constexpr int RPI = 64 / LPC;       // tokens per load instruction
+    constexpr int NI = TPH / RPI;       // loads per lane per tile, for each of K and V
     constexpr int RS = D + 8;           // LDS row stride (bf16 elements): +16 bytes per row
-    static_assert(NI >= 1 && kTile % RPI == 0, "tile shape");
+    static_assert(LPC <= 64 && NI >= 1 && TPH % RPI == 0, "tile shape");
 
     extern __shared__ float smem[];
     for_each_item(a, [&](const WorkItem& wi) {
@@ -88,22 +98,26 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         const int c = lane & 15;
         const int gq = lane >> 4;
         const int g = a.group;
+        const int kvh0 = wi.kvh * HP;  // first KV head of this unit
         uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * 2 * kTile * RS;  // V tile
         uint16_t* ks = vs + kTile * RS;                                               // K tile
         const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RS + 4 * (lane & 3);
 
-        // Q^T operands: MFMA j takes d = 32 j + 8 gq + 0..7 of head c, the d
-        // range of the lane's K operand of MFMA j. The group's q rows (zero
-        // rows past g) sit in LDS after the staging tiles and are read per
-        // tile, which keeps 16 registers per lane free for the load ring.
+        // Q^T operands: MFMA j takes d = 32 j + 8 gq + 0..7 of column c, the
+        // d range of the lane's K operand of MFMA j. Column c is query head
+        // c % TPH of KV head kvh0 + c / TPH (zero when c % TPH >= g). The q
+        // rows sit in LDS after the staging tiles and are read per tile,
+        // which keeps 16 registers per lane free for the load ring.
         uint16_t* qs = reinterpret_cast<uint16_t*>(smem) + W * 2 * kTile * RS;
         for (int i = (int)threadIdx.x; i < kTile * (D / 8); i += (int)blockDim.x) {
-            const int h = i / (D / 8);
-            const int d8 = i - h * (D / 8);
+            const int col = i / (D / 8);
+            const int d8 = i - col * (D / 8);
+            const int qi = col % TPH;
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (h < g)
-                w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + h) * D + 8 * d8);
-            *reinterpret_cast<u32x4*>(qs + h * RS + 8 * d8) = w;
+            if (qi < g)
+                w = *reinterpret_cast<const u32x4*>(
+                    a.q + ((int64_t)wi.seq * a.num_q_heads + (kvh0 + col / TPH) * g + qi) * D + 8 * d8);
+            *reinterpret_cast<u32x4*>(qs + col * RS + 8 * d8) = w;
         }
         __syncthreads();
         const uint16_t* q_row = qs + c * RS + 8 * gq;
@@ -115,12 +129,13 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         const int span = wi.t_end - wi.t_begin;
-        const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
-        const uint32_t head_off = (uint32_t)wi.kvh * a.head_bytes;
+        const int ntiles = span > 0 ? (span + TPH - 1) / TPH : 0;
+        const uint32_t head_off = (uint32_t)kvh0 * a.head_bytes;
         // per-lane byte offset inside a tile (the same for K and V), fixed for
-        // the whole item: load i of lane l covers row i * RPI + l / LPR; the
-        // i * RPI rows go into the wave-uniform offset
-        const uint32_t roff = (uint32_t)(lane / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPR);
+        // the whole item: load i of lane l covers token i * RPI + l / LPC,
+        // bytes 16 (l % LPC) of its HP-head chunk; the i * RPI tokens go into
+        // the wave-uniform offset
+        const uint32_t roff = (uint32_t)(lane / LPC) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPC);
         const uint32_t rstep = (uint32_t)RPI * a.slot_bytes;
         const int bs_mask = (1 << a.block_size_log2) - 1;
         const float qk = a.qk_scale_log2;
@@ -140,9 +155,9 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
 
         auto issue = [&](int t, int64_t blk, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
             const bool live = t < t_stop;
-            const int t0 = wi.t_begin + (live ? t : t_stop - 1) * kTile;
+            const int t0 = wi.t_begin + (live ? t : t_stop - 1) * TPH;
             const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
-            const int valid = min(wi.t_end - t0, kTile);
+            const int valid = min(wi.t_end - t0, TPH);
             const uint32_t nbytes = live ? row0 + (uint32_t)valid * a.slot_bytes : 0u;
             const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
             const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
@@ -153,9 +168,28 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         };
 
         auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
-            const int t0 = wi.t_begin + t * kTile;
+            const int t0 = wi.t_begin + t * TPH;
             const int valid = wi.t_end - t0;
-            const bool full = valid >= kTile;
+            const bool full = valid >= TPH;
+
+            // With HP > 1 the P.V MFMA also multiplies each V row by the zero
+            // probabilities of the other heads' columns; 0 * Inf or 0 * NaN
+            // would leak a non-finite V value into those heads. A tile whose V
+            // holds one (never in practice) takes the per-head path below.
+            bool v_nonfinite = false;
+            if constexpr (HP > 1) {
+                uint32_t flag = 0;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (!FP8)  // bf16: exponent field all ones, per 16-bit half
+                            flag |= ((vb[i][q] & 0x7f807f80u) + 0x00800080u) & 0x80008000u;
+                        else  // e4m3fn: S.1111.111 per byte
+                            flag |= ((vb[i][q] & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+                    }
+                v_nonfinite = __builtin_amdgcn_ballot_w64(flag != 0) != 0;
+            }
 
             // K and V rows -> LDS as bf16 (rows past the context arrived as zeros)
             auto stage = [&](uint16_t* dst, const u32x4& w, int row) {
@@ -170,7 +204,8 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             };
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                const int row = i * RPI + lane / LPR;
+                // MFMA row of this chunk: head (l % LPC) / LPR, token i * RPI + l / LPC
+                const int row = ((lane % LPC) / LPR) * TPH + i * RPI + lane / LPC;
                 stage(ks, kb[i], row);
                 stage(vs, vb[i], row);
             }
@@ -187,10 +222,15 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
             }
 
-            // online softmax for head c over tokens 4*gq + r
+            // online softmax for column c over rows 4*gq + r: a row counts
+            // when it is a token of the column's KV head inside the context
             float x[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = (!full && 4 * gq + r >= valid) ? -INFINITY : s[r] * qk;
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * gq + r;
+                const bool mine = HP == 1 || (row / TPH) == (c / TPH);
+                x[r] = (!mine || (!full && row % TPH >= valid)) ? -INFINITY : s[r] * qk;
+            }
             float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
             mx = fmaxf(mx, xor_shfl(mx, 16));
             mx = fmaxf(mx, xor_shfl(mx, 32));
@@ -221,13 +261,35 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             // V[4 gq + s/4][16 j + 4 (s % 4)], so lane (gq, c) receives
             // V[4 gq + k][16 j + c], k = 0..3: the A operand, one instruction
             // per MFMA.
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            typedef __attribute__((address_space(3))) uint16_t lds_u16;
+            if (!v_nonfinite) {
 #pragma unroll
-            for (int j = 0; j < NPV; ++j) {
-                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                typedef __attribute__((address_space(3))) uint16_t lds_u16;
-                lds_s16x4* src = (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_base) + 16 * j);
-                const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
+                for (int j = 0; j < NPV; ++j) {
+                    lds_s16x4* src = (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_base) + 16 * j);
+                    const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));
+                    o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
+                }
+            } else {
+                // one MFMA per head with the other heads' V rows zeroed; a
+                // lane keeps the result of its own column's head. Lane (gq, c)
+                // supplies V rows 4 gq .. 4 gq + 3, all of head 4 gq / TPH.
+                const int row_head = (4 * gq) / TPH, col_head = c / TPH;
+#pragma unroll 1
+                for (int h = 0; h < HP; ++h) {
+                    const uint32_t keep = row_head == h ? 0xffffffffu : 0u;
+#pragma unroll
+                    for (int j = 0; j < NPV; ++j) {
+                        // one MFMA at a time: this path is rare, keep its registers few
+                        __builtin_amdgcn_sched_barrier(0);
+                        lds_s16x4* src = (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_base) + 16 * j);
+                        const u32x2 vw = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));
+                        const bf16x4 va = __builtin_bit_cast(bf16x4, u32x2{vw[0] & keep, vw[1] & keep});
+                        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                                 0, 0, 0);
+                        if (col_head == h) o[j] += t;
+                    }
+                }
             }
             // the next tile's staging overwrites this one
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -244,7 +306,7 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             // leave the prefetch behind it outstanding. sched_barrier keeps
             // the compiler from sinking the prefetch below those waits.
             // The table entry of each issued tile was fetched one step earlier.
-            const TableReader tab = make_table_reader(a, wi, t_stop - 1);
+            const TableReader tab = make_table_reader(a, wi, t_stop - 1, TPH);
             uint32_t entry = table_fetch(tab, t_first);
 #pragma unroll
             for (int b = 0; b < NB - 1; ++b) {
@@ -272,46 +334,57 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         l += xor_shfl(l, 32);
 
         __syncthreads();  // V staging is dead; reuse LDS for the combine
+        // column c -> query head cc = (c / TPH) * g + c % TPH of the unit's
+        // G = HP * g heads
+        const int G = HP * g;
         float* sm_ml = smem;
-        float* sm_o = smem + W * g * 2;
-        if (c < g) {
+        float* sm_o = smem + W * G * 2;
+        if (c % TPH < g) {
+            const int cc = (c / TPH) * g + c % TPH;
             if (gq == 0) {
-                sm_ml[(wave * g + c) * 2] = m;
-                sm_ml[(wave * g + c) * 2 + 1] = l;
+                sm_ml[(wave * G + cc) * 2] = m;
+                sm_ml[(wave * G + cc) * 2 + 1] = l;
             }
 #pragma unroll
             for (int j = 0; j < NPV; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm_o[(wave * g + c) * D + 16 * j + 4 * gq + r] = o[j][r];
+                for (int r = 0; r < 4; ++r) sm_o[(wave * G + cc) * D + 16 * j + 4 * gq + r] = o[j][r];
         }
         __syncthreads();
-        combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+        combine_and_store<D>(a, sm_ml, sm_o, W, G, wi.seq, wi.kvh, wi.part, wi.final_out);
     });
 }
 
-template <int D, bool FP8, int NB>
+template <int D, bool FP8, int NB, int HP>
 hipError_t launch_d(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
     const dim3 block((unsigned)(64 * ls.waves));
     const size_t stage = ((size_t)ls.waves * 2 + 1) * kTile * (D + 8) * sizeof(uint16_t);
-    const size_t comb = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
+    const size_t comb = (size_t)ls.waves * HP * a.group * (D + 2) * sizeof(float);
     const size_t lds = stage > comb ? stage : comb;
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB>), grid, block, lds, s, a);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.units_per_seq * a.num_partitions));
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB, HP>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int HP>
 hipError_t launch_nb(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
-    if (ls.depth <= 2) return launch_d<D, FP8, 2>(a, ls, s);
-    if (ls.depth == 3) return launch_d<D, FP8, 3>(a, ls, s);
-    return launch_d<D, FP8, 4>(a, ls, s);
+    if (ls.depth <= 2) return launch_d<D, FP8, 2, HP>(a, ls, s);
+    if (ls.depth == 3) return launch_d<D, FP8, 3, HP>(a, ls, s);
+    return launch_d<D, FP8, 4, HP>(a, ls, s);
+}
+
+template <int D, bool FP8>
+hipError_t launch_hp(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
+    if (ls.heads_per_unit == 4) return launch_nb<D, FP8, 4>(a, ls, s);
+    if (ls.heads_per_unit == 2) return launch_nb<D, FP8, 2>(a, ls, s);
+    return launch_nb<D, FP8, 1>(a, ls, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s) {
-    if (head_dim == 64) return fp8 ? launch_nb<64, true>(a, ls, s) : launch_nb<64, false>(a, ls, s);
-    return fp8 ? launch_nb<128, true>(a, ls, s) : launch_nb<128, false>(a, ls, s);
+    if (head_dim == 64) return fp8 ? launch_hp<64, true>(a, ls, s) : launch_hp<64, false>(a, ls, s);
+    return fp8 ? launch_hp<128, true>(a, ls, s) : launch_hp<128, false>(a, ls, s);
 }
 
 }  // namespace pa

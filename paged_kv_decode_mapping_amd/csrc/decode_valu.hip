@@ -253,7 +253,7 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
             }
         }
         __syncthreads();
-        combine_and_store<D>(a, sm_ml, sm_o, W, wi.seq, wi.kvh, wi.part, wi.final_out);
+        combine_and_store<D>(a, sm_ml, sm_o, W, g, wi.seq, wi.kvh, wi.part, wi.final_out);
     });
 }
 

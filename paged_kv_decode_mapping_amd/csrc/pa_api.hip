@@ -51,6 +51,7 @@ struct Plan {
     int num_partitions = 1;
     bool scheduled = true;
     bool multi = false;          // the multi-row kernel (more than 16 query rows per KV head)
+    int heads_per_unit = 1;      // MFMA kernel: adjacent KV heads sharing a 16-row tile
     int row_blocks = 1;          // multi: blocks of 16 * waves rows per (sequence, KV head)
     int64_t num_workgroups = 0;  // direct grid size, or the item bound when scheduled
     // workspace layout (byte offsets); total = workspace
@@ -195,10 +196,36 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
             return PA_ERR_SHAPE;
         p.waves = o.waves_per_group;
     }
-    // The epilogue stages W * g * (D + 2) floats in LDS; stay within 64 KiB.
-    while (p.waves > 1 && (size_t)p.waves * g * (D + 2) * sizeof(float) > 65536) p.waves /= 2;
+    // MFMA tiles are 16 rows by 16 query-head columns. With g <= 8 a KV
+    // head fills at most half of the columns, so 2 adjacent KV heads share a
+    // tile, 8 tokens each: the columns do useful work and each token's two
+    // rows are read as one contiguous chunk (512 bytes for bf16, D = 128).
+    // Measured on the 70B batch (g = 8, bf16): 79 -> 84 % of peak. 4 heads
+    // of 4-token tiles (g <= 4) measured slower than 1, and fp8 caches gave
+    // erratic times when packed; both are only used when asked for. Only
+    // g in 5..8 packs by default: below that half the columns would still
+    // be padding.
+    if (o.heads_per_tile != 0 && o.heads_per_tile != 1 && o.heads_per_tile != 2 && o.heads_per_tile != 4)
+        return PA_ERR_SHAPE;
+    if (p.variant == PA_VARIANT_MFMA) {
+        int hp = 1;
+        if (o.heads_per_tile != 0) {
+            hp = o.heads_per_tile;
+            if (g * hp > 16 || Hkv % hp != 0) return PA_ERR_UNSUPPORTED;
+        } else if (g >= 5 && g <= 8 && Hkv % 2 == 0 && kv_dtype == PA_KV_BF16) {
+            hp = 2;
+            // the packed bf16 kernel measured best two tiles ahead
+            if (o.prefetch_tiles == 0) p.depth = 3;
+        }
+        p.heads_per_unit = hp;
+    } else if (o.heads_per_tile > 1) {
+        return PA_ERR_UNSUPPORTED;
+    }
+    const int G = g * p.heads_per_unit;  // query heads per work unit
+    // The epilogue stages W * G * (D + 2) floats in LDS; stay within 64 KiB.
+    while (p.waves > 1 && (size_t)p.waves * G * (D + 2) * sizeof(float) > 65536) p.waves /= 2;
     const int64_t cap = (int64_t)MB * bs;  // longest context the tables can hold
-    const int64_t units = (int64_t)S * Hkv;
+    const int64_t units = (int64_t)S * (Hkv / p.heads_per_unit);
     int64_t P = 0;
     st = choose_partition(units, cap, o.partition_tokens, &P);
     if (st != PA_OK) return st;
@@ -214,7 +241,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     // pre-pass; an unsplit grid has one workgroup per (sequence, KV head)
     // and no empty ones. Items pack (partition << 16 | KV head) into 32 bits.
     const bool want = o.schedule == 1 || (o.schedule == 0 && p.num_partitions > 1);
-    p.scheduled = want && p.num_partitions < 32768 && Hkv < 65536;
+    p.scheduled = want && p.num_partitions < 32768 && Hkv / p.heads_per_unit < 65536;
     size_t off = 0;
     if (p.scheduled) {
         p.items_off = kHeaderBytes;
@@ -369,6 +396,7 @@ int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     plan->scheduled = p.scheduled ? 1 : 0;
     plan->num_workgroups = p.num_workgroups;
     plan->workspace_bytes = p.workspace;
+    plan->heads_per_tile = p.heads_per_unit;
     return PA_OK;
 }
 
@@ -436,6 +464,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = num_q_heads / num_kv_heads;
+    a.units_per_seq = num_kv_heads / p.heads_per_unit;
     a.block_size_log2 = log2i(block_size);
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.partition_tokens = p.partition_tokens;
@@ -454,14 +483,14 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
         sa.items = reinterpret_cast<int4*>(ws + p.items_off);
         sa.item_count = reinterpret_cast<int*>(ws);
         sa.num_seqs = num_seqs;
-        sa.num_kv_heads = num_kv_heads;
+        sa.num_kv_heads = a.units_per_seq;  // items are (sequence, unit, partition)
         sa.partition_tokens = p.partition_tokens;
         sa.num_partitions = p.num_partitions;
         sa.max_context = max_blocks_per_seq * block_size;
         e = pa::launch_schedule(sa, s);
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
-    const pa::LaunchShape ls{p.waves, p.depth};
+    const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit};
     e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, ls, s)
                                      : pa::launch_decode_valu(a, head_dim, fp8, ls, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;

@@ -21,13 +21,16 @@ __device__ __forceinline__ float state_weight(float m_w, float M) {
     return (m_w == -INFINITY) ? 0.0f : fast_exp2(m_w - M);
 }
 
-// sm_ml: [W][g][2] (m, l); sm_o: [W][g][D]. Called by all threads of the
+// A workgroup's unit covers G consecutive query heads: unit * G .. unit * G
+// + G - 1 (G = g with one KV head per unit, HP * g with HP of them).
+// sm_ml: [W][G][2] (m, l); sm_o: [W][G][D]. Called by all threads of the
 // workgroup after a barrier that follows the writes into LDS.
 template <int D>
 __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const float* sm_ml,
-                                                  const float* sm_o, int W, int seq, int kvh,
+                                                  const float* sm_o, int W, int G, int seq, int unit,
                                                   int part, bool final_out) {
-    const int g = a.group;
+    const int g = G;
+    const int kvh = unit;
     for (int idx = (int)threadIdx.x; idx < g * D; idx += (int)blockDim.x) {
         const int h = idx / D;
         const int d = idx - h * D;
@@ -83,12 +86,13 @@ __device__ __forceinline__ WorkItem make_work_item(const DecodeArgs& a, int seq,
     return w;
 }
 
-// Direct grid: workgroup b takes item (unit = b / P, part = b % P).
+// Direct grid: workgroup b takes item (unit = b / P, part = b % P); a
+// sequence has units_per_seq units (its KV heads, or groups of them).
 __device__ __forceinline__ WorkItem decode_work_item(const DecodeArgs& a) {
     const int bid = (int)blockIdx.x;
     const int P = a.num_partitions;
     const int unit = bid / P;
-    return make_work_item(a, unit / a.num_kv_heads, unit % a.num_kv_heads, bid % P);
+    return make_work_item(a, unit / a.units_per_seq, unit % a.units_per_seq, bid % P);
 }
 
 __device__ __forceinline__ WorkItem scheduled_item(const int4& r) {
@@ -136,30 +140,33 @@ struct TableReader {
     __amdgpu_buffer_rsrc_t rsrc;  // this sequence's table row
     int t_begin;                  // first token of the item
     int last_tile;                // entries past the item's last tile read its entry
+    int tile_tokens;              // tokens per tile (a divisor of the block size)
     int block_size_log2;
     int last_block;
 };
 
 __device__ __forceinline__ TableReader make_table_reader(const int32_t* block_tables, int max_blocks_per_seq,
                                                          int block_size_log2, int last_block, int seq,
-                                                         int t_begin, int last_tile) {
+                                                         int t_begin, int last_tile, int tile_tokens = kTile) {
     TableReader r;
     r.rsrc = make_rsrc(block_tables + (int64_t)seq * max_blocks_per_seq, (uint32_t)max_blocks_per_seq * 4u);
     r.t_begin = t_begin;
     r.last_tile = last_tile;
+    r.tile_tokens = tile_tokens;
     r.block_size_log2 = block_size_log2;
     r.last_block = last_block;
     return r;
 }
 
-__device__ __forceinline__ TableReader make_table_reader(const DecodeArgs& a, const WorkItem& wi, int last_tile) {
+__device__ __forceinline__ TableReader make_table_reader(const DecodeArgs& a, const WorkItem& wi, int last_tile,
+                                                         int tile_tokens = kTile) {
     return make_table_reader(a.block_tables, a.max_blocks_per_seq, a.block_size_log2, a.last_block, wi.seq,
-                             wi.t_begin, last_tile);
+                             wi.t_begin, last_tile, tile_tokens);
 }
 
 // Start fetching the table entry of tile t (an index within the item).
 __device__ __forceinline__ uint32_t table_fetch(const TableReader& r, int t) {
-    const int tok = r.t_begin + min(t, r.last_tile) * kTile;
+    const int tok = r.t_begin + min(t, r.last_tile) * r.tile_tokens;
     return __builtin_amdgcn_raw_buffer_load_b32(r.rsrc, (uint32_t)(tok >> r.block_size_log2) << 2, 0, 0);
 }
 

@@ -20,6 +20,7 @@ struct DecodeArgs {
     float* part_ml;                // [S, Hq, P, 2] (max in log2 units, sum), split only
     float* part_o;                 // [S, Hq, P, D] unnormalised outputs, split only
     int32_t num_seqs, num_q_heads, num_kv_heads, group;
+    int32_t units_per_seq;         // work units per sequence: KV heads / heads per unit
     int32_t block_size_log2, max_blocks_per_seq;
     int32_t partition_tokens, num_partitions;
     int32_t last_block;            // min(num_blocks, 2^31) - 1: the largest usable block id
@@ -105,6 +106,7 @@ struct CopyBlocksArgs {
 struct LaunchShape {
     int waves;          // wavefronts per workgroup
     int depth;          // tiles a wave keeps in its register ring (2..4)
+    int heads_per_unit; // MFMA kernel: adjacent KV heads sharing one 16-row tile (1, 2 or 4)
 };
 
 // Launchers: return the hipError_t of the launch.

@@ -93,6 +93,11 @@ def _reserved(v):
     (dict(opts=pa._opts(partition_tokens=-1, schedule=1)), -6), (dict(opts=pa._opts(partition_tokens=-1, schedule=2)), -2),
     (dict(opts=pa._opts(partition_tokens=-1, schedule=1), ws=A + 16, wsb=1 << 20), -4),
     (dict(opts=_reserved(1)), -2), (dict(opts=_reserved(-1)), -2),
+    (dict(opts=pa._opts(partition_tokens=-1, heads_per_tile=3)), -2),
+    (dict(opts=pa._opts(partition_tokens=-1, heads_per_tile=8)), -2),
+    (dict(Hkv=1, Hq=4, opts=pa._opts(partition_tokens=-1, variant="mfma", heads_per_tile=2)), -3),
+    (dict(Hq=16, Hkv=2, opts=pa._opts(partition_tokens=-1, heads_per_tile=4)), -3),
+    (dict(opts=pa._opts(partition_tokens=-1, variant="valu", heads_per_tile=2)), -3),
 ])
 def test_decode_rejects_bad_arguments_without_launching(lib, kw, code):
     assert _decode(lib, **kw) == code

@@ -255,6 +255,29 @@ def test_decode_fp8_matches_oracle(lib, name, variant):
     compare(host_bits(out), ref, *BF16_TOL)
 
 
+@pytest.mark.parametrize("name,hp", [("tiny", 1), ("tiny", 2), ("mixed_batch", 1), ("mixed_batch", 2),
+                                     ("mixed_batch", 4), ("long_splitk", 4), ("llama70b_gqa", 1),
+                                     ("llama70b_gqa", 2)])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_heads_per_tile_agree_with_oracle(lib, name, hp, kv):
+    """The MFMA kernel packs HP adjacent KV heads into one 16-row tile (16 / HP
+    tokens of each): every packing, unsplit and split, against the oracle."""
+    w = W.make_workload(name, **REDUCED[name])
+    ks = vs = 1.0
+    kc, vc, kvd, tol = w.k_cache, w.v_cache, oracle.KV_BF16, BF16_TOL
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
+    ref = _oracle(w, kv_dtype=kvd, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+    d = DeviceWorkload(w, kc, vc)
+    for part in (-1, 48):
+        note(f"heads_per_tile={hp} {name} {kv} partition={part}")
+        got = host_bits(d.decode(k_scale=ks, v_scale=vs, variant="mfma", heads_per_tile=hp, partition_tokens=part))
+        torch.cuda.synchronize()
+        compare(got, ref, *tol)
+
+
 @pytest.mark.parametrize("prefetch", [1, 2])
 def test_fp8_decode_edge_contexts_and_pairs(lib, prefetch):
     """The fp8 MFMA kernel consumes a wave's tiles in pairs: contexts that
