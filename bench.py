@@ -64,7 +64,7 @@ def load_traffic(workload: str, kv: str, plan: dict):
     except Exception:
         return None
     from paged_kv_decode_mapping_amd.profiling import kernel_source_hash
-    if d.get("kernel_source_hash") != kernel_source_hash() or d.get("plan") != plan:
+    if d.get("kernel_source_hash") != kernel_source_hash(plan) or d.get("plan") != plan:
         return None
     return d.get("bytes_per_launch")
 
@@ -273,6 +273,123 @@ def bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b: int, k_scale: floa
     return 0
 
 
+def bench_cascade(args, w, k_cache, v_cache, kv_b: int, k_scale: float, v_scale: float, kq=None, vq=None) -> int:
+    """Time pa_decode_cascade on a workload whose sequences share a prefix (the
+    mixed batch): the batch reordered with its sharers first (one group), the
+    shared prefix attended once for the group. pa_decode on the same batch is
+    timed beside it."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    from paged_kv_decode_mapping_amd import workloads as W
+    s = w.spec
+    b = W.cascade_batch(w)
+    if b.num_groups == 0:
+        log(f"{s.name} has no shared prefix: nothing to cascade")
+        return 2
+    dev = k_cache.device
+    q = torch.from_numpy(b.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    tables = torch.from_numpy(b.block_tables).to(dev)
+    ctx = torch.from_numpy(b.context_lens).to(dev)
+    ptab = torch.from_numpy(b.prefix_tables).to(dev)
+    plen = torch.from_numpy(b.prefix_lens).to(dev)
+    gst = torch.from_numpy(b.group_start).to(dev)
+    kvd = pa.PA_KV_BF16 if kv_b == 2 else pa.PA_KV_FP8_E4M3FN
+    need = pa.pa_decode_cascade_workspace_size(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
+                                               w.max_blocks_per_seq, b.num_groups, b.max_group_size,
+                                               b.prefix_tables.shape[1], kvd, partition_tokens=args.partition)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
+                                 w.max_blocks_per_seq, kvd, partition_tokens=args.partition)
+    ws_d = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    out_d = torch.empty_like(q)
+
+    def cascade():
+        pa.pa_decode_cascade(q, k_cache, v_cache, tables, ctx, ptab, plen, gst, w.scale, out,
+                             max_group_size=b.max_group_size, k_scale=k_scale, v_scale=v_scale, workspace=ws,
+                             partition_tokens=args.partition)
+
+    def plain():
+        pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out_d, k_scale=k_scale, v_scale=v_scale,
+                     workspace=ws_d, partition_tokens=args.partition)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(e) for a, e in ev]), time.perf_counter() - t0
+
+    cas_ms, wall = timed(cascade)
+    dec_ms, _ = timed(plain)
+    cl = b.context_lens.astype(np.int64)
+    n_sh = int(b.group_start[1])
+    shared = np.zeros_like(cl)
+    shared[:n_sh] = np.minimum(cl[:n_sh], int(b.prefix_lens[0]))
+    row = s.num_kv_heads * s.head_dim * kv_b
+    logical = decode_bytes(w, kv_b)
+    # the cascade must read the prefix once (as far as its longest member
+    # goes) and each sequence's tokens after it; q, out and tables as before
+    unique = logical - int(2 * shared.sum() * row) + int(2 * shared.max() * row)
+    avg = float(cas_ms.mean())
+    avg_d = float(dec_ms.mean())
+    log(f"cascade avg {avg * 1e3:.1f} us (p10 {np.percentile(cas_ms, 10) * 1e3:.1f}, p90 "
+        f"{np.percentile(cas_ms, 90) * 1e3:.1f}); pa_decode on the same batch {avg_d * 1e3:.1f} us; "
+        f"logical {logical / (avg * 1e-3) / 1e9:.0f} GB/s, unique {unique / (avg * 1e-3) / 1e9:.0f} GB/s")
+    base = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kvd_o = oracle.KV_BF16 if kv_b == 2 else oracle.KV_FP8_E4M3FN
+        kc = w.k_cache if kq is None else kq
+        vc = w.v_cache if vq is None else vq
+        units_all = np.random.default_rng(5).permutation(s.num_seqs * s.num_kv_heads)
+        done, t_total, ob = 0, 0.0, 0
+        while done < len(units_all) and t_total < 12.0:
+            u = units_all[done:done + 64]
+            t1 = time.perf_counter()
+            oracle.cascade_decode(b.q, kc, vc, b.block_tables, b.context_lens, b.prefix_tables, b.prefix_lens,
+                                  b.group_start, w.scale, max_group_size=b.max_group_size, units=u,
+                                  kv_dtype=kvd_o, k_scale=k_scale, v_scale=v_scale)
+            t_total += time.perf_counter() - t1
+            seqs = u // s.num_kv_heads
+            ob += int((2 * cl[seqs] * s.head_dim * kv_b + 4 * s.group * s.head_dim).sum())
+            done += len(u)
+        base = {"value": round(ob / t_total / 1e9, 3), "unit": "GB/s (logical)", "cores": oracle.num_threads(),
+                "kind": "oracle", "sample": f"{done} of {len(units_all)} (sequence, KV head) units, "
+                                            f"{t_total:.1f} s, float64, gather through the composed table"}
+        log(f"cpu baseline {base}")
+    achieved = unique / (avg * 1e-3) / 1e9
+    res = {
+        "metric": "shared-prefix (cascade) decode: logical GB/s (bytes a plain decode reads for the same outputs)",
+        "value": round(logical * args.steps / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.kv, "data": "synthetic",
+        "config": {"workload": f"{s.name} reordered, {n_sh} sequences sharing a {int(b.prefix_lens[0])}-token "
+                               f"prefix as one group", "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads,
+                   "num_kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "block_size": s.block_size},
+        "cascade_us": {"avg": round(avg * 1e3, 2), "p10": round(float(np.percentile(cas_ms, 10)) * 1e3, 2),
+                       "p90": round(float(np.percentile(cas_ms, 90)) * 1e3, 2)},
+        "pa_decode_us": round(avg_d * 1e3, 2),
+        "bytes": {"logical": logical, "unique": unique},
+        "decode_tokens_per_s_kernel": round(s.num_seqs / (avg * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "pa_decode_cascade (schedule + prefix pass + decode + merge), unique bytes"},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_copy_blocks(args, w, k_cache, v_cache, kv_b: int, kq=None, vq=None) -> int:
     """Time pa_copy_blocks: each call copies --pairs whole blocks of K and V
     (src and dst drawn without replacement from a fresh permutation of the
@@ -350,12 +467,14 @@ def main() -> int:
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
     ap.add_argument("--prefetch", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
-    ap.add_argument("--op", choices=["step", "copy_blocks", "multi", "graph", "stream"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "multi", "graph", "stream", "cascade"], default="step",
                     help="step: cache write + decode (the default measurement); copy_blocks: time "
                          "pa_copy_blocks on the workload's pool; multi: time pa_decode_multi with "
                          "--qlen query tokens per sequence; graph: the step captured in a HIP graph, "
                          "replayed (eager step time reported beside it); stream: the streaming-read "
-                         "reference: the library's probe kernel reading 4 GiB once, the practical read ceiling")
+                         "reference: the library's probe kernel reading 4 GiB once, the practical read ceiling; "
+                         "cascade: pa_decode_cascade on a workload with a shared prefix (mixed_batch), its "
+                         "sharers as one group, pa_decode timed beside it")
     ap.add_argument("--qlen", type=int, default=4, help="query tokens per sequence for --op multi")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs per pa_copy_blocks call")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -417,6 +536,8 @@ def main() -> int:
         return bench_copy_blocks(args, w, k_cache, v_cache, kv_b, kq, vq)
     if args.op == "multi":
         return bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b, k_scale, v_scale, kq, vq)
+    if args.op == "cascade":
+        return bench_cascade(args, w, k_cache, v_cache, kv_b, k_scale, v_scale, kq, vq)
     plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
                                  w.max_blocks_per_seq, pa.PA_KV_BF16 if args.kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
                                  partition_tokens=args.partition, variant=args.variant, waves=args.waves,

@@ -249,6 +249,67 @@ size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens
                                       int32_t partition_tokens);
 
 /*
+ * pa_decode_cascade -- pa_decode for a batch in which groups of sequences
+ * share a cached prefix, reading each shared prefix once per group instead
+ * of once per sequence. Tutorial §4.3 (Prefix Caching): requests that share
+ * a system prompt reuse the physical blocks cached for it; the prefix cache
+ * keeps, per prefix, its list of blocks and its length -- here row k of
+ * prefix_tables and prefix_lens[k].
+ *
+ * Group k is the run of sequences group_start[k] .. group_start[k+1] - 1 of
+ * the batch (order the batch so that sharers are adjacent). Member i of
+ * group k, with shared_i = min(context_lens[i], prefix_lens[k]), reads its
+ * tokens 0 .. shared_i - 1 through prefix_tables[k] and its tokens shared_i
+ * .. context_lens[i] - 1 through its own block_tables row; a sequence in no
+ * group reads everything through its own row. Apart from that gather the
+ * result is pa_decode's: for every query head, softmax(scale * q K^T) V over
+ * the sequence's context_lens[i] tokens, bf16 output. When each member's
+ * table already names the prefix blocks (as with prefix caching) it is the
+ * same attention as pa_decode on the same arguments.
+ *
+ * How: one pass attends each group's prefix for all query heads of all its
+ * members at once (the multi-row kernel of pa_decode_multi, so a prefix
+ * tile is loaded once for the whole group), the decode kernels attend the
+ * rest of every context, and a log-sum-exp merge combines the two.
+ *
+ *   prefix_tables    device, [num_groups, max_prefix_blocks] int32
+ *   prefix_lens      device, [num_groups] int32 tokens, each a multiple of
+ *                    block_size and <= max_prefix_blocks * block_size
+ *   group_start      device, [num_groups + 1] int32, non-decreasing, from
+ *                    >= 0 to <= num_seqs
+ *   max_group_size   host, >= every group's size (sequences past it in a
+ *                    group are treated as in no group)
+ *   workspace        device, >= pa_decode_cascade_workspace_size(...) bytes,
+ *                    256-byte aligned (always needed): the work list and
+ *                    both passes' partial states
+ * Other arguments as in pa_decode (opts apply to the decode kernels of the
+ * second pass; the work list is always used). num_groups = 0 (the three
+ * group arrays may then be NULL) is a plain decode. Supported: as pa_decode
+ * with at most 16 query heads per KV head (PA_ERR_UNSUPPORTED beyond).
+ * Preconditions (pa_check_cascade_inputs verifies them): those of pa_decode
+ * for block_tables and context_lens, the layout of the three group arrays
+ * above, and prefix table entries covering prefix_lens[k] inside the pool.
+ * A prefix length that is not whole blocks is rounded down, its last
+ * tokens then being read through the member's own row.
+ */
+int pa_decode_cascade(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* prefix_tables, const int32_t* prefix_lens,
+                      const int32_t* group_start, float scale, void* out,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                      int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
+                      int32_t kv_dtype, float k_scale, float v_scale,
+                      void* workspace, size_t workspace_bytes,
+                      const pa_decode_opts* opts, void* stream);
+
+/* Bytes of workspace pa_decode_cascade needs (0 for invalid sizes). */
+size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                        int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
+                                        int32_t kv_dtype, const pa_decode_opts* opts);
+
+/*
  * pa_decode_get_plan -- the launch plan pa_decode would use for these sizes
  * on the current device (no launch). Returns PA_OK and fills *plan, or the
  * error pa_decode would return for these sizes.
@@ -282,6 +343,15 @@ int pa_check_cache_write_inputs(const int64_t* slot_mapping, int64_t num_tokens,
 int pa_check_decode_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                            void* stream);
+/* pa_check_cascade_inputs -- those of pa_decode_cascade's group arrays:
+ * group_start non-decreasing from >= 0 to <= num_seqs with no group larger
+ * than max_group_size; every prefix length a multiple of block_size in
+ * [0, max_prefix_blocks * block_size]; the prefix table entries covering it
+ * in [0, num_blocks). Same conventions as the two checks above. */
+int pa_check_cascade_inputs(const int32_t* prefix_tables, const int32_t* prefix_lens,
+                            const int32_t* group_start, int32_t num_groups, int32_t max_group_size,
+                            int32_t max_prefix_blocks, int32_t num_seqs, int32_t block_size,
+                            int64_t num_blocks, void* stream);
 
 /*
  * pa_probe_stream_read -- read `bytes` bytes of device memory once with

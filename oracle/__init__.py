@@ -210,6 +210,54 @@ def multi_decode(q, k_cache, v_cache, block_tables, context_lens, query_start, s
     return out
 
 
+def cascade_tables(block_tables, context_lens, prefix_tables, prefix_lens, group_start, block_size: int,
+                   max_group_size: Optional[int] = None) -> np.ndarray:
+    """The block table a cascade decode reads through (Tutorial §4.3, prefix
+    caching: a cached prefix is a list of physical blocks plus a length,
+    reused by every request that starts with it). Group k is the run of
+    sequences group_start[k] .. group_start[k+1] - 1 (its first
+    max_group_size members, when given); member i holds shared_i =
+    min(context_lens[i], prefix_lens[k]) prefix tokens, so its logical
+    blocks b with b * block_size < shared_i are the prefix's blocks
+    prefix_tables[k][b], and the rest come from its own row. Returns the
+    composed int32 [S, MB] table (rows of sequences in no group unchanged).
+    Prefix lengths must be whole blocks, so no block mixes the two sources."""
+    tables = np.array(block_tables, dtype=np.int32, copy=True)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    pt = np.asarray(prefix_tables, dtype=np.int64)
+    pl = np.asarray(prefix_lens, dtype=np.int64)
+    gs = np.asarray(group_start, dtype=np.int64)
+    S, MB = tables.shape
+    G = pl.shape[0]
+    assert gs.shape == (G + 1,) and pt.shape[0] == G
+    assert np.all(np.diff(gs) >= 0) and (G == 0 or (gs[0] >= 0 and gs[-1] <= S))
+    assert np.all(pl % block_size == 0) and np.all(pl >= 0) and np.all(pl <= pt.shape[1] * block_size)
+    for k in range(G):
+        last = gs[k + 1] if max_group_size is None else min(gs[k + 1], gs[k] + max_group_size)
+        for i in range(int(gs[k]), int(last)):
+            shared = min(int(ctx[i]), int(pl[k]))
+            nb = (shared + block_size - 1) // block_size
+            tables[i, :nb] = pt[k, :nb]
+    return tables
+
+
+def cascade_decode(q, k_cache, v_cache, block_tables, context_lens, prefix_tables, prefix_lens, group_start,
+                   scale, *, max_group_size: Optional[int] = None, units: Optional[Sequence[int]] = None,
+                   kv_dtype: int = KV_BF16, k_scale: float = 1.0, v_scale: float = 1.0,
+                   threads: int = 0) -> np.ndarray:
+    """Decode of a cascade call -> float64 [S, Hq, D] (or [n_units, g, D] for
+    `units`): the plain decode definition over each sequence's context,
+    gathered through the table cascade_tables() composes."""
+    bs = k_cache.shape[1]
+    tables = cascade_tables(block_tables, context_lens, prefix_tables, prefix_lens, group_start, bs,
+                            max_group_size)
+    if units is None:
+        return decode(q, k_cache, v_cache, tables, context_lens, scale, kv_dtype=kv_dtype, k_scale=k_scale,
+                      v_scale=v_scale, threads=threads)
+    return decode_units(q, k_cache, v_cache, tables, context_lens, scale, units, q.shape[1], kv_dtype=kv_dtype,
+                        k_scale=k_scale, v_scale=v_scale, threads=threads)
+
+
 def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> int:
     """In-place block copy of both caches ([N, bs, Hkv, D], uint16 bf16 bits or
     uint8 fp8 codes) for (src, dst) pairs; negative ids are skipped."""

@@ -19,6 +19,14 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 
 PA_OK = 0
+PA_ERR_NULL = -1
+PA_ERR_SHAPE = -2
+PA_ERR_UNSUPPORTED = -3
+PA_ERR_ALIGN = -4
+PA_ERR_DTYPE = -5
+PA_ERR_WORKSPACE = -6
+PA_ERR_LAUNCH = -7
+PA_ERR_DEVICE = -8
 PA_ERR_PRECONDITION = -9
 PA_KV_BF16 = 1
 PA_KV_FP8_E4M3FN = 2
@@ -79,6 +87,14 @@ def load_library(path: Optional[str] = None):
     lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_decode_multi_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.pa_decode_multi_workspace_size.restype = sz
+    lib.pa_decode_cascade.argtypes = [P, P, P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, i32, i64,
+                                      i32, i32, i32, i32, f32, f32, P, sz, ctypes.POINTER(pa_decode_opts), P]
+    lib.pa_decode_cascade.restype = ctypes.c_int
+    lib.pa_decode_cascade_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(pa_decode_opts)]
+    lib.pa_decode_cascade_workspace_size.restype = sz
+    lib.pa_check_cascade_inputs.argtypes = [P, P, P, i32, i32, i32, i32, i32, i64, P]
+    lib.pa_check_cascade_inputs.restype = ctypes.c_int
     lib.pa_probe_stream_read.argtypes = [P, i64, i32, P, P]
     lib.pa_probe_stream_read.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [P, P, P, i64, i32, i32, i32, i64, i32, P]
@@ -292,6 +308,70 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     return out
 
 
+def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, prefix_tables, prefix_lens, group_start,
+                      scale: float, out=None, *, max_group_size: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                      workspace=None, partition_tokens: int = 0, variant="auto", waves: int = 0, prefetch: int = 0,
+                      heads_per_tile: int = 0, stream=None):
+    """Decode step for a batch whose prefix groups (sequences group_start[k] ..
+    group_start[k+1] - 1) share a cached prefix: prefix_tables [G, PMB] int32
+    and prefix_lens [G] int32 name each prefix's blocks and length; each
+    prefix is read once per group. max_group_size (host) bounds the group
+    sizes. Otherwise as pa_decode; returns out [S, Hq, D] bf16."""
+    import torch
+    lib = load_library()
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_cache, "k_cache", None, 4)
+    _check(v_cache, "v_cache", None, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    _check(prefix_tables, "prefix_tables", torch.int32, 2)
+    _check(prefix_lens, "prefix_lens", torch.int32, 1)
+    _check(group_start, "group_start", torch.int32, 1)
+    kvd = _kv_dtype(k_cache)
+    if _kv_dtype(v_cache) != kvd or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache differ")
+    S, Hq, D = q.shape
+    N, bs, Hkv, D2 = k_cache.shape
+    G, PMB = prefix_tables.shape
+    if D2 != D or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("shape mismatch")
+    if prefix_lens.shape != (G,) or group_start.shape != (G + 1,):
+        raise ValueError("group arrays: prefix_lens [G], group_start [G + 1]")
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out shape")
+    o = _opts(partition_tokens, variant, waves, prefetch, 0, heads_per_tile)
+    need = lib.pa_decode_cascade_workspace_size(S, Hq, Hkv, D, bs, MB, G, int(max_group_size), PMB, kvd,
+                                                ctypes.byref(o))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    st = lib.pa_decode_cascade(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                               context_lens.data_ptr(), ptr(prefix_tables), ptr(prefix_lens), ptr(group_start),
+                               float(scale), out.data_ptr(), S, Hq, Hkv, D, bs, MB, N, G, int(max_group_size),
+                               PMB, kvd, float(k_scale), float(v_scale), ws_ptr, ws_bytes, ctypes.byref(o),
+                               _stream_ptr(stream))
+    if st != PA_OK:
+        raise PAError(st, "pa_decode_cascade")
+    return out
+
+
+def pa_decode_cascade_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, num_groups, max_group_size, max_prefix_blocks,
+                                     kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0,
+                                     prefetch=0, heads_per_tile=0) -> int:
+    o = _opts(partition_tokens, variant, waves, prefetch, 0, heads_per_tile)
+    return int(load_library().pa_decode_cascade_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_groups,
+        max_group_size, max_prefix_blocks, kv_dtype, ctypes.byref(o)))
+
+
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                              kv_dtype=PA_KV_BF16, partition_tokens=0, variant="auto", waves=0, prefetch=0,
                              schedule=0, heads_per_tile=0) -> int:
@@ -330,6 +410,29 @@ def pa_check_decode_inputs(block_tables, context_lens, num_blocks: int, block_si
                                     int(num_blocks), _stream_ptr(stream))
     if st not in (PA_OK, PA_ERR_PRECONDITION):
         raise PAError(st, "pa_check_decode_inputs")
+    return st
+
+
+def pa_check_cascade_inputs(prefix_tables, prefix_lens, group_start, num_seqs: int, max_group_size: int,
+                            num_blocks: int, block_size: int, stream=None) -> int:
+    """Check pa_decode_cascade's group arrays (offsets rising within the batch,
+    group sizes, whole-block prefix lengths within the table row, covering
+    prefix table entries inside the pool). Synchronises. Returns PA_OK or
+    PA_ERR_PRECONDITION; raises on argument errors."""
+    import torch
+    lib = load_library()
+    _check(prefix_tables, "prefix_tables", torch.int32, 2)
+    _check(prefix_lens, "prefix_lens", torch.int32, 1)
+    _check(group_start, "group_start", torch.int32, 1)
+    G, PMB = prefix_tables.shape
+    if prefix_lens.shape != (G,) or group_start.shape != (G + 1,):
+        raise ValueError("group arrays: prefix_lens [G], group_start [G + 1]")
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    st = lib.pa_check_cascade_inputs(ptr(prefix_tables), ptr(prefix_lens), ptr(group_start), G,
+                                     int(max_group_size), PMB, int(num_seqs), int(block_size), int(num_blocks),
+                                     _stream_ptr(stream))
+    if st not in (PA_OK, PA_ERR_PRECONDITION):
+        raise PAError(st, "pa_check_cascade_inputs")
     return st
 
 

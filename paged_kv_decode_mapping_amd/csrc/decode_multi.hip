@@ -42,11 +42,22 @@
 // than one partition it stores unnormalised partial states (m, l, o) per row
 // and pa_multi_merge_kernel combines them by log-sum-exp.
 //
+// Cascade prefix pass. Sequences that share a cached prefix (Tutorial §4.3,
+// prefix caching: the same physical blocks in every sharer's table) attend
+// to it here once per group instead of once per sequence: the grid's
+// "sequences" are the prefix groups, each group's rows are the query heads
+// of all its member sequences, the tiles come from the prefix's own table
+// row, and a member attends the first min(its context, prefix length)
+// tokens. The states are always stored as partials; the cascade merge adds
+// the states of the suffix pass (the decode kernels over the rest of each
+// context).
+//
 // Order. With a work list (the decode path's longest-first list of
 // (sequence, KV head, partition) items) workgroups take items in that order,
 // so the longest contexts start first; one cooperative tile stream per
 // workgroup makes a long item slow, and a long item started last would
 // stretch the whole launch.
+#include "pa_cascade.h"
 #include "pa_epilogue.h"
 
 namespace pa {
@@ -114,13 +125,21 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
         it.seq = bid / a.num_kv_heads;
     }
     const int cap = a.max_blocks_per_seq << a.block_size_log2;
-    int L = a.context_lens[it.seq];
-    it.L = L < 0 ? 0 : (L > cap ? cap : L);
-    if (a.query_start != nullptr) {
-        it.q0 = a.query_start[it.seq];
-        int n = a.query_start[it.seq + 1] - it.q0;
+    // A cascade prefix pass: item "sequence" k is prefix group k, whose
+    // member sequences are the query rows (one token each).
+    const bool prefix_pass = a.cascade.group_start != nullptr;
+    if (prefix_pass) {
+        it.L = min(cascade_prefix_tokens(a.cascade, it.seq, a.block_size_log2), cap);
+    } else {
+        const int L = a.context_lens[it.seq];
+        it.L = L < 0 ? 0 : (L > cap ? cap : L);
+    }
+    if (prefix_pass || a.query_start != nullptr) {
+        const int32_t* starts = prefix_pass ? a.cascade.group_start : a.query_start;
+        it.q0 = starts[it.seq];
+        int n = starts[it.seq + 1] - it.q0;
         n = n > a.max_query_len ? a.max_query_len : n;
-        // rows outside [0, num_query_rows) are never touched, whatever query_start holds
+        // rows outside [0, num_query_rows) are never touched, whatever the offsets hold
         if (it.q0 < 0 || it.q0 > a.num_query_rows) n = 0;
         else if (n > a.num_query_rows - it.q0) n = a.num_query_rows - it.q0;
         it.n = n < 0 ? 0 : n;
@@ -134,7 +153,7 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     if (row0 >= rows) return;
     // the last position any row of this block attends to
     const int last_row = min(rows, row0 + 16 * W) - 1;
-    const int pos_max = it.L - it.n + last_row / g;
+    const int pos_max = prefix_pass ? it.L - 1 : it.L - it.n + last_row / g;
     const int t_begin = it.part * a.partition_tokens;
     const int t_end = min(min(t_begin + a.partition_tokens, pos_max + 1), it.L);
     if (it.part > 0 && t_begin >= t_end) return;  // nothing of this block here (partition 0 always stores)
@@ -159,8 +178,18 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
 
     // this lane's row (column c of the wave's tile) and its causal limit
     const int my_rho = row0 + wave * 16 + c;
-    const bool my_valid = my_rho < rows;
-    const int my_pos = my_valid ? it.L - it.n + my_rho / g : -1;  // sees tokens <= my_pos
+    bool my_valid = my_rho < rows;
+    int my_pos = my_valid ? it.L - it.n + my_rho / g : -1;  // sees tokens <= my_pos
+    if (prefix_pass && my_valid) {
+        // a member attends min(its context, the prefix) tokens here; a row
+        // that the group lookup does not place in this group (malformed
+        // offsets) stores nothing, so no two groups write one row's state
+        const int seq = it.q0 + my_rho / g;
+        int ctx = a.context_lens[seq];
+        ctx = ctx < 0 ? 0 : (ctx > a.cascade.max_context ? a.cascade.max_context : ctx);
+        my_valid = cascade_group(a.cascade, seq) == it.seq;
+        my_pos = my_valid ? min(ctx, it.L) - 1 : -1;
+    }
     const uint16_t* q_row = qs + (wave * 16 + c) * RS + 8 * gq;
 
     float m = -INFINITY, l = 0.0f;
@@ -308,7 +337,7 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     if (!my_valid) return;
     const int r = my_rho / g, hh = my_rho - (my_rho / g) * g;
     const int64_t row = (int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh;
-    if (a.num_partitions == 1) {
+    if (a.num_partitions == 1 && !prefix_pass) {
         const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
 #pragma unroll
         for (int j = 0; j < NPV; ++j) {
@@ -405,7 +434,7 @@ hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, h
     hipError_t e;
     if (head_dim == 64) e = fp8 ? launch_df<64, true>(a, waves, s) : launch_df<64, false>(a, waves, s);
     else e = fp8 ? launch_df<128, true>(a, waves, s) : launch_df<128, false>(a, waves, s);
-    if (e != hipSuccess || a.num_partitions == 1) return e;
+    if (e != hipSuccess || a.num_partitions == 1 || a.cascade.group_start != nullptr) return e;
     const int64_t waves_total = (int64_t)a.num_query_rows * a.num_q_heads;
     const dim3 grid((unsigned)((waves_total * 64 + 255) / 256));
     if (head_dim == 64) hipLaunchKernelGGL(pa_multi_merge_kernel<64>, grid, dim3(256), 0, s, a);

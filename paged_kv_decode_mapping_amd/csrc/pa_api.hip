@@ -55,6 +55,7 @@ struct Plan {
     int row_blocks = 1;          // multi: blocks of 16 * waves rows per (sequence, KV head)
     int64_t num_workgroups = 0;  // direct grid size, or the item bound when scheduled
     // workspace layout (byte offsets); total = workspace
+    bool partials = false;       // split-K partial states in the workspace
     size_t items_off = 0, ml_off = 0, o_off = 0;
     size_t workspace = 0;
 };
@@ -144,6 +145,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     }
     if (p.num_partitions > 1) {
         const size_t prow = (size_t)Tq * Hq * p.num_partitions;
+        p.partials = true;
         p.ml_off = off;
         p.o_off = off + align_up(prow * 2 * sizeof(float), 256);
         off = p.o_off + prow * D * sizeof(float);
@@ -249,6 +251,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     }
     if (p.num_partitions > 1) {
         const size_t rows = (size_t)S * Hq * p.num_partitions;
+        p.partials = true;
         p.ml_off = off;
         p.o_off = off + align_up(rows * 2 * sizeof(float), 256);
         off = p.o_off + rows * D * sizeof(float);
@@ -258,12 +261,86 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     return PA_OK;
 }
 
-// Launch the multi-row kernel for a plan made by make_multi_plan.
-int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
-              float scale, void* out, int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv,
-              int32_t D, int32_t bs, int32_t MB, int64_t num_blocks, int32_t kv_dtype, float k_scale,
-              float v_scale, void* workspace, void* stream) {
+// Plan of a cascade call: the decode plan for the suffix pass, on the
+// device work list (its items start after each sequence's prefix tokens)
+// and always with partial states (a sequence with prefix tokens is merged
+// even when its suffix is one partition); and, when there are groups, a
+// multi-row plan for the prefix pass over G groups of at most maxg member
+// sequences, whose states (prefix_partitions slots per row) follow the
+// suffix partials in the workspace.
+struct CascadePlan {
+    Plan suffix;
+    Plan prefix;
+    bool has_prefix = false;
+    size_t pre_ml_off = 0, pre_o_off = 0;
+    size_t workspace = 0;
+};
+
+int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB, int32_t kv_dtype,
+                      int32_t G, int32_t maxg, int32_t PMB, const pa_decode_opts* opts, CascadePlan* out) {
+    CascadePlan c;
+    int st = make_plan(S, Hq, Hkv, D, bs, MB, kv_dtype, opts, &c.suffix);
+    if (st != PA_OK) return st;
+    if (G < 0 || maxg < 0 || PMB < 0) return PA_ERR_SHAPE;
+    if (G >= (int64_t(1) << 30) || (int64_t)PMB * bs >= (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
+    Plan& p = c.suffix;
+    // the suffix pass runs on the decode kernels (at most 16 query heads per KV head)
+    if (p.multi) return PA_ERR_UNSUPPORTED;
+    if (p.num_partitions >= 32768 || Hkv / p.heads_per_unit >= 65536) return PA_ERR_UNSUPPORTED;
+    p.scheduled = true;
+    p.partials = true;
+    size_t off = kHeaderBytes;
+    p.items_off = off;
+    off += align_up((size_t)p.num_workgroups * 4 * sizeof(int32_t), 256);
+    const size_t rows = (size_t)S * Hq;
+    p.ml_off = off;
+    p.o_off = off + align_up(rows * p.num_partitions * 2 * sizeof(float), 256);
+    off = align_up(p.o_off + rows * p.num_partitions * D * sizeof(float), 256);
+    p.workspace = off;
+    c.has_prefix = G > 0 && maxg > 0 && PMB > 0;
+    if (c.has_prefix) {
+        // The groups are few, so the prefix is split into short partitions
+        // (down to 64 tokens) until there are about two workgroups per
+        // compute unit; each partition adds one state per member row.
+        const int cus = current_cu_count();
+        if (cus <= 0) return PA_ERR_DEVICE;
+        Plan& q = c.prefix;
+        st = make_multi_plan(G, S, maxg, Hq, Hkv, D, bs, PMB, -1, &q);
+        if (st != PA_OK) return st;
+        const int64_t units = (int64_t)G * Hkv * q.row_blocks;
+        const int64_t cap = align_up((size_t)PMB * bs, pa::kTile);
+        int64_t P = cap;
+        while (P > 64 && units * ((cap + P - 1) / P) < 2 * cus) P = align_up((size_t)(P / 2), pa::kTile);
+        q.partition_tokens = (int)P;
+        q.num_partitions = (int)((cap + P - 1) / P);
+        q.num_workgroups = units * q.num_partitions;
+        if (q.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+        q.scheduled = false;
+        q.partials = true;
+        q.items_off = 0;
+        c.pre_ml_off = off;
+        c.pre_o_off = off + align_up(rows * q.num_partitions * 2 * sizeof(float), 256);
+        off = c.pre_o_off + rows * q.num_partitions * D * sizeof(float);
+        q.ml_off = c.pre_ml_off;
+        q.o_off = c.pre_o_off;
+        q.workspace = 0;
+    }
+    c.workspace = off;
+    *out = c;
+    return PA_OK;
+}
+
+int32_t last_block_id(int64_t num_blocks) {
+    return (int32_t)((num_blocks > INT32_MAX ? (int64_t)INT32_MAX + 1 : num_blocks) - 1);
+}
+
+// Arguments of the multi-row kernel for a plan made by make_multi_plan
+// (partials at the plan's workspace offsets when it splits).
+pa::MultiArgs multi_args(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                         float scale, void* out, int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t bs, int32_t MB, int64_t num_blocks, int32_t kv_dtype, float k_scale,
+                         float v_scale, void* workspace) {
     const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
     const int64_t esz = fp8 ? 1 : 2;
     pa::MultiArgs a{};
@@ -274,7 +351,7 @@ int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_c
     a.context_lens = context_lens;
     a.query_start = query_start;
     a.out = static_cast<uint16_t*>(out);
-    if (p.num_partitions > 1) {
+    if (p.partials) {
         char* ws = static_cast<char*>(workspace);
         a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
         a.part_o = reinterpret_cast<float*>(ws + p.o_off);
@@ -290,12 +367,24 @@ int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_c
     a.partition_tokens = p.partition_tokens;
     a.num_partitions = p.num_partitions;
     a.row_blocks = p.row_blocks;
-    a.last_block = (int32_t)((num_blocks > INT32_MAX ? (int64_t)INT32_MAX + 1 : num_blocks) - 1);
+    a.last_block = last_block_id(num_blocks);
     a.head_bytes = (uint32_t)(D * esz);
     a.slot_bytes = (uint32_t)((int64_t)Hkv * D * esz);
     a.block_bytes = (uint32_t)((int64_t)bs * Hkv * D * esz);
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
+    return a;
+}
+
+// Launch the multi-row kernel for a plan made by make_multi_plan.
+int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+              float scale, void* out, int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv,
+              int32_t D, int32_t bs, int32_t MB, int64_t num_blocks, int32_t kv_dtype, float k_scale,
+              float v_scale, void* workspace, void* stream) {
+    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
+    pa::MultiArgs a = multi_args(p, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out, S,
+                                 Tq, maxq, Hq, Hkv, D, bs, MB, num_blocks, kv_dtype, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.scheduled) {
         char* ws = static_cast<char*>(workspace);
@@ -314,6 +403,64 @@ int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_c
     }
     const hipError_t e = pa::launch_multi(a, D, fp8, p.waves, s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// Arguments of the decode kernels for a plan made by make_plan (partials
+// and work list at the plan's workspace offsets).
+pa::DecodeArgs decode_args(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                           int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB,
+                           int64_t num_blocks, int32_t kv_dtype, float k_scale, float v_scale, void* workspace) {
+    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
+    const int64_t esz = fp8 ? 1 : 2;
+    pa::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    char* ws = static_cast<char*>(workspace);
+    if (p.partials) {
+        a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
+        a.part_o = reinterpret_cast<float*>(ws + p.o_off);
+    }
+    if (p.scheduled) {
+        a.item_count = reinterpret_cast<int*>(ws);
+        a.items = reinterpret_cast<const int4*>(ws + p.items_off);
+    }
+    a.num_seqs = S;
+    a.num_q_heads = Hq;
+    a.num_kv_heads = Hkv;
+    a.group = Hq / Hkv;
+    a.units_per_seq = Hkv / p.heads_per_unit;
+    a.block_size_log2 = log2i(bs);
+    a.max_blocks_per_seq = MB;
+    a.partition_tokens = p.partition_tokens;
+    a.num_partitions = p.num_partitions;
+    a.last_block = last_block_id(num_blocks);
+    a.head_bytes = (uint32_t)(D * esz);
+    a.slot_bytes = (uint32_t)((int64_t)Hkv * D * esz);
+    a.block_bytes = (uint32_t)((int64_t)bs * Hkv * D * esz);
+    a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    return a;
+}
+
+// Arguments of the work-list builder for the decode kernels' items.
+pa::ScheduleArgs schedule_args(const Plan& p, const pa::DecodeArgs& a, const int32_t* context_lens,
+                               int32_t max_context) {
+    pa::ScheduleArgs sa{};
+    sa.context_lens = context_lens;
+    sa.items = const_cast<int4*>(a.items);
+    sa.item_count = const_cast<int*>(a.item_count);
+    sa.num_seqs = a.num_seqs;
+    sa.num_kv_heads = a.units_per_seq;  // items are (sequence, unit, partition)
+    sa.partition_tokens = p.partition_tokens;
+    sa.num_partitions = p.num_partitions;
+    sa.max_context = max_context;
+    sa.block_size_log2 = a.block_size_log2;
+    return sa;
 }
 
 }  // namespace
@@ -443,50 +590,13 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
         return run_multi(p, q, k_cache, v_cache, block_tables, context_lens, nullptr, scale, out, num_seqs,
                          num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                          num_blocks, kv_dtype, k_scale, v_scale, workspace, stream);
-    const int64_t esz = fp8 ? 1 : 2;
-    pa::DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.out = static_cast<uint16_t*>(out);
-    char* ws = static_cast<char*>(workspace);
-    if (p.num_partitions > 1) {
-        a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
-        a.part_o = reinterpret_cast<float*>(ws + p.o_off);
-    }
-    if (p.scheduled) {
-        a.item_count = reinterpret_cast<int*>(ws);
-        a.items = reinterpret_cast<const int4*>(ws + p.items_off);
-    }
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = num_q_heads / num_kv_heads;
-    a.units_per_seq = num_kv_heads / p.heads_per_unit;
-    a.block_size_log2 = log2i(block_size);
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.partition_tokens = p.partition_tokens;
-    a.num_partitions = p.num_partitions;
-    a.last_block = (int32_t)((num_blocks > INT32_MAX ? (int64_t)INT32_MAX + 1 : num_blocks) - 1);
-    a.head_bytes = (uint32_t)(head_dim * esz);
-    a.slot_bytes = (uint32_t)((int64_t)num_kv_heads * head_dim * esz);
-    a.block_bytes = (uint32_t)((int64_t)block_size * num_kv_heads * head_dim * esz);
-    a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
-    a.v_scale = fp8 ? v_scale : 1.0f;
+    pa::DecodeArgs a = decode_args(p, q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                   num_blocks, kv_dtype, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (p.scheduled) {
-        pa::ScheduleArgs sa{};
-        sa.context_lens = context_lens;
-        sa.items = reinterpret_cast<int4*>(ws + p.items_off);
-        sa.item_count = reinterpret_cast<int*>(ws);
-        sa.num_seqs = num_seqs;
-        sa.num_kv_heads = a.units_per_seq;  // items are (sequence, unit, partition)
-        sa.partition_tokens = p.partition_tokens;
-        sa.num_partitions = p.num_partitions;
-        sa.max_context = max_blocks_per_seq * block_size;
+        const pa::ScheduleArgs sa = schedule_args(p, a, context_lens, max_blocks_per_seq * block_size);
         e = pa::launch_schedule(sa, s);
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
@@ -510,6 +620,103 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
     return PA_OK;
+}
+
+size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                        int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
+                                        int32_t kv_dtype, const pa_decode_opts* opts) {
+    CascadePlan c;
+    if (make_cascade_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                          kv_dtype, num_groups, max_group_size, max_prefix_blocks, opts, &c) != PA_OK)
+        return 0;
+    return c.workspace;
+}
+
+int pa_decode_cascade(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, const int32_t* prefix_tables, const int32_t* prefix_lens,
+                      const int32_t* group_start, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                      int64_t num_blocks, int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
+                      int32_t kv_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                      const pa_decode_opts* opts, void* stream) {
+    CascadePlan c;
+    int st = make_cascade_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                               kv_dtype, num_groups, max_group_size, max_prefix_blocks, opts, &c);
+    if (st != PA_OK) return st;
+    if (num_blocks <= 0) return PA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
+    if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+        return PA_ERR_DTYPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+    if (c.has_prefix && (!prefix_tables || !prefix_lens || !group_start)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
+    const auto mis4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
+    if (mis4(block_tables) || mis4(context_lens) || mis4(prefix_tables) || mis4(prefix_lens) || mis4(group_start))
+        return PA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < c.workspace) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+    if (pa::debug_validate_enabled()) {
+        int vs = pa_check_decode_inputs(block_tables, context_lens, num_seqs, block_size, max_blocks_per_seq,
+                                        num_blocks, stream);
+        if (vs == PA_OK && c.has_prefix)
+            vs = pa_check_cascade_inputs(prefix_tables, prefix_lens, group_start, num_groups, max_group_size,
+                                         max_prefix_blocks, num_seqs, block_size, num_blocks, stream);
+        if (vs != PA_OK) return vs;
+    }
+    pa::CascadeGroups groups{};
+    if (c.has_prefix) {
+        groups.group_start = group_start;
+        groups.prefix_lens = prefix_lens;
+        groups.num_groups = num_groups;
+        groups.max_group_size = max_group_size;
+        groups.max_prefix_tokens = max_prefix_blocks * block_size;
+        groups.max_context = max_blocks_per_seq * block_size;
+    }
+    const Plan& p = c.suffix;
+    const pa::DecodeArgs a = decode_args(p, q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                         num_blocks, kv_dtype, k_scale, v_scale, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // 1. suffix work list
+    pa::ScheduleArgs sa = schedule_args(p, a, context_lens, max_blocks_per_seq * block_size);
+    sa.cascade = groups;
+    if (pa::launch_schedule(sa, s) != hipSuccess) return PA_ERR_LAUNCH;
+    // 2. prefix pass: each group's prefix once for all its members
+    pa::MultiArgs m{};
+    if (c.has_prefix) {
+        m = multi_args(c.prefix, q, k_cache, v_cache, prefix_tables, context_lens, nullptr, scale, out,
+                       num_groups, num_seqs, max_group_size, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_prefix_blocks, num_blocks, kv_dtype, k_scale, v_scale, workspace);
+        m.cascade = groups;
+        if (pa::launch_multi(m, head_dim, fp8, c.prefix.waves, s) != hipSuccess) return PA_ERR_LAUNCH;
+    }
+    // 3. suffix pass
+    const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit};
+    const hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, ls, s)
+                                                      : pa::launch_decode_valu(a, head_dim, fp8, ls, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+    // 4. merge both passes' states
+    pa::CascadeMergeArgs mg{};
+    mg.context_lens = context_lens;
+    mg.cascade = groups;
+    mg.pre_ml = m.part_ml;
+    mg.pre_o = m.part_o;
+    mg.part_ml = a.part_ml;
+    mg.part_o = a.part_o;
+    mg.out = a.out;
+    mg.num_seqs = num_seqs;
+    mg.num_q_heads = num_q_heads;
+    mg.head_dim = head_dim;
+    mg.prefix_partition_tokens = c.has_prefix ? c.prefix.partition_tokens : 1;
+    mg.prefix_partitions = c.has_prefix ? c.prefix.num_partitions : 0;
+    mg.partition_tokens = p.partition_tokens;
+    mg.num_partitions = p.num_partitions;
+    mg.max_context = max_blocks_per_seq * block_size;
+    mg.block_size_log2 = a.block_size_log2;
+    return pa::launch_cascade_merge(mg, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,

@@ -9,6 +9,17 @@ namespace pa {
 
 constexpr int kTile = 16;  // tokens per decode tile (one MFMA M/N extent)
 
+// Shared-prefix groups of a cascade call. Group k is the run of sequences
+// group_start[k] .. group_start[k+1] - 1 (at most max_group_size of them);
+// its members' first prefix_lens[k] tokens (whole blocks, at most
+// max_prefix_tokens) sit in the blocks of prefix table row k.
+struct CascadeGroups {
+    const int32_t* group_start;    // [num_groups + 1]; null = no groups
+    const int32_t* prefix_lens;    // [num_groups] tokens
+    int32_t num_groups, max_group_size, max_prefix_tokens;
+    int32_t max_context;           // members' table rows: max_blocks_per_seq * block_size
+};
+
 // Arguments of the decode kernels, passed by value.
 struct DecodeArgs {
     const uint16_t* q;             // [S, Hq, D] bf16
@@ -43,6 +54,10 @@ struct ScheduleArgs {
     int* item_count;
     int32_t num_seqs, num_kv_heads, partition_tokens, num_partitions;
     int32_t max_context;           // max_blocks_per_seq * block_size
+    // Cascade suffix pass: a sequence's items start after the tokens its
+    // prefix group covers and, when it has any, none stores the final output.
+    CascadeGroups cascade;
+    int32_t block_size_log2;
 };
 
 struct MergeArgs {
@@ -91,6 +106,29 @@ struct MultiArgs {
     // item b / row_blocks, row block b % row_blocks.
     const int4* items;
     const int* item_count;
+    // Cascade prefix pass (cascade.group_start non-null): the grid's
+    // "sequence" k is prefix group k, block_tables holds the prefix tables,
+    // the query rows are the members' (one token each, q row = sequence),
+    // member i attends the first cascade_shared() tokens, and every state is
+    // stored as a partial (stride num_partitions).
+    CascadeGroups cascade;
+};
+
+// Arguments of the cascade merge: per (sequence, query head) the states of
+// the prefix pass (prefix_partitions slots) and of the suffix pass
+// (num_partitions slots), combined by log-sum-exp.
+struct CascadeMergeArgs {
+    const int32_t* context_lens;
+    CascadeGroups cascade;
+    const float* pre_ml;           // [S, Hq, prefix_partitions, 2]
+    const float* pre_o;            // [S, Hq, prefix_partitions, D]
+    const float* part_ml;          // [S, Hq, num_partitions, 2]
+    const float* part_o;           // [S, Hq, num_partitions, D]
+    uint16_t* out;
+    int32_t num_seqs, num_q_heads, head_dim;
+    int32_t prefix_partition_tokens, prefix_partitions;
+    int32_t partition_tokens, num_partitions;
+    int32_t max_context, block_size_log2;
 };
 
 struct CopyBlocksArgs {
@@ -113,13 +151,14 @@ struct LaunchShape {
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s);
 hipError_t launch_schedule(const ScheduleArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 // streaming-read reference kernel (probe.hip)
 hipError_t launch_probe_read(const void* buf, int64_t bytes, bool nontemporal, uint32_t* sink, int cus,
                              hipStream_t s);
-// the multi-row kernel, then (split) its merge
+// the multi-row kernel, then (split, not a cascade prefix pass) its merge
 hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, hipStream_t s);
 
 // PA_DEBUG_VALIDATE set (and not "0"): the hot-path calls first run the

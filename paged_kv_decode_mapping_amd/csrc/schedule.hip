@@ -18,11 +18,16 @@
 // within a bucket land in an arbitrary order; the result does not depend on
 // which workgroup computes an item, so the outputs are still deterministic.
 //
+// In a cascade call's suffix pass a sequence's pairs start after the tokens
+// its prefix group covers (those are attended once for the whole group by
+// the prefix pass); a sequence with such tokens gets no pair when nothing
+// follows them, and its items never store the final output, which the
+// cascade merge forms from both passes' states.
+//
 // Context lengths are staged through LDS in chunks, so the loops below hold
 // no global loads: a load there would make every iteration wait for the
 // previous iteration's item stores (both count in the same vmcnt counter).
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_cascade.h"
 
 namespace pa {
 namespace {
@@ -36,18 +41,28 @@ __device__ __forceinline__ int pair_key(int len) {
     return kBuckets - 1 - min(tiles, kBuckets - 1);  // longer -> smaller key -> earlier
 }
 
-// Stage the clamped lengths of sequences [c0, c0 + n) into sctx.
-__device__ __forceinline__ void stage_lengths(const ScheduleArgs& a, int* sctx, int c0, int n) {
+// Stage the clamped lengths of sequences [c0, c0 + n) into sctx and the
+// token their pairs start at into sbeg (0 unless a cascade prefix covers it).
+__device__ __forceinline__ void stage_lengths(const ScheduleArgs& a, int* sctx, int* sbeg, int c0, int n) {
     for (int i = (int)threadIdx.x; i < n; i += kThreads) {
-        const int ctx = a.context_lens[c0 + i];
-        sctx[i] = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+        int ctx = a.context_lens[c0 + i];
+        ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+        sctx[i] = ctx;
+        sbeg[i] = cascade_shared(a.cascade, c0 + i, ctx, a.block_size_log2);
     }
+}
+
+// (sequence, partition) pairs of a sequence whose pairs cover [beg, ctx).
+__device__ __forceinline__ int pair_count(int beg, int ctx, int P) {
+    const int np = (ctx - beg + P - 1) / P;
+    return beg > 0 ? np : max(np, 1);
 }
 
 __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
     __shared__ int hist[kBuckets];
     __shared__ int wsum[kThreads / 64];
     __shared__ int sctx[kChunk];
+    __shared__ int sbeg[kChunk];
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -59,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
     //    lanes over its partitions
     for (int c0 = 0; c0 < a.num_seqs; c0 += kChunk) {
         const int n = min(kChunk, a.num_seqs - c0);
-        stage_lengths(a, sctx, c0, n);
+        stage_lengths(a, sctx, sbeg, c0, n);
         __syncthreads();
         for (int i = wave; i < n; i += nwaves) {
-            const int ctx = sctx[i];
-            const int np = max((ctx + P - 1) / P, 1);
-            for (int p = lane; p < np; p += 64) atomicAdd(&hist[pair_key(min(P, ctx - p * P))], 1);
+            const int ctx = sctx[i], beg = sbeg[i];
+            const int np = pair_count(beg, ctx, P);
+            for (int p = lane; p < np; p += 64) atomicAdd(&hist[pair_key(min(P, ctx - beg - p * P))], 1);
         }
         __syncthreads();
     }
@@ -91,19 +106,19 @@ __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
     for (int c0 = 0; c0 < a.num_seqs; c0 += kChunk) {
         const int n = min(kChunk, a.num_seqs - c0);
         __syncthreads();
-        stage_lengths(a, sctx, c0, n);
+        stage_lengths(a, sctx, sbeg, c0, n);
         __syncthreads();
         for (int i = wave; i < n; i += nwaves) {
-            const int ctx = sctx[i];
-            const int np = max((ctx + P - 1) / P, 1);
-            const int flags = (np <= 1 || a.num_partitions == 1) ? kItemFinal : 0;
+            const int ctx = sctx[i], beg = sbeg[i];
+            const int np = pair_count(beg, ctx, P);
+            const int flags = (beg == 0 && (np <= 1 || a.num_partitions == 1)) ? kItemFinal : 0;
             const int Hkv = a.num_kv_heads;
             for (int p0 = 0; p0 < np; p0 += 64) {
                 // one slot per pair (lane p0 + lane), then the pair's Hkv items
                 // spread over the lanes so that each store instruction writes
                 // consecutive items
                 const int p = p0 + lane;
-                const int len = p < np ? min(P, ctx - p * P) : 0;
+                const int len = p < np ? min(P, ctx - beg - p * P) : 0;
                 const int pos = p < np ? atomicAdd(&hist[pair_key(len)], 1) : 0;
                 const int nitems = min(64, np - p0) * Hkv;
                 for (int f0 = 0; f0 < nitems; f0 += 64) {  // uniform trip count: the shuffle sees all lanes
@@ -112,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
                     const int slot = __shfl(pos, pp < 64 ? pp : 0, 64);
                     if (f < nitems) {
                         const int h = f - pp * Hkv;
-                        const int tb = (p0 + pp) * P;
+                        const int tb = beg + (p0 + pp) * P;
                         a.items[(int64_t)slot * Hkv + h] =
                             make_int4(c0 + i, ((p0 + pp) << 16) | h, tb, min(tb + P, ctx) | flags);
                     }

@@ -16,7 +16,12 @@
 //                [0, num_blocks * block_size), and no slot appears twice;
 //   decode:      every context length is in [0, max_blocks_per_seq *
 //                block_size], and the table entries that cover it (the first
-//                ceil(ctx / block_size) of the row) name blocks inside the pool.
+//                ceil(ctx / block_size) of the row) name blocks inside the pool;
+//   cascade:     the group offsets rise from >= 0 to <= num_seqs, no group
+//                has more than max_group_size sequences, every prefix length
+//                is a whole number of blocks within its table row, and the
+//                entries that cover it name blocks inside the pool (Tutorial
+//                §4.3: a cached prefix is shared as whole blocks).
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -90,6 +95,35 @@ int pa_check_decode_inputs(const int32_t* block_tables, const int32_t* context_l
         const int64_t nb = (c + block_size - 1) / block_size;
         const int32_t* row = table.data() + (size_t)i * max_blocks_per_seq;
         for (int64_t b = 0; b < nb; ++b)
+            if (row[b] < 0 || row[b] >= num_blocks) return PA_ERR_PRECONDITION;
+    }
+    return PA_OK;
+}
+
+int pa_check_cascade_inputs(const int32_t* prefix_tables, const int32_t* prefix_lens, const int32_t* group_start,
+                            int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks, int32_t num_seqs,
+                            int32_t block_size, int64_t num_blocks, void* stream) {
+    if (num_groups < 0 || max_group_size < 0 || max_prefix_blocks < 0 || num_seqs < 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return PA_ERR_SHAPE;
+    if (num_groups == 0) return PA_OK;
+    if (!group_start || !prefix_lens || (max_prefix_blocks > 0 && !prefix_tables)) return PA_ERR_NULL;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> starts, lens, table;
+    int st = copy_to_host(starts, group_start, (int64_t)num_groups + 1, s);
+    if (st != PA_OK) return st;
+    st = copy_to_host(lens, prefix_lens, num_groups, s);
+    if (st != PA_OK) return st;
+    st = copy_to_host(table, prefix_tables, (int64_t)num_groups * max_prefix_blocks, s);
+    if (st != PA_OK) return st;
+    if (starts[0] < 0 || starts[(size_t)num_groups] > num_seqs) return PA_ERR_PRECONDITION;
+    for (int32_t k = 0; k < num_groups; ++k) {
+        const int64_t n = (int64_t)starts[(size_t)k + 1] - starts[(size_t)k];
+        if (n < 0 || n > max_group_size) return PA_ERR_PRECONDITION;
+        const int64_t pl = lens[(size_t)k];
+        if (pl < 0 || pl % block_size != 0 || pl > (int64_t)max_prefix_blocks * block_size) return PA_ERR_PRECONDITION;
+        const int32_t* row = table.data() + (size_t)k * max_prefix_blocks;
+        for (int64_t b = 0; b < pl / block_size; ++b)
             if (row[b] < 0 || row[b] >= num_blocks) return PA_ERR_PRECONDITION;
     }
     return PA_OK;

@@ -22,6 +22,7 @@ import json
 import os
 import sys
 from collections import defaultdict
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -29,10 +30,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # What decides the decode kernels' traffic: their sources, the headers they
 # include, and the argument blocks they receive. The launch plan (waves,
 # tiles in flight, partitions) is stored next to the figure and compared
-# separately, so host-side changes elsewhere do not invalidate it.
-DECODE_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "schedule.hip", "merge.hip", "pa_epilogue.h",
-                  "pa_device.h")
-DECODE_STRUCTS = ("DecodeArgs", "ScheduleArgs", "MergeArgs", "LaunchShape")
+# separately, so host-side changes elsewhere do not invalidate it. With a
+# plan, only the kernels it launches count: the work-list builder when it is
+# scheduled, the merge when it splits contexts.
+COMMON_SOURCES = ("pa_epilogue.h", "pa_device.h")
+KERNEL_SOURCES = {"mfma": "decode_mfma.hip", "valu": "decode_valu.hip"}
+COMMON_STRUCTS = ("DecodeArgs", "LaunchShape")
 
 
 def _struct_text(src: str, name: str) -> str:
@@ -40,14 +43,26 @@ def _struct_text(src: str, name: str) -> str:
     return src[i:src.index("};", i) + 2]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(plan: Optional[dict] = None) -> str:
+    """Hash of what the decode launches of `plan` run (every decode kernel,
+    the builder and the merge when no plan is given)."""
+    files = list(COMMON_SOURCES)
+    structs = list(COMMON_STRUCTS)
+    variants = [plan["variant"]] if plan else sorted(KERNEL_SOURCES)
+    files += [KERNEL_SOURCES[v] for v in variants]
+    if plan is None or plan.get("scheduled"):
+        files.append("schedule.hip")
+        structs.append("ScheduleArgs")
+    if plan is None or plan.get("num_partitions", 1) > 1:
+        files.append("merge.hip")
+        structs.append("MergeArgs")
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_decode_mapping_amd", "csrc")
-    for f in DECODE_SOURCES:
+    for f in files:
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     internal = open(os.path.join(csrc, "pa_internal.h")).read()
-    for name in DECODE_STRUCTS:
+    for name in structs:
         h.update(_struct_text(internal, name).encode())
     return h.hexdigest()[:16]
 
@@ -143,8 +158,9 @@ def cmd_traffic(a) -> None:
            "copy_kernel": _short(copy_name), "copy_bytes": a.copy_bytes,
            "fetch_counter_per_copy_byte": cf / a.copy_bytes, "write_counter_per_copy_byte": cw / a.copy_bytes,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
-           "dispatches": len(dfetch), "kernel_source_hash": kernel_source_hash(),
-           "plan": _plan_or_none(a.workload, a.kv), "command": a.cmd}
+           "dispatches": len(dfetch)}
+    plan = _plan_or_none(a.workload, a.kv)
+    res.update({"kernel_source_hash": kernel_source_hash(plan), "plan": plan, "command": a.cmd})
     json.dump(res, open(a.out, "w"), indent=1)
     print(json.dumps(res, indent=1))
 

@@ -127,6 +127,8 @@ class Workload:
     v_amax: float
     shared_seqs: np.ndarray       # int64 indices of prefix-sharing sequences
     unique_blocks: int            # physical blocks holding context data
+    prefix_ids: np.ndarray = dataclasses.field(  # int64 physical blocks of the shared prefix
+        default_factory=lambda: np.zeros(0, np.int64))
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -306,7 +308,8 @@ def make_workload(name_or_spec, *, seed: Optional[int] = None, num_seqs: Optiona
         spec=spec, context_lens=ctx.astype(np.int32), block_tables=tables.astype(np.int32),
         num_blocks=N, poison_block=poison_block, q=q, k_cache=k_cache, v_cache=v_cache,
         new_k=new_k, new_v=new_v, slot_mapping=slot_mapping.astype(np.int64),
-        k_amax=kmax, v_amax=vmax, shared_seqs=shared.astype(np.int64), unique_blocks=unique)
+        k_amax=kmax, v_amax=vmax, shared_seqs=shared.astype(np.int64), unique_blocks=unique,
+        prefix_ids=prefix_ids.astype(np.int64))
 
 
 def reduced(name: str, num_seqs: int, context: Sequence[int], **kw) -> Workload:
@@ -344,3 +347,136 @@ def make_multi_query(w: Workload, q_lens, *, seed: Optional[int] = None) -> Mult
     qs = np.zeros(s.num_seqs + 1, dtype=np.int64)
     qs[1:] = np.cumsum(q_lens)
     return MultiQuery(q=q, query_start=qs.astype(np.int32), q_lens=q_lens.astype(np.int32))
+
+
+@dataclasses.dataclass
+class CascadeBatch:
+    """A decode batch laid out for a cascade call: prefix group k is the run
+    of sequences group_start[k] .. group_start[k+1] - 1, whose first
+    prefix_lens[k] tokens are the cached prefix held in the blocks of
+    prefix_tables[k] (Tutorial §4.3, prefix caching: the cache keeps each
+    prefix's block list and length). Members' own table rows name the same
+    blocks for those tokens, as a prefix cache hands them out."""
+
+    q: np.ndarray                 # uint16 [S, Hq, D]
+    k_cache: np.ndarray           # uint16 [N, bs, Hkv, D]
+    v_cache: np.ndarray
+    block_tables: np.ndarray      # int32 [S, MB]
+    context_lens: np.ndarray      # int32 [S]
+    prefix_tables: np.ndarray     # int32 [G, PMB]
+    prefix_lens: np.ndarray       # int32 [G]
+    group_start: np.ndarray       # int32 [G + 1]
+    max_group_size: int
+    num_blocks: int
+    poison_block: int
+    block_size: int
+    scale: float
+    order: Optional[np.ndarray] = None  # batch position -> sequence of the source workload
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.prefix_lens.shape[0])
+
+
+def cascade_batch(w: Workload) -> CascadeBatch:
+    """The workload's batch reordered for a cascade call: the sequences that
+    share its prefix first, as one group, then the others in their order.
+    Arrays are permuted copies; `order` maps batch positions back."""
+    s = w.spec
+    shared = np.asarray(w.shared_seqs, dtype=np.int64)
+    rest = np.setdiff1d(np.arange(s.num_seqs), shared)
+    order = np.concatenate([shared, rest])
+    n = len(shared)
+    pb = len(w.prefix_ids)
+    return CascadeBatch(
+        q=np.ascontiguousarray(w.q[order]), k_cache=w.k_cache, v_cache=w.v_cache,
+        block_tables=np.ascontiguousarray(w.block_tables[order]),
+        context_lens=np.ascontiguousarray(w.context_lens[order]),
+        prefix_tables=np.asarray(w.prefix_ids, dtype=np.int32).reshape(1 if n else 0, pb if n else 1)
+        if n else np.zeros((0, 1), np.int32),
+        prefix_lens=np.array([s.shared_prefix_tokens] if n else [], dtype=np.int32),
+        group_start=np.array([0, n] if n else [0], dtype=np.int32),
+        max_group_size=max(n, 1), num_blocks=w.num_blocks, poison_block=w.poison_block,
+        block_size=s.block_size, scale=s.scale, order=order)
+
+
+def make_prefix_groups(*, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                       groups: Sequence[tuple], lead: Sequence[int] = (), tail: Sequence[int] = (),
+                       seed: int = 2024, pool_factor: float = 1.25) -> CascadeBatch:
+    """A batch of `lead` ungrouped sequences, then one run per entry
+    (prefix_tokens, [member context lengths]) of `groups`, then `tail`
+    ungrouped sequences (each list gives context lengths). prefix_tokens is
+    a whole number of blocks; a member may be shorter than its prefix.
+    Every member's table names its group's prefix blocks for the prefix
+    tokens it holds and its own blocks after them. Values are N(0,1) bf16;
+    free rows and the poison block padding every table row hold NaN."""
+    bs = block_size
+    Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    rng = np.random.default_rng(seed)
+    ctx = [int(c) for c in lead]
+    member_group: List[int] = [-1] * len(lead)
+    starts = [len(lead)]
+    for k, (ptok, members) in enumerate(groups):
+        if ptok % bs:
+            raise ValueError("prefix lengths are whole blocks")
+        ctx += [int(c) for c in members]
+        member_group += [k] * len(members)
+        starts.append(len(ctx))
+    ctx += [int(c) for c in tail]
+    member_group += [-1] * len(tail)
+    S = len(ctx)
+    ctx_a = np.asarray(ctx, dtype=np.int64)
+    nblk = (ctx_a + bs - 1) // bs
+    pblocks = [ptok // bs for ptok, _ in groups]
+    shared_blk = np.array([min(int(nblk[i]), pblocks[member_group[i]]) if member_group[i] >= 0 else 0
+                           for i in range(S)], dtype=np.int64)
+    own = nblk - shared_blk
+    used = int(own.sum()) + sum(pblocks)
+    N = max(int(math.ceil(pool_factor * used)), used + 1)
+    perm = rng.permutation(N).astype(np.int64)
+    cur = 0
+    prefix_ids = []
+    for pbk in pblocks:
+        prefix_ids.append(perm[cur:cur + pbk])
+        cur += pbk
+    own_ids = []
+    for i in range(S):
+        own_ids.append(perm[cur:cur + own[i]])
+        cur += int(own[i])
+    poison = int(perm[cur])
+    MB = max(1, int(nblk.max()) if S else 1)
+    PMB = max([1] + pblocks)
+    tables = np.full((S, MB), poison, dtype=np.int64)
+    for i in range(S):
+        sb = int(shared_blk[i])
+        if sb:
+            tables[i, :sb] = prefix_ids[member_group[i]][:sb]
+        tables[i, sb:nblk[i]] = own_ids[i]
+    ptables = np.full((len(groups), PMB), poison, dtype=np.int64)
+    for k, ids in enumerate(prefix_ids):
+        ptables[k, :len(ids)] = ids
+    k_cache = np.full((N, bs, Hkv, D), BF16_QNAN, dtype=np.uint16)
+    v_cache = np.full((N, bs, Hkv, D), BF16_QNAN, dtype=np.uint16)
+    q = _to_bf16_bits(rng.standard_normal((S, Hq, D), dtype=np.float32))
+    for ids in prefix_ids:
+        if len(ids):
+            k_cache[ids] = _to_bf16_bits(rng.standard_normal((len(ids), bs, Hkv, D), dtype=np.float32))
+            v_cache[ids] = _to_bf16_bits(rng.standard_normal((len(ids), bs, Hkv, D), dtype=np.float32))
+    for i in range(S):
+        ids = own_ids[i]
+        if len(ids) == 0:
+            continue
+        valid = int(ctx_a[i]) - int(shared_blk[i]) * bs
+        kb = _to_bf16_bits(rng.standard_normal((len(ids), bs, Hkv, D), dtype=np.float32))
+        vb = _to_bf16_bits(rng.standard_normal((len(ids), bs, Hkv, D), dtype=np.float32))
+        kb.reshape(-1, Hkv, D)[valid:] = BF16_QNAN
+        vb.reshape(-1, Hkv, D)[valid:] = BF16_QNAN
+        k_cache[ids] = kb
+        v_cache[ids] = vb
+    sizes = np.diff(np.asarray(starts))
+    return CascadeBatch(
+        q=q, k_cache=k_cache, v_cache=v_cache, block_tables=tables.astype(np.int32),
+        context_lens=ctx_a.astype(np.int32), prefix_tables=ptables.astype(np.int32).reshape(len(groups), PMB),
+        prefix_lens=np.array([ptok for ptok, _ in groups], dtype=np.int32),
+        group_start=np.asarray(starts, dtype=np.int32), max_group_size=int(max([1] + list(sizes))),
+        num_blocks=N, poison_block=poison, block_size=bs, scale=1.0 / math.sqrt(D))

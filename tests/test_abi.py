@@ -35,6 +35,15 @@ def test_every_declared_function_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defs = dict((n, int(v)) for n, v in re.findall(r"#define (PA_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", text))
+    assert len(defs) >= 14
+    for name, value in defs.items():
+        if name.startswith(("PA_OK", "PA_ERR_", "PA_KV_", "PA_VARIANT_")):
+            assert getattr(pa, name) == value, name
+
+
 def test_status_strings(lib):
     for code in range(0, -10, -1):
         s = pa.strerror(code)
@@ -205,6 +214,57 @@ def test_multi_workspace_size(lib):
     n = pa.pa_decode_multi_workspace_size(S, Tq, 4, Hq, Hkv, D, 16, 7, partition_tokens=32)
     P = -(-7 * 16 // 32)
     assert n == 256 + _align(S * Hkv * P * 16) + _align(Tq * Hq * P * 2 * 4) + Tq * Hq * P * D * 4
+
+
+def _cascade(lib, **kw):
+    args = dict(q=A, k=A, v=A, bt=A, cl=A, pt=None, pl=None, gs=None, scale=0.125, out=A, S=4, Hq=8, Hkv=2,
+                D=64, bs=16, MB=7, N=32, G=0, maxg=0, PMB=1, kvd=1, ks=1.0, vs=1.0, ws=A, wsb=1 << 20,
+                opts=pa._opts(partition_tokens=-1))
+    args.update(kw)
+    o = args["opts"]
+    return lib.pa_decode_cascade(args["q"], args["k"], args["v"], args["bt"], args["cl"], args["pt"], args["pl"],
+                                 args["gs"], args["scale"], args["out"], args["S"], args["Hq"], args["Hkv"],
+                                 args["D"], args["bs"], args["MB"], args["N"], args["G"], args["maxg"],
+                                 args["PMB"], args["kvd"], args["ks"], args["vs"], args["ws"], args["wsb"],
+                                 ctypes.byref(o) if o is not None else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=-1), -2), (dict(maxg=-1), -2), (dict(PMB=-1), -2), (dict(Hq=64, Hkv=2), -3), (dict(D=96), -3),
+    (dict(kvd=9), -5), (dict(N=0), -2), (dict(scale=float("nan")), -2), (dict(q=None), -1), (dict(cl=None), -1),
+    (dict(out=A + 8), -4), (dict(bt=A + 2), -4), (dict(ws=None), -6), (dict(wsb=256), -6), (dict(ws=A + 16), -4),
+    (dict(kvd=2, ks=-1.0), -5), (dict(PMB=1 << 27), -3), (dict(opts=pa._opts(partition_tokens=24)), -2),
+])
+def test_cascade_rejects_bad_arguments_without_launching(lib, kw, code):
+    """Checks that precede the device query (no groups, or sizes already
+    invalid); the group arrays' own checks run in the GPU tests."""
+    assert _cascade(lib, **kw) == code
+
+
+def test_cascade_zero_sequences_is_a_no_op(lib):
+    assert _cascade(lib, S=0, q=None, out=None, ws=None, wsb=0) == 0
+
+
+def test_cascade_workspace_without_groups(lib):
+    """No groups: header + the suffix pass's work list + its partial states,
+    which a cascade keeps even when contexts are not split."""
+    S, Hq, Hkv, D, MB = 4, 8, 2, 64, 7
+    n = pa.pa_decode_cascade_workspace_size(S, Hq, Hkv, D, 16, MB, 0, 0, 1, partition_tokens=-1)
+    P = 1
+    assert n == 256 + _align(S * Hkv * P * 16) + _align(S * Hq * P * 2 * 4) + _align(S * Hq * P * D * 4)
+    n2 = pa.pa_decode_cascade_workspace_size(S, Hq, Hkv, D, 16, MB, 0, 0, 1, partition_tokens=32)
+    P = -(-MB * 16 // 32)
+    assert n2 == 256 + _align(S * Hkv * P * 16) + _align(S * Hq * P * 2 * 4) + _align(S * Hq * P * D * 4)
+    assert pa.pa_decode_cascade_workspace_size(S, 64, 2, D, 16, MB, 0, 0, 1, partition_tokens=-1) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, None, None, 0, 0, 0, 4, 16, 32), 0), ((None, None, None, -1, 0, 0, 4, 16, 32), -2),
+    ((None, None, None, 1, 1, 1, 4, 16, 32), -1), ((A, A, A, 1, 1, 1, 4, 0, 32), -2),
+    ((A, A, A, 1, 1, 1, 4, 16, 0), -2),
+])
+def test_cascade_check_argument_errors(lib, args, code):
+    assert lib.pa_check_cascade_inputs(*args, None) == code
 
 
 def _copy(lib, **kw):

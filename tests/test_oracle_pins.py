@@ -335,6 +335,137 @@ def test_multi_row_equals_decode_of_the_truncated_context():
     assert np.array_equal(got1, ref1)
 
 
+# ---------------------------------------------------------------- cascade (shared prefix)
+
+def _dense_cascade(rng, Hq, Hkv, D, bs, groups, lead, tail, max_group_size):
+    """Dense K/V of each group's prefix and each sequence's own tokens, stored
+    in scattered pool blocks. Members' own rows name a NaN block wherever the
+    prefix lies; a member past max_group_size holds its whole context in its
+    own row. Returns the cascade arguments and, per sequence, the dense K/V
+    it must attend to (prefix[:shared] followed by its own tokens)."""
+    blocks = [np.full((bs, Hkv, D), 0x7FC0, np.uint16)]  # block 0: NaN
+    kblk, vblk = [blocks[0]], [blocks[0].copy()]
+
+    def store(k, v):
+        ids = []
+        for b0 in range(0, len(k), bs):
+            kb = np.full((bs, Hkv, D), 0x7FC0, np.uint16)
+            vb = kb.copy()
+            kb[:len(k[b0:b0 + bs])] = k[b0:b0 + bs]
+            vb[:len(v[b0:b0 + bs])] = v[b0:b0 + bs]
+            kblk.append(kb)
+            vblk.append(vb)
+            ids.append(len(kblk) - 1)
+        return ids
+
+    ctx, grp = list(lead), [-1] * len(lead)
+    starts = [len(lead)]
+    prefixes, ptables = [], []
+    for k, (ptok, members) in enumerate(groups):
+        pk = _bits(rng.standard_normal((ptok, Hkv, D)))
+        pv = _bits(rng.standard_normal((ptok, Hkv, D)))
+        prefixes.append((pk, pv))
+        ptables.append(store(pk, pv))
+        ctx += members
+        grp += [k if j < max_group_size else -1 for j in range(len(members))]
+        starts.append(len(ctx))
+    ctx += list(tail)
+    grp += [-1] * len(tail)
+    S = len(ctx)
+    q = _bits(rng.standard_normal((S, Hq, D)))
+    rows, dense = [], []
+    for i in range(S):
+        shared = min(ctx[i], groups[grp[i]][0]) if grp[i] >= 0 else 0
+        own_k = _bits(rng.standard_normal((ctx[i] - shared, Hkv, D)))
+        own_v = _bits(rng.standard_normal((ctx[i] - shared, Hkv, D)))
+        row = [0] * ((shared + bs - 1) // bs) + store(own_k, own_v)
+        rows.append(row)
+        if grp[i] >= 0:
+            pk, pv = prefixes[grp[i]]
+            dense.append((np.concatenate([pk[:shared], own_k]), np.concatenate([pv[:shared], own_v])))
+        else:
+            dense.append((own_k, own_v))
+    N = len(kblk)
+    pi = np.concatenate([[0], 1 + rng.permutation(N - 1)])  # scatter every block but the NaN one
+    kc = np.empty((N, bs, Hkv, D), np.uint16)
+    vc = np.empty_like(kc)
+    kc[pi] = np.stack(kblk)
+    vc[pi] = np.stack(vblk)
+    MB = max(1, max(len(r) for r in rows))
+    tables = np.zeros((S, MB), np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = pi[r]
+    PMB = max([1] + [len(t) for t in ptables])
+    pt = np.zeros((len(groups), PMB), np.int32)
+    for k, t in enumerate(ptables):
+        pt[k, :len(t)] = pi[t]
+    return (q, kc, vc, tables, np.asarray(ctx, np.int32), pt,
+            np.array([g[0] for g in groups], np.int32), np.asarray(starts, np.int32), dense)
+
+
+def test_cascade_matches_torch_sdpa_on_dense_prefix_and_suffix():
+    """Pin: torch scaled_dot_product_attention (float64, enable_gqa) over
+    prefix[:shared_i] followed by sequence i's own tokens, built as dense
+    arrays. The members' own rows hold a NaN block where the prefix lies, so
+    only a gather through the prefix table gives this. Covers a member
+    shorter than its prefix, empty contexts, a zero-length prefix, an empty
+    group, sequences in no group before and after the groups, and a member
+    past max_group_size (it reads its whole context through its own row)."""
+    rng = np.random.default_rng(97)
+    Hq, Hkv, D, bs = 8, 2, 32, 8
+    groups = [(24, [24, 40, 10, 30]), (0, [7]), (16, []), (40, [41, 80, 0])]
+    q, kc, vc, tables, ctx, pt, pl, gs, dense = _dense_cascade(rng, Hq, Hkv, D, bs, groups, [9], [0, 33], 3)
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.cascade_decode(q, kc, vc, tables, ctx, pt, pl, gs, scale, max_group_size=3)
+    for i, (k, v) in enumerate(dense):
+        if len(k) == 0:
+            assert np.all(got[i] == 0.0)
+            continue
+        qt = torch.from_numpy(bf16_f32(q[i]).astype(np.float64))[None, :, None, :]
+        kt = torch.from_numpy(bf16_f32(k).astype(np.float64)).permute(1, 0, 2)[None]
+        vt = torch.from_numpy(bf16_f32(v).astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale, enable_gqa=True)
+        np.testing.assert_allclose(got[i], ref[0, :, 0, :].numpy(), rtol=0, atol=1e-12)
+    # the members' own rows alone give NaN where they rely on the prefix
+    plain = oracle.decode(q, kc, vc, tables, ctx, scale)
+    assert np.isnan(plain[2]).all() and np.isfinite(got).all()
+
+
+def test_cascade_equals_decode_when_members_name_the_prefix_blocks():
+    """Pin (invariant, against the decode oracle): when every member's table
+    names its group's prefix blocks, as a prefix cache hands them out, the
+    cascade result is bit-identical to the decode of the same batch; with
+    those entries of the members' rows replaced by a NaN block, the cascade
+    result does not change while the plain decode turns NaN."""
+    b = W.make_prefix_groups(num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                             groups=[(64, [64, 100, 30, 200]), (160, [500, 160, 1]), (32, []), (0, [50, 0])],
+                             lead=[5], tail=[0, 17, 300], seed=5)
+    args = (b.prefix_tables, b.prefix_lens, b.group_start, b.scale)
+    ref = oracle.decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
+    got = oracle.cascade_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, *args)
+    assert np.array_equal(got, ref)
+    poisoned = b.block_tables.copy()
+    for k in range(b.num_groups):
+        nb = int(b.prefix_lens[k]) // b.block_size
+        poisoned[b.group_start[k]:b.group_start[k + 1], :nb] = b.poison_block
+    got2 = oracle.cascade_decode(b.q, b.k_cache, b.v_cache, poisoned, b.context_lens, *args)
+    assert np.array_equal(got2, ref)
+    bad = oracle.decode(b.q, b.k_cache, b.v_cache, poisoned, b.context_lens, b.scale)
+    assert np.isnan(bad[1:8]).any(axis=(1, 2)).all()  # members of groups 0 and 1
+
+
+def test_cascade_tables_reject_malformed_groups():
+    b = W.make_prefix_groups(num_q_heads=4, num_kv_heads=2, head_dim=16, block_size=16,
+                             groups=[(32, [40, 50])], seed=1)
+    base = (b.block_tables, b.context_lens)
+    with pytest.raises(AssertionError):
+        oracle.cascade_tables(*base, b.prefix_tables, np.array([20], np.int32), b.group_start, 16)
+    with pytest.raises(AssertionError):
+        oracle.cascade_tables(*base, b.prefix_tables, b.prefix_lens, np.array([2, 0], np.int32), 16)
+    with pytest.raises(AssertionError):
+        oracle.cascade_tables(*base, b.prefix_tables, np.array([48], np.int32), b.group_start, 16)
+
+
 def test_multi_rejects_more_queries_than_context():
     w = W.make_workload("tiny")
     qs = np.array([0, 2, 2, 2, 2], np.int32)  # sequence 0 has one cached token

@@ -49,3 +49,15 @@ def test_traffic_scaling(tmp_path):
     assert r["write_bytes_per_launch"] == 12.0 * 1024
     assert r["kernel_source_hash"] == profiling.kernel_source_hash()
     assert r["plan"] is None  # unknown workload: no plan, so bench.py never reports this figure
+
+
+def test_source_hash_follows_the_plan():
+    """A plan's hash covers the kernels it launches: the work-list builder
+    only when scheduled, the merge only when split, one decode kernel."""
+    base = {"variant": "mfma", "scheduled": False, "num_partitions": 1}
+    h = profiling.kernel_source_hash(base)
+    assert h == profiling.kernel_source_hash(dict(base))
+    assert h != profiling.kernel_source_hash(dict(base, variant="valu"))
+    assert h != profiling.kernel_source_hash(dict(base, scheduled=True))
+    assert h != profiling.kernel_source_hash(dict(base, num_partitions=2))
+    assert profiling.kernel_source_hash() not in (h, profiling.kernel_source_hash(dict(base, scheduled=True)))
