@@ -314,6 +314,10 @@ def bench_cascade(args, w, k_cache, v_cache, kv_b: int, k_scale: float, v_scale:
                      workspace=ws_d, partition_tokens=args.partition)
 
     stream = torch.cuda.current_stream()
+    # In serving, every other layer's KV passes through the caches between two
+    # steps of one layer: a scratch write before each timed call (outside its
+    # events) evicts the 256 MB Infinity Cache, so no call starts warm.
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -321,16 +325,16 @@ def bench_cascade(args, w, k_cache, v_cache, kv_b: int, k_scale: float, v_scale:
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-        t0 = time.perf_counter()
         for i in range(args.steps):
+            scratch.add_(1)
             ev[i][0].record(stream)
             fn()
             ev[i][1].record(stream)
         torch.cuda.synchronize()
-        return np.array([a.elapsed_time(e) for a, e in ev]), time.perf_counter() - t0
+        return np.array([a.elapsed_time(e) for a, e in ev])
 
-    cas_ms, wall = timed(cascade)
-    dec_ms, _ = timed(plain)
+    cas_ms = timed(cascade)
+    dec_ms = timed(plain)
     cl = b.context_lens.astype(np.int64)
     n_sh = int(b.group_start[1])
     shared = np.zeros_like(cl)
@@ -370,8 +374,9 @@ def bench_cascade(args, w, k_cache, v_cache, kv_b: int, k_scale: float, v_scale:
     achieved = unique / (avg * 1e-3) / 1e9
     res = {
         "metric": "shared-prefix (cascade) decode: logical GB/s (bytes a plain decode reads for the same outputs)",
-        "value": round(logical * args.steps / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "value": round(logical / (avg * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(avg, 5),
+        "timing": "HIP events around each call, caches evicted before each (512 MiB scratch write)",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.kv, "data": "synthetic",
         "config": {"workload": f"{s.name} reordered, {n_sh} sequences sharing a {int(b.prefix_lens[0])}-token "
                                f"prefix as one group", "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads,
@@ -379,6 +384,7 @@ def bench_cascade(args, w, k_cache, v_cache, kv_b: int, k_scale: float, v_scale:
         "cascade_us": {"avg": round(avg * 1e3, 2), "p10": round(float(np.percentile(cas_ms, 10)) * 1e3, 2),
                        "p90": round(float(np.percentile(cas_ms, 90)) * 1e3, 2)},
         "pa_decode_us": round(avg_d * 1e3, 2),
+        "speedup_vs_pa_decode": round(avg_d / avg, 3),
         "bytes": {"logical": logical, "unique": unique},
         "decode_tokens_per_s_kernel": round(s.num_seqs / (avg * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -142,6 +142,8 @@ def decode_units(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     MB = tables.shape[1]
     units = np.ascontiguousarray(np.asarray(units, dtype=np.int64))
+    if len(units) and (units.min() < 0 or units.max() >= S * Hkv):
+        raise ValueError("unit outside [0, num_seqs * num_kv_heads)")
     out = np.zeros((len(units), g, D), dtype=np.float64)
     kc = np.ascontiguousarray(k_cache)
     vc = np.ascontiguousarray(v_cache)

@@ -61,7 +61,8 @@ class WorkloadSpec:
     # ("fixed", num_blocks) | ("factor", f): pool = ceil(f * blocks in use)
     pool: tuple = ("factor", 1.25)
     k_mult: float = 1.0
-    shared_prefix_tokens: int = 0  # shared by half of the sequences
+    shared_prefix_tokens: int = 0  # shared by shared_fraction of the sequences
+    shared_fraction: float = 0.5
     seed: int = 1000
     partition_tokens: int = 0  # split-K partition the workload names (0 = none)
     description: str = ""
@@ -106,6 +107,15 @@ SPECS: Dict[str, WorkloadSpec] = {
                     "32/8 heads, D 128, bs 16, half share a 512-token prefix"),
 }
 ORDER: List[str] = ["tiny", "llama7b_mha", "llama70b_gqa", "long_splitk", "mixed_batch"]
+
+# A batch for the shared-prefix (cascade) decode beyond the five above: every
+# request starts with the same long system prompt (Tutorial §4.3 names the
+# shared system prompt as prefix caching's case), on the 70B layer shape.
+SPECS["system_prompt"] = WorkloadSpec(
+    name="system_prompt", num_seqs=128, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+    context=("uniform", 4096 + 16, 4096 + 512), shared_prefix_tokens=4096, shared_fraction=1.0, seed=1005,
+    description="128 seqs, 64/8 heads, D 128, bs 16, all share a 4096-token system prompt, "
+                "own tokens U[16,512] after it")
 
 
 @dataclasses.dataclass
@@ -208,7 +218,8 @@ def make_workload(name_or_spec, *, seed: Optional[int] = None, num_seqs: Optiona
     prefix_blocks = spec.shared_prefix_tokens // bs
     if spec.shared_prefix_tokens % bs:
         raise ValueError("shared prefix must be a whole number of blocks")
-    shared = np.sort(rng.choice(S, S // 2, replace=False)) if prefix_blocks else np.zeros(0, np.int64)
+    n_shared = int(S * spec.shared_fraction)
+    shared = np.sort(rng.choice(S, n_shared, replace=False)) if prefix_blocks else np.zeros(0, np.int64)
     is_shared = np.zeros(S, dtype=bool)
     is_shared[shared] = True
     own = np.where(is_shared, np.maximum(nblk - prefix_blocks, 0), nblk)

@@ -157,21 +157,23 @@ def test_cascade_equals_decode_on_the_mixed_batch(lib):
         compare(plain, ref, *BF16_TOL)
 
 
-def test_cascade_full_size_mixed_batch_sampled(lib):
-    """The full mixed batch (256 sequences, 128 sharing the 512-token prefix),
-    in the launch configuration the benchmark times: sampled (sequence, KV
+@pytest.mark.parametrize("name", ["mixed_batch", "system_prompt"])
+def test_cascade_full_size_sampled(lib, name):
+    """Full size, in the launch configuration the benchmark times: the mixed
+    batch (256 sequences, 128 sharing a 512-token prefix) and the system
+    prompt batch (128 sequences sharing 4096 tokens); sampled (sequence, KV
     head) units against the oracle, every element against pa_decode."""
-    w = W.make_workload("mixed_batch")
+    w = W.make_workload(name)
     b = W.cascade_batch(w)
     d = DeviceCascade(b)
-    note("cascade full-size mixed_batch")
+    note(f"cascade full-size {name}")
     got = host_bits(d.cascade())
     plain = host_bits(pa.pa_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale))
     Hkv, g = w.spec.num_kv_heads, w.spec.group
     n_shared = int(b.group_start[1])
     ctx = b.context_lens
     rng = np.random.default_rng(21)
-    pick = [0, n_shared - 1, n_shared, int(np.argmax(ctx)), int(np.argmin(ctx[:n_shared])),
+    pick = [0, n_shared - 1, min(n_shared, len(ctx) - 1), int(np.argmax(ctx)), int(np.argmin(ctx[:n_shared])),
             int(np.argmax(ctx[:n_shared]))]
     seqs = np.unique(np.concatenate([pick, rng.choice(len(ctx), 10, replace=False)]))
     units = np.concatenate([seqs * Hkv + rng.integers(0, Hkv, len(seqs)), seqs[:4] * Hkv + Hkv - 1])
