@@ -24,9 +24,13 @@
 // follows them, and its items never store the final output, which the
 // cascade merge forms from both passes' states.
 //
-// Context lengths are staged through LDS in chunks, so the loops below hold
-// no global loads: a load there would make every iteration wait for the
-// previous iteration's item stores (both count in the same vmcnt counter).
+// Parallel over (sequence, partition) pairs, not over sequences: the
+// lengths of a chunk of sequences are staged in LDS with one thread per four
+// sequences, a block-wide scan numbers their pairs, and then one thread per
+// pair counts and places it (a binary search over the scanned offsets finds
+// its sequence). A loop with one sequence per wave and iteration, the
+// simpler form, cost about 1 µs per iteration on MI355X (19 µs for 256
+// sequences); here a batch of up to 1024 pairs takes one pass.
 #include "pa_cascade.h"
 
 namespace pa {
@@ -34,22 +38,12 @@ namespace {
 
 constexpr int kBuckets = 1024;
 constexpr int kThreads = 1024;
-constexpr int kChunk = 4096;  // sequences staged in LDS at a time
+constexpr int kPerThread = 4;
+constexpr int kChunk = kThreads * kPerThread;  // sequences staged in LDS at a time
 
 __device__ __forceinline__ int pair_key(int len) {
     const int tiles = (len + kTile - 1) / kTile;
     return kBuckets - 1 - min(tiles, kBuckets - 1);  // longer -> smaller key -> earlier
-}
-
-// Stage the clamped lengths of sequences [c0, c0 + n) into sctx and the
-// token their pairs start at into sbeg (0 unless a cascade prefix covers it).
-__device__ __forceinline__ void stage_lengths(const ScheduleArgs& a, int* sctx, int* sbeg, int c0, int n) {
-    for (int i = (int)threadIdx.x; i < n; i += kThreads) {
-        int ctx = a.context_lens[c0 + i];
-        ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
-        sctx[i] = ctx;
-        sbeg[i] = cascade_shared(a.cascade, c0 + i, ctx, a.block_size_log2);
-    }
 }
 
 // (sequence, partition) pairs of a sequence whose pairs cover [beg, ctx).
@@ -58,31 +52,94 @@ __device__ __forceinline__ int pair_count(int beg, int ctx, int P) {
     return beg > 0 ? np : max(np, 1);
 }
 
+struct Chunk {
+    int* ctx;   // [kChunk] clamped context lengths
+    int* beg;   // [kChunk] first token of the sequence's pairs
+    int* off;   // [kChunk] first pair of each sequence (exclusive scan of the pair counts)
+    int* wsum;  // [kThreads / 64] scratch of the scan
+    int* total; // pairs of the chunk
+};
+
+// Stage sequences [c0, c0 + n) (thread t: sequences 4t .. 4t + 3 of the
+// chunk) and number their pairs. Ends with a barrier.
+__device__ __forceinline__ void stage_chunk(const ScheduleArgs& a, const Chunk& ch, int c0, int n) {
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int cnt[kPerThread];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = tid * kPerThread + k;
+        cnt[k] = 0;
+        if (j < n) {
+            int ctx = a.context_lens[c0 + j];
+            ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+            const int beg = cascade_shared(a.cascade, c0 + j, ctx, a.block_size_log2);
+            ch.ctx[j] = ctx;
+            ch.beg[j] = beg;
+            cnt[k] = pair_count(beg, ctx, a.partition_tokens);
+        }
+        local += cnt[k];
+    }
+    int x = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) ch.wsum[wave] = x;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += ch.wsum[w];
+    int run = base + x - local;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = tid * kPerThread + k;
+        if (j < n) ch.off[j] = run;
+        run += cnt[k];
+    }
+    if (tid == kThreads - 1) *ch.total = base + x;
+    __syncthreads();
+}
+
+// Sequence (within the chunk) of pair f: the last j with off[j] <= f.
+__device__ __forceinline__ int pair_seq(const int* off, int n, int f) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= f) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
     __shared__ int hist[kBuckets];
     __shared__ int wsum[kThreads / 64];
-    __shared__ int sctx[kChunk];
-    __shared__ int sbeg[kChunk];
+    __shared__ int sctx[kChunk], sbeg[kChunk], soff[kChunk];
+    __shared__ int stotal;
+    const Chunk ch{sctx, sbeg, soff, wsum, &stotal};
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nwaves = kThreads / 64;
     const int P = a.partition_tokens;
-    for (int b = tid; b < kBuckets; b += kThreads) hist[b] = 0;
+    const int Hkv = a.num_kv_heads;
+    const int nchunks = (a.num_seqs + kChunk - 1) / kChunk;
+    static_assert(kBuckets == kThreads, "one bucket per thread");
+    hist[tid] = 0;
 
-    // 1. histogram of (sequence, partition) pairs; one wave per sequence,
-    //    lanes over its partitions
-    for (int c0 = 0; c0 < a.num_seqs; c0 += kChunk) {
-        const int n = min(kChunk, a.num_seqs - c0);
-        stage_lengths(a, sctx, sbeg, c0, n);
-        __syncthreads();
-        for (int i = wave; i < n; i += nwaves) {
-            const int ctx = sctx[i], beg = sbeg[i];
-            const int np = pair_count(beg, ctx, P);
-            for (int p = lane; p < np; p += 64) atomicAdd(&hist[pair_key(min(P, ctx - beg - p * P))], 1);
+    // 1. histogram of (sequence, partition) pairs, one thread per pair
+    for (int c = 0; c < nchunks; ++c) {
+        const int c0 = c * kChunk, n = min(kChunk, a.num_seqs - c0);
+        __syncthreads();  // the previous chunk's readers are done (and hist is zeroed)
+        stage_chunk(a, ch, c0, n);
+        const int pairs = stotal;
+        for (int f = tid; f < pairs; f += kThreads) {
+            const int j = pair_seq(soff, n, f);
+            const int p = f - soff[j];
+            atomicAdd(&hist[pair_key(min(P, sctx[j] - sbeg[j] - p * P))], 1);
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // 2. exclusive prefix sum over the buckets (one bucket per thread)
     const int mine = hist[tid];
@@ -98,41 +155,25 @@ __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
     for (int w = 0; w < wave; ++w) base += wsum[w];
     __syncthreads();
     hist[tid] = base + x - mine;  // now: next free slot of the bucket
-    if (tid == kThreads - 1) {
-        *a.item_count = (base + x) * a.num_kv_heads;
-    }
+    if (tid == kThreads - 1) *a.item_count = (base + x) * Hkv;
 
-    // 3. scatter, expanded over KV heads
-    for (int c0 = 0; c0 < a.num_seqs; c0 += kChunk) {
-        const int n = min(kChunk, a.num_seqs - c0);
-        __syncthreads();
-        stage_lengths(a, sctx, sbeg, c0, n);
-        __syncthreads();
-        for (int i = wave; i < n; i += nwaves) {
-            const int ctx = sctx[i], beg = sbeg[i];
+    // 3. place each pair at its bucket's next slot, expanded over the KV heads
+    for (int c = 0; c < nchunks; ++c) {
+        const int c0 = c * kChunk, n = min(kChunk, a.num_seqs - c0);
+        __syncthreads();  // bucket offsets published; the previous chunk's readers are done
+        if (nchunks > 1) stage_chunk(a, ch, c0, n);  // a single chunk is still staged
+        const int pairs = stotal;
+        for (int f = tid; f < pairs; f += kThreads) {
+            const int j = pair_seq(soff, n, f);
+            const int p = f - soff[j];
+            const int ctx = sctx[j], beg = sbeg[j];
+            const int pos = atomicAdd(&hist[pair_key(min(P, ctx - beg - p * P))], 1);
             const int np = pair_count(beg, ctx, P);
             const int flags = (beg == 0 && (np <= 1 || a.num_partitions == 1)) ? kItemFinal : 0;
-            const int Hkv = a.num_kv_heads;
-            for (int p0 = 0; p0 < np; p0 += 64) {
-                // one slot per pair (lane p0 + lane), then the pair's Hkv items
-                // spread over the lanes so that each store instruction writes
-                // consecutive items
-                const int p = p0 + lane;
-                const int len = p < np ? min(P, ctx - beg - p * P) : 0;
-                const int pos = p < np ? atomicAdd(&hist[pair_key(len)], 1) : 0;
-                const int nitems = min(64, np - p0) * Hkv;
-                for (int f0 = 0; f0 < nitems; f0 += 64) {  // uniform trip count: the shuffle sees all lanes
-                    const int f = f0 + lane;
-                    const int pp = f / Hkv;  // pair within this group of 64
-                    const int slot = __shfl(pos, pp < 64 ? pp : 0, 64);
-                    if (f < nitems) {
-                        const int h = f - pp * Hkv;
-                        const int tb = beg + (p0 + pp) * P;
-                        a.items[(int64_t)slot * Hkv + h] =
-                            make_int4(c0 + i, ((p0 + pp) << 16) | h, tb, min(tb + P, ctx) | flags);
-                    }
-                }
-            }
+            const int tb = beg + p * P;
+            const int4 rec = make_int4(c0 + j, p << 16, tb, min(tb + P, ctx) | flags);
+            int4* dst = a.items + (int64_t)pos * Hkv;
+            for (int h = 0; h < Hkv; ++h) dst[h] = make_int4(rec.x, rec.y | h, rec.z, rec.w);
         }
     }
 }
