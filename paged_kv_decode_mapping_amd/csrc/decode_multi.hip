@@ -163,32 +163,60 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     const int c = lane & 15;
     const int gq = lane >> 4;
 
-    // ---- query rows of this block -> LDS (zero rows past the block's rows)
-    for (int i = (int)threadIdx.x; i < 16 * W * (D / 8); i += 64 * W) {
+    const int span = t_end - t_begin;
+    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
+    // Block-table entries of the item, 64 at a time in one register (lane
+    // l holds entry w_base + l), read with readlane; the next 64 are loaded
+    // as soon as a window is entered, so the tile loop never waits on a
+    // table load. (Fetching one entry per tile a tile ahead, as the decode
+    // kernels do, made every iteration here wait for a load issued one
+    // iteration earlier: all waves of a workgroup step through the tiles
+    // together, so nothing hid that wait.) They go out before the query rows.
+    const auto tab_rsrc = make_rsrc(a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq,
+                                    (uint32_t)a.max_blocks_per_seq * 4u);
+    const int e_last = (t_begin + max(ntiles - 1, 0) * kTile) >> a.block_size_log2;
+    auto table_load = [&](int base) {
+        return __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, (uint32_t)min(base + lane, e_last) << 2, 0, 0);
+    };
+    int w_base = t_begin >> a.block_size_log2;
+    uint32_t w_cur = 0u, w_next = 0u;
+    if (ntiles > 0) {
+        w_cur = table_load(w_base);
+        w_next = table_load(w_base + 64);
+    }
+
+    // ---- query rows of this block -> LDS (zero rows past the block's rows):
+    // every load first, then the stores
+    constexpr int QPT = (16 * W * (D / 8)) / (64 * W);  // 16-byte chunks per thread
+    u32x4 qv[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int i = (int)threadIdx.x + 64 * W * k;
         const int rr = i / (D / 8);
         const int d8 = i - rr * (D / 8);
         const int rho = row0 + rr;
-        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        qv[k] = u32x4{0u, 0u, 0u, 0u};
         if (rho < rows) {
             const int r = rho / g, hh = rho - (rho / g) * g;
-            w = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh) * D + 8 * d8);
+            qv[k] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh) * D + 8 * d8);
         }
-        *reinterpret_cast<u32x4*>(qs + rr * RS + 8 * d8) = w;
     }
 
     // this lane's row (column c of the wave's tile) and its causal limit
     const int my_rho = row0 + wave * 16 + c;
-    bool my_valid = my_rho < rows;
+    const bool my_valid = my_rho < rows;
     int my_pos = my_valid ? it.L - it.n + my_rho / g : -1;  // sees tokens <= my_pos
     if (prefix_pass && my_valid) {
-        // a member attends min(its context, the prefix) tokens here; a row
-        // that the group lookup does not place in this group (malformed
-        // offsets) stores nothing, so no two groups write one row's state
-        const int seq = it.q0 + my_rho / g;
-        int ctx = a.context_lens[seq];
+        // a member attends min(its context, the prefix) tokens here
+        int ctx = a.context_lens[it.q0 + my_rho / g];
         ctx = ctx < 0 ? 0 : (ctx > a.cascade.max_context ? a.cascade.max_context : ctx);
-        my_valid = cascade_group(a.cascade, seq) == it.seq;
-        my_pos = my_valid ? min(ctx, it.L) - 1 : -1;
+        my_pos = min(ctx, it.L) - 1;
+    }
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int i = (int)threadIdx.x + 64 * W * k;
+        const int rr = i / (D / 8);
+        *reinterpret_cast<u32x4*>(qs + rr * RS + 8 * (i - rr * (D / 8))) = qv[k];
     }
     const uint16_t* q_row = qs + (wave * 16 + c) * RS + 8 * gq;
 
@@ -197,8 +225,6 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
 #pragma unroll
     for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int span = t_end - t_begin;
-    const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
     const uint32_t head_off = (uint32_t)it.kvh * a.head_bytes;
     const int bs_mask = (1 << a.block_size_log2) - 1;
     const float qk = a.qk_scale_log2;
@@ -218,10 +244,32 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     u32x4 kb[NB][NI], vb[NB][NI];
 
     __syncthreads();  // query rows in LDS
+    // With 4 or 8 waves (many rows: the kernel is LDS-bound), this wave's
+    // query fragments, the B operand of every q.K^T MFMA, stay in registers
+    // instead of being read from LDS for every tile; with 1 or 2 waves (few
+    // rows, memory-bound) the 16 registers would cost occupancy.
+    constexpr bool kQInRegs = W >= 4;
+    bf16x8 qf[NQK];
+    if constexpr (kQInRegs) {
+#pragma unroll
+        for (int j = 0; j < NQK; ++j) qf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+    }
 
     if (ntiles > 0) {
-        const TableReader tab = make_table_reader(a.block_tables, a.max_blocks_per_seq, a.block_size_log2,
-                                                  a.last_block, it.seq, t_begin, ntiles - 1);
+        // physical block of tile t (tiles past the last take the last one's),
+        // clamped into the pool; t grows by at most one between calls
+        auto block_of = [&](int t) -> int64_t {
+            const int e = (t_begin + min(t, ntiles - 1) * kTile) >> a.block_size_log2;
+            if (e >= w_base + 64) {
+                w_base += 64;
+                w_cur = w_next;
+                w_next = table_load(w_base + 64);
+            }
+            int b = __builtin_amdgcn_readlane((int)w_cur, e - w_base);
+            b = b < 0 ? 0 : b;
+            b = b > a.last_block ? a.last_block : b;
+            return (int64_t)b;
+        };
 
         auto issue = [&](int t, int64_t blk, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
             const bool live = t < ntiles;
@@ -267,7 +315,8 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
                 const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
-                const bf16x8 qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+                const bf16x8 qb = kQInRegs ? qf[j]
+                                           : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
             }
             float x[4];
@@ -309,11 +358,9 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
             }
         };
 
-        uint32_t entry = table_fetch(tab, 0);
 #pragma unroll
         for (int b = 0; b < NB - 1; ++b) {
-            const int64_t blk = table_block(tab, entry);
-            entry = table_fetch(tab, b + 1);
+            const int64_t blk = block_of(b);
             __builtin_amdgcn_sched_barrier(0);
             issue(b, blk, kb[b], vb[b]);
         }
@@ -321,8 +368,7 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int ti = t + b + NB - 1;
-                const int64_t blk = table_block(tab, entry);
-                entry = table_fetch(tab, ti + 1);
+                const int64_t blk = block_of(ti);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(ti, blk, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
                 __builtin_amdgcn_sched_barrier(0);
