@@ -200,13 +200,14 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     }
     // MFMA tiles are 16 rows by 16 query-head columns. With g <= 8 a KV
     // head fills at most half of the columns, so 2 adjacent KV heads share a
-    // tile, 8 tokens each: the columns do useful work and each token's two
-    // rows are read as one contiguous chunk (512 bytes for bf16, D = 128).
-    // Measured on the 70B batch (g = 8, bf16): 79 -> 84 % of peak. 4 heads
-    // of 4-token tiles (g <= 4) measured slower than 1, and fp8 caches gave
-    // erratic times when packed; both are only used when asked for. Only
-    // g in 5..8 packs by default: below that half the columns would still
-    // be padding.
+    // tile, 8 tokens each, and each token's two rows are read as one
+    // contiguous chunk (512 bytes for bf16, 256 for fp8, D = 128). Measured
+    // on MI355X: 70B batch (g = 8) bf16 79 -> 84 % of peak, fp8 68 -> 74 %;
+    // mixed batch (g = 4) bf16 81 -> 86 %; long contexts (g = 4) bf16
+    // 72 -> 75 %. fp8 with g = 4 packed gained on long contexts but lost on
+    // the mixed batch, and 4 heads of 4-token tiles measured slower than 1:
+    // those are only used when asked for. Packed bf16 does best two tiles
+    // ahead, packed fp8 one.
     if (o.heads_per_tile != 0 && o.heads_per_tile != 1 && o.heads_per_tile != 2 && o.heads_per_tile != 4)
         return PA_ERR_SHAPE;
     if (p.variant == PA_VARIANT_MFMA) {
@@ -214,10 +215,9 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
         if (o.heads_per_tile != 0) {
             hp = o.heads_per_tile;
             if (g * hp > 16 || Hkv % hp != 0) return PA_ERR_UNSUPPORTED;
-        } else if (g >= 5 && g <= 8 && Hkv % 2 == 0 && kv_dtype == PA_KV_BF16) {
+        } else if (g <= 8 && Hkv % 2 == 0 && (kv_dtype == PA_KV_BF16 ? g >= 4 : g >= 5)) {
             hp = 2;
-            // the packed bf16 kernel measured best two tiles ahead
-            if (o.prefetch_tiles == 0) p.depth = 3;
+            if (o.prefetch_tiles == 0) p.depth = kv_dtype == PA_KV_BF16 ? 3 : 2;
         }
         p.heads_per_unit = hp;
     } else if (o.heads_per_tile > 1) {

@@ -249,12 +249,13 @@ def test_cascade_workspace_without_groups(lib):
     """No groups: header + the suffix pass's work list + its partial states,
     which a cascade keeps even when contexts are not split."""
     S, Hq, Hkv, D, MB = 4, 8, 2, 64, 7
+    units = Hkv // pa.pa_decode_get_plan(S, Hq, Hkv, D, 16, MB, partition_tokens=-1)["heads_per_tile"]
     n = pa.pa_decode_cascade_workspace_size(S, Hq, Hkv, D, 16, MB, 0, 0, 1, partition_tokens=-1)
     P = 1
-    assert n == 256 + _align(S * Hkv * P * 16) + _align(S * Hq * P * 2 * 4) + _align(S * Hq * P * D * 4)
+    assert n == 256 + _align(S * units * P * 16) + _align(S * Hq * P * 2 * 4) + _align(S * Hq * P * D * 4)
     n2 = pa.pa_decode_cascade_workspace_size(S, Hq, Hkv, D, 16, MB, 0, 0, 1, partition_tokens=32)
     P = -(-MB * 16 // 32)
-    assert n2 == 256 + _align(S * Hkv * P * 16) + _align(S * Hq * P * 2 * 4) + _align(S * Hq * P * D * 4)
+    assert n2 == 256 + _align(S * units * P * 16) + _align(S * Hq * P * 2 * 4) + _align(S * Hq * P * D * 4)
     assert pa.pa_decode_cascade_workspace_size(S, 64, 2, D, 16, MB, 0, 0, 1, partition_tokens=-1) == 0
 
 
