@@ -410,3 +410,37 @@ def test_copy_blocks_then_decode_through_copies(lib):
     after = host_bits(d.decode())
     torch.cuda.synchronize()
     assert np.array_equal(before, after)
+
+
+def test_tutorial_paged_cache_example(lib):
+    """The worked example of Tutorial §4.2 (PagedKVCache usage: 5 sequences of
+    100 tokens, 32 KV heads of 128, blocks of 16 in a pool of 500), one layer:
+    pa_cache_write of all 500 tokens through the slots the example's block
+    tables imply (tests/golden/), then pa_decode. The pool matches the
+    oracle's cache write bit for bit and the output matches the oracle."""
+    import json, math, os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tutorial_4_2_paged_cache_example.json")))
+    bs, N, Hkv, D = fx["block_size"], fx["num_blocks"], fx["num_kv_heads"], fx["head_dim"]
+    lens = fx["seq_lengths"]
+    S, T = len(lens), sum(lens)
+    slots = np.array([fx["block_tables"][i][j // bs] * bs + j % bs for i, L in enumerate(lens) for j in range(L)],
+                     np.int64)
+    rng = np.random.default_rng(43)
+    bits = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    k = bits(rng.standard_normal((T, Hkv, D)))
+    v = bits(rng.standard_normal((T, Hkv, D)))
+    q = bits(rng.standard_normal((S, Hkv, D)))
+    kc = np.zeros((N, bs, Hkv, D), np.uint16)
+    vc = np.zeros_like(kc)
+    oracle.cache_write(k, v, slots, kc, vc)
+    tables = np.array(fx["block_tables"], np.int32)
+    ctx = np.array(lens, np.int32)
+    ref = oracle.decode(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D))
+    dk = torch.zeros((N, bs, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    dv = torch.zeros_like(dk)
+    note("tutorial paged cache example")
+    pa.pa_cache_write(dev_bf16(k), dev_bf16(v), torch.from_numpy(slots).cuda(), dk, dv)
+    out = pa.pa_decode(dev_bf16(q), dk, dv, torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(),
+                       1.0 / math.sqrt(D))
+    assert np.array_equal(host_bits(dk), kc) and np.array_equal(host_bits(dv), vc)
+    compare(host_bits(out), ref, *BF16_TOL)
