@@ -78,11 +78,11 @@ int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32
 }
 
 // Tokens per partition for `units` independent workgroup groups over
-// contexts of at most `cap` tokens: enough workgroups to fill the chip
-// several times over, but no split while whole contexts already give that
-// and stay short. partition_tokens: 0 = choose, -1 = never split, > 0 =
-// forced (a multiple of the tile).
-int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int64_t* P_out) {
+// contexts of at most `cap` tokens: enough workgroups to fill every
+// resident slot (groups_per_cu per CU) twice over, but no split while whole
+// contexts already give two per CU and stay short. partition_tokens: 0 =
+// choose, -1 = never split, > 0 = forced (a multiple of the tile).
+int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int groups_per_cu, int64_t* P_out) {
     const int64_t cap16 = align_up((size_t)cap, pa::kTile);
     int64_t P;
     if (partition_tokens > 0) {
@@ -97,7 +97,7 @@ int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int64
             P = cap16;
         } else {
             P = 4096;
-            while (P > 512 && units * ((cap + P - 1) / P) < 4 * cus) P /= 2;
+            while (P > 512 && units * ((cap + P - 1) / P) < 2 * (int64_t)groups_per_cu * cus) P /= 2;
         }
     }
     if (P >= cap16) P = cap16;
@@ -125,7 +125,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     p.row_blocks = (int)rb;
     const int64_t cap = (int64_t)MB * bs;
     int64_t P = 0;
-    const int st = choose_partition((int64_t)S * Hkv * rb, cap, partition_tokens, &P);
+    const int st = choose_partition((int64_t)S * Hkv * rb, cap, partition_tokens, 2, &P);
     if (st != PA_OK) return st;
     p.partition_tokens = (int)P;
     p.num_partitions = (int)((cap + P - 1) / P);
@@ -229,7 +229,18 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     const int64_t cap = (int64_t)MB * bs;  // longest context the tables can hold
     const int64_t units = (int64_t)S * (Hkv / p.heads_per_unit);
     int64_t P = 0;
-    st = choose_partition(units, cap, o.partition_tokens, &P);
+    // Resident workgroups per CU: the MFMA kernel's register budget targets
+    // waves per SIMD by ring depth (decode_mfma.hip, mfma_waves_per_eu), one
+    // wave per SIMD for 4 waves a workgroup. Measured on the long-context
+    // batch (fp8, one KV head per tile, 4 resident): 2048-token partitions
+    // 138 us against 151 us for 4096, which a target of 2 per CU kept.
+    int groups_per_cu = 2;
+    if (p.variant == PA_VARIANT_MFMA) {
+        const int base = p.depth <= 2 ? 4 : (p.depth == 3 ? 3 : 2);
+        const int wpe = (p.heads_per_unit > 1 && kv_dtype == PA_KV_BF16 && base > 2) ? base - 1 : base;
+        groups_per_cu = wpe * 4 / p.waves > 1 ? wpe * 4 / p.waves : 1;
+    }
+    st = choose_partition(units, cap, o.partition_tokens, groups_per_cu, &P);
     if (st != PA_OK) return st;
     p.partition_tokens = (int)P;
     p.num_partitions = (int)((cap + P - 1) / P);
