@@ -113,6 +113,28 @@ def stats(d: str) -> list:
     return rows
 
 
+def last_dispatches(d: str, n: int) -> list:
+    """Per kernel, statistics over its last n dispatches (in dispatch order)
+    from the kernel trace CSV: the timed steps of a benchmark run, without
+    its warm-up."""
+    per = defaultdict(list)
+    with open(_find(d, "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            per[r["Kernel_Name"]].append((int(r["Dispatch_Id"]),
+                                          float(r["End_Timestamp"]) - float(r["Start_Timestamp"])))
+    rows = []
+    for name, ds in per.items():
+        ds.sort()
+        t = [x for _, x in ds[-n:]]
+        rows.append({"name": name, "calls": len(t), "total_ns": sum(t), "avg_ns": sum(t) / len(t),
+                     "min_ns": min(t), "max_ns": max(t)})
+    total = sum(r["total_ns"] for r in rows) or 1.0
+    for r in rows:
+        r["pct"] = 100.0 * r["total_ns"] / total
+    rows.sort(key=lambda r: -r["total_ns"])
+    return rows
+
+
 def counters(d: str) -> dict:
     """{kernel name: {counter: [value per dispatch]}}"""
     out = defaultdict(lambda: defaultdict(list))
@@ -123,8 +145,11 @@ def counters(d: str) -> dict:
 
 
 def cmd_stats(a) -> None:
-    rows = stats(a.dir)
-    lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+    last = getattr(a, "last", 0) or 0
+    rows = last_dispatches(a.dir, last) if last > 0 else stats(a.dir)
+    head = ([f"Last {last} dispatches of each kernel (the timed steps), from the per-dispatch kernel trace.", ""]
+            if last > 0 else [])
+    lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", ""] + head + [
              "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{_short(r['name'])}` | {r['calls']} | {r['avg_ns'] / 1e3:.2f} | {r['min_ns'] / 1e3:.2f} | "
@@ -143,9 +168,10 @@ def cmd_traffic(a) -> None:
                 return k, v[counter]
         raise KeyError(f"{key_sub} / {counter} not in the counter CSV: {list(cs)}")
 
-    # the copy kernel: the non-pa kernel that both reads and writes (a fill
-    # only writes)
-    copy_name = next(k for k in fetch if "pa_" not in k and "Fill" not in k and "copyBuffer" not in k)
+    # the copy kernel: of the kernels outside the library, the one that reads
+    # the most (the 1 GiB copy; fills read nothing, index helpers little)
+    others = [k for k in fetch if "pa_" not in k and "FETCH_SIZE" in fetch[k] and k in write]
+    copy_name = max(others, key=lambda k: fetch[k]["FETCH_SIZE"][0])
     cf = fetch[copy_name]["FETCH_SIZE"][0]
     cw = write[copy_name]["WRITE_SIZE"][0]
     f_scale = a.copy_bytes / cf
@@ -173,6 +199,8 @@ def main() -> int:
     s.add_argument("out")
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", default="rocprofv3 kernel statistics")
+    s.add_argument("--last", type=int, default=0,
+                   help="summarise each kernel's last N dispatches only (the timed steps)")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")

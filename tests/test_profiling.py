@@ -35,10 +35,13 @@ def test_traffic_scaling(tmp_path):
     copy = "void at::native::elementwise_kernel<...>(int)"
     dec = "void pa::(anonymous namespace)::pa_decode_mfma_kernel<128, false, 3>(pa::DecodeArgs)"
     # counters read in KiB: the copy of 1 MiB reads 1024 KiB and writes 1024 KiB
+    idx = "void at::native::elementwise_kernel_with_index<int, arange>(int)"  # a small helper kernel first
     _write(str(tmp_path / "f" / "a_counter_collection.csv"), hdr,
-           [[1, copy, "FETCH_SIZE", 1024.0], [2, dec, "FETCH_SIZE", 2000.0], [3, dec, "FETCH_SIZE", 2100.0]])
+           [[0, idx, "FETCH_SIZE", 3.0], [1, copy, "FETCH_SIZE", 1024.0], [2, dec, "FETCH_SIZE", 2000.0],
+            [3, dec, "FETCH_SIZE", 2100.0]])
     _write(str(tmp_path / "w" / "a_counter_collection.csv"), hdr,
-           [[1, copy, "WRITE_SIZE", 1024.0], [2, dec, "WRITE_SIZE", 10.0], [3, dec, "WRITE_SIZE", 12.0]])
+           [[0, idx, "WRITE_SIZE", 8.0], [1, copy, "WRITE_SIZE", 1024.0], [2, dec, "WRITE_SIZE", 10.0],
+            [3, dec, "WRITE_SIZE", 12.0]])
     class A:
         fetch_dir, write_dir = str(tmp_path / "f"), str(tmp_path / "w")
         out = str(tmp_path / "t.json")
