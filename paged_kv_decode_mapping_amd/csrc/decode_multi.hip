@@ -80,6 +80,18 @@ __device__ __forceinline__ void fp8x16_to_bf16_m(const u32x4& w, u32x4& lo, u32x
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
+// Maximum over the four lanes c, c + 16, c + 32, c + 48 (one MFMA column),
+// returned to all four: v_permlane16_swap exchanges lanes 16 apart and
+// v_permlane32_swap lanes 32 apart, each result pair holding the lane's own
+// value and its partner's. Both run on the VALU; a ds_bpermute exchange
+// costs an LDS round trip per step, on the critical path of every tile.
+__device__ __forceinline__ float column_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Work item of a workgroup: (sequence, KV head, row block, partition).
 struct MultiItem {
     int seq, kvh, rb, part;
@@ -95,14 +107,35 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     constexpr int EPL = 16 / ESZ;            // elements per 16-byte chunk
     constexpr int LPR = D / EPL;             // chunks per token row
     constexpr int CHUNKS = kTile * LPR;      // chunks per tile (of K, and of V)
-    constexpr int NI = (CHUNKS + 64 * W - 1) / (64 * W);  // chunks per lane
-    constexpr int RS = D + 8;                // LDS row stride, bf16 elements
+    constexpr int LANES = 64 * W;
+    // Tiles per ring slot: with at least twice as many lanes as a tile has
+    // chunks, the two halves of the workgroup load two consecutive tiles at
+    // once (one chunk of each per lane), which doubles the bytes in flight
+    // at no register cost: every wave of the workgroup steps through the
+    // same tiles, so the tiles in flight per workgroup are what hides the
+    // memory latency. One barrier then stages both.
+    constexpr int TPS = LANES >= 2 * CHUNKS ? 2 : 1;
+    constexpr int NI = TPS > 1 ? 1 : (CHUNKS + LANES - 1) / LANES;  // chunks per lane and slot
+    constexpr int SROWS = TPS * kTile;       // token rows staged per LDS buffer
+    constexpr int RS = D + 8;                // LDS row stride of q and K rows, bf16 elements
+    // V rows: 16 more elements. A transposing read takes 4 rows x 32 bytes
+    // per 16 lanes; rows 32 bytes apart in bank order (stride 288 bytes for
+    // D = 128) keep those 4 segments on disjoint banks, where 272 bytes
+    // overlaps them two-way. K rows keep 272 bytes: their 16-byte reads by
+    // 16 lanes are conflict-free there and would collide at 288.
+    constexpr int RSV = D + 16;
     static_assert(NB % 2 == 0, "the LDS buffer of a ring slot is its parity");
 
+    // With 4 or 8 waves (many rows: LDS traffic counts), this wave's query
+    // fragments, the B operand of every q.K^T MFMA, stay in registers instead
+    // of being read from LDS for every tile, and the query rows' LDS is then
+    // reused for the K/V buffers; with 1 or 2 waves (few rows, memory-bound)
+    // the 16 registers would cost occupancy.
+    constexpr bool kQInRegs = W >= 4;
     extern __shared__ float smem[];
-    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);  // [16 W][RS] query rows
-    uint16_t* kbuf = qs + 16 * W * RS;                  // [2][16][RS]
-    uint16_t* vbuf = kbuf + 2 * kTile * RS;             // [2][16][RS]
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);   // [16 W][RS] query rows
+    uint16_t* kbuf = kQInRegs ? qs : qs + 16 * W * RS;   // [2][SROWS][RS]
+    uint16_t* vbuf = kbuf + 2 * SROWS * RS;              // [2][SROWS][RSV]
 
     // ---- the work item
     int bid = (int)blockIdx.x;
@@ -219,6 +252,12 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
         *reinterpret_cast<u32x4*>(qs + rr * RS + 8 * (i - rr * (D / 8))) = qv[k];
     }
     const uint16_t* q_row = qs + (wave * 16 + c) * RS + 8 * gq;
+    // The last token every valid row of this wave sees (wave-uniform): tiles
+    // that end at or before it, and before t_end, need no mask.
+    int wave_pos = my_valid ? my_pos : 0x7fffffff;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) wave_pos = min(wave_pos, __shfl_xor(wave_pos, off, 64));
+    wave_pos = __builtin_amdgcn_readfirstlane(wave_pos);
 
     float m = -INFINITY, l = 0.0f;
     f32x4 o[NPV];
@@ -229,35 +268,38 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     const int bs_mask = (1 << a.block_size_log2) - 1;
     const float qk = a.qk_scale_log2;
 
-    // chunk i of this lane: id k = tid + 64 W i -> token row k / LPR, chunk k % LPR
+    // Chunk i of this lane. One tile per slot: id k = tid + 64 W i -> token
+    // row k / LPR, chunk k % LPR. Two: lanes [0, CHUNKS) load the slot's
+    // first tile and [CHUNKS, 2 CHUNKS) its second (id k = tid % CHUNKS);
+    // my_ts is that tile (wave-uniform, as CHUNKS is a multiple of 64).
+    const int my_ts = TPS > 1 ? min((int)threadIdx.x / CHUNKS, TPS - 1) : 0;
     uint32_t coff[NI];
     bool cown[NI];
+    int cid[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int k = (int)threadIdx.x + 64 * W * i;
-        cown[i] = k < CHUNKS;
+        const int k = TPS > 1 ? (int)threadIdx.x - my_ts * CHUNKS : (int)threadIdx.x + LANES * i;
+        cown[i] = TPS > 1 ? (int)threadIdx.x < TPS * CHUNKS : k < CHUNKS;
         const int kk = cown[i] ? k : 0;
+        cid[i] = kk;
         // a lane past the tile's chunks reads past every descriptor (zeros)
         coff[i] = cown[i] ? (uint32_t)(kk / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(kk % LPR) : 0x7fffffffu;
     }
+    const int nslots = (ntiles + TPS - 1) / TPS;
 
     u32x4 kb[NB][NI], vb[NB][NI];
 
     __syncthreads();  // query rows in LDS
-    // With 4 or 8 waves (many rows: the kernel is LDS-bound), this wave's
-    // query fragments, the B operand of every q.K^T MFMA, stay in registers
-    // instead of being read from LDS for every tile; with 1 or 2 waves (few
-    // rows, memory-bound) the 16 registers would cost occupancy.
-    constexpr bool kQInRegs = W >= 4;
     bf16x8 qf[NQK];
     if constexpr (kQInRegs) {
 #pragma unroll
         for (int j = 0; j < NQK; ++j) qf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+        __syncthreads();  // every wave has its fragments: the K/V staging may overwrite the rows
     }
 
     if (ntiles > 0) {
         // physical block of tile t (tiles past the last take the last one's),
-        // clamped into the pool; t grows by at most one between calls
+        // clamped into the pool; a wave calls it with t growing by at most TPS
         auto block_of = [&](int t) -> int64_t {
             const int e = (t_begin + min(t, ntiles - 1) * kTile) >> a.block_size_log2;
             if (e >= w_base + 64) {
@@ -271,7 +313,11 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
             return (int64_t)b;
         };
 
-        auto issue = [&](int t, int64_t blk, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+        // loads of ring slot sl: this lane's tile of it is sl * TPS + my_ts
+        auto issue = [&](int sl, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+            const int t = sl * TPS + my_ts;
+            const int64_t blk = block_of(t);
+            __builtin_amdgcn_sched_barrier(0);
             const bool live = t < ntiles;
             const int t0 = t_begin + (live ? t : ntiles - 1) * kTile;
             const uint32_t rowb = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
@@ -285,31 +331,20 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
             for (int i = 0; i < NI; ++i) vr[i] = buf_load_b128_stream(rv, coff[i], rowb);
         };
 
-        auto stage = [&](uint16_t* dst, const u32x4& w, int k) {
-            const int row = k / LPR, ch = k % LPR;
+        auto stage = [&](uint16_t* dst, int rs, const u32x4& w, int k) {
+            const int row = my_ts * kTile + k / LPR, ch = k % LPR;
             if constexpr (!FP8) {
-                *reinterpret_cast<u32x4*>(dst + row * RS + ch * 8) = w;
+                *reinterpret_cast<u32x4*>(dst + row * rs + ch * 8) = w;
             } else {
                 u32x4 lo, hi;
                 fp8x16_to_bf16_m(w, lo, hi);
-                *reinterpret_cast<u32x4*>(dst + row * RS + ch * 16) = lo;
-                *reinterpret_cast<u32x4*>(dst + row * RS + ch * 16 + 8) = hi;
+                *reinterpret_cast<u32x4*>(dst + row * rs + ch * 16) = lo;
+                *reinterpret_cast<u32x4*>(dst + row * rs + ch * 16 + 8) = hi;
             }
         };
 
-        auto consume = [&](int t, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], int buf) {
-            uint16_t* ks = kbuf + buf * kTile * RS;
-            uint16_t* vs = vbuf + buf * kTile * RS;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                if (cown[i]) {
-                    const int k = (int)threadIdx.x + 64 * W * i;
-                    stage(ks, kr[i], k);
-                    stage(vs, vr[i], k);
-                }
-            }
-            __syncthreads();  // the tile is in LDS; the other buffer's readers are done
-
+        // one tile of a staged slot: scores, online softmax, P.V
+        auto compute = [&](int t, const uint16_t* ks, const uint16_t* vs) {
             const int t0 = t_begin + t * kTile;
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -320,14 +355,17 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
             }
             float x[4];
+            if (t0 + kTile - 1 <= wave_pos && t0 + kTile <= t_end) {  // uniform: every row sees the whole tile
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = t0 + 4 * gq + r;
-                x[r] = (tok > my_pos || tok >= t_end) ? -INFINITY : s[r] * qk;
+                for (int r = 0; r < 4; ++r) x[r] = s[r] * qk;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = t0 + 4 * gq + r;
+                    x[r] = (tok > my_pos || tok >= t_end) ? -INFINITY : s[r] * qk;
+                }
             }
-            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            mx = fmaxf(mx, xor_shfl(mx, 16));
-            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
             const float m_new = fmaxf(m, mx);
             const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
             const float alpha = fast_exp2(m - ms);
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
                 for (int j = 0; j < NPV; ++j) o[j] *= alpha;
             }
             // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c]
-            const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RS + 4 * (lane & 3);
+            const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RSV + 4 * (lane & 3);
 #pragma unroll
             for (int j = 0; j < NPV; ++j) {
                 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -358,21 +396,103 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
             }
         };
 
+        // Two consecutive tiles t and t + 1 as one step of 32 tokens (the
+        // second may lie past the item: its scores are masked and its V rows
+        // were loaded as zeros): one softmax update, and P.V as
+        // v_mfma_f32_16x16x32_bf16, half as many as 16x16x16 steps. Its K
+        // index 8 gq + j stands for token 4 gq + j of the first tile (j < 4)
+        // and 4 gq + j - 4 of the second (j >= 4): the lane's own eight
+        // probabilities in that order, and V^T as the two tiles' transposed
+        // reads side by side.
+        auto compute_pair = [&](int t, const uint16_t* ks, const uint16_t* vs) {
+            const int t0 = t_begin + t * kTile;
+            f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < NB - 1; ++b) {
-            const int64_t blk = block_of(b);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(b, blk, kb[b], vb[b]);
-        }
-        for (int t = 0; t < ntiles; t += NB) {
+            for (int j = 0; j < NQK; ++j) {
+                const bf16x8 qb = kQInRegs ? qf[j]
+                                           : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
+                const bf16x8 kb2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + (kTile + c) * RS + 32 * j + 8 * gq));
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb2, qb, sb, 0, 0, 0);
+            }
+            float x[8];
+            if (t0 + 2 * kTile - 1 <= wave_pos && t0 + 2 * kTile <= t_end) {  // uniform: nothing to mask
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[r] = sa[r] * qk;
+                    x[4 + r] = sb[r] * qk;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ta = t0 + 4 * gq + r, tb = ta + kTile;
+                    x[r] = (ta > my_pos || ta >= t_end) ? -INFINITY : sa[r] * qk;
+                    x[4 + r] = (tb > my_pos || tb >= t_end) ? -INFINITY : sb[r] * qk;
+                }
+            }
+            const float mx = column_max4(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+            const float m_new = fmaxf(m, mx);
+            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m - ms);
+            const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
+            m = m_new;
+            bf16x8 pb;
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
+                pb[r] = b;
+                psum += (float)b;
+            }
+            l = fmaf(l, alpha, psum);
+            if (moved) {
+#pragma unroll
+                for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+            }
+            // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c] of each tile
+            const uint16_t* tr_a = vs + (4 * gq + (c >> 2)) * RSV + 4 * (lane & 3);
+            const uint16_t* tr_b = tr_a + kTile * RSV;
+#pragma unroll
+            for (int j = 0; j < NPV; ++j) {
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                typedef __attribute__((address_space(3))) uint16_t lds_u16;
+                const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_a) + 16 * j)));
+                const bf16x4 vb2 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_b) + 16 * j)));
+                const bf16x8 v8 = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pb, o[j], 0, 0, 0);
+            }
+        };
+
+        auto consume = [&](int sl, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], int buf) {
+            uint16_t* ks = kbuf + buf * SROWS * RS;
+            uint16_t* vs = vbuf + buf * SROWS * RSV;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                if (cown[i]) {
+                    stage(ks, RS, kr[i], cid[i]);
+                    stage(vs, RSV, vr[i], cid[i]);
+                }
+            }
+            __syncthreads();  // the slot is in LDS; the other buffer's readers are done
+            if constexpr (TPS == 2) {
+                compute_pair(sl * 2, ks, vs);
+            } else {
+                compute(sl, ks, vs);
+            }
+        };
+
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b) issue(b, kb[b], vb[b]);
+        for (int sl = 0; sl < nslots; sl += NB) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int ti = t + b + NB - 1;
-                const int64_t blk = block_of(ti);
+                issue(sl + b + NB - 1, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
                 __builtin_amdgcn_sched_barrier(0);
-                issue(ti, blk, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (t + b < ntiles) consume(t + b, kb[b], vb[b], b & 1);  // uniform over the workgroup
+                if (sl + b < nslots) consume(sl + b, kb[b], vb[b], b & 1);  // uniform over the workgroup
             }
         }
     }
@@ -460,7 +580,12 @@ __global__ __launch_bounds__(256) void pa_multi_merge_kernel(MultiArgs a) {
 template <int D, bool FP8, int W>
 hipError_t launch_w(const MultiArgs& a, hipStream_t s) {
     constexpr int NB = W == 1 ? 2 : 4;
-    const size_t lds = ((size_t)16 * W + 4 * kTile) * (D + 8) * sizeof(uint16_t);
+    // as in the kernel: tiles per ring slot, query rows' LDS reused by the K/V buffers at 4 or 8 waves
+    constexpr int LPR = D / (FP8 ? 16 : 8);
+    constexpr int TPS = 64 * W >= 2 * kTile * LPR ? 2 : 1;
+    const size_t q_elems = (size_t)16 * W * (D + 8);
+    const size_t kv_elems = (size_t)2 * TPS * kTile * (D + 8) + (size_t)2 * TPS * kTile * (D + 16);
+    const size_t lds = (W >= 4 ? (q_elems > kv_elems ? q_elems : kv_elems) : q_elems + kv_elems) * sizeof(uint16_t);
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.row_blocks * a.num_partitions));
     hipLaunchKernelGGL((pa_multi_kernel<D, FP8, W, NB>), grid, dim3(64 * W), lds, s, a);
     return hipGetLastError();
