@@ -96,6 +96,27 @@ def cpu_baseline(w, kv: str, kq=None, vq=None, budget_s: float = 12.0) -> dict:
                       f"float64 gather + softmax(qK^T)V, same byte model"}
 
 
+def stream_read_gbps(dev, nbytes: int, iters: int, nontemporal: bool = True) -> float:
+    """Read rate of the library's streaming-read probe over nbytes (one pass,
+    16-byte loads), averaged over iters timed launches after two untimed."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        pa.pa_probe_stream_read(x, sink, nontemporal)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        pa.pa_probe_stream_read(x, sink, nontemporal)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    del x
+    return nbytes / (ms.mean() * 1e-3) / 1e9
+
+
 def bench_stream(args, dev) -> int:
     """Streaming-read reference on the same GPU: the library's probe kernel
     reads a 4 GiB buffer once with 16-byte loads, with the default cache
@@ -628,6 +649,11 @@ def main() -> int:
         check = {"units": len(units), "max_abs": float(errs.max()), "mean_abs": float(errs.mean())}
         log(f"check vs oracle on {len(units)} units: {check}")
 
+    # the practical read ceiling on this GPU, for context: the library's
+    # streaming-read probe over 2 GiB with the decode kernels' non-temporal loads
+    stream_gbps = stream_read_gbps(dev, 2 << 30, 10)
+    log(f"streaming read {stream_gbps:.0f} GB/s; decode at {achieved / stream_gbps:.1%} of it")
+
     base = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -663,6 +689,8 @@ def main() -> int:
         "decode_us": {"avg": round(dec_avg * 1e3, 2), "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                       "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
         "cache_write_us": round(float(write_ms.mean()) * 1e3, 2),
+        "stream_read_gbps": round(stream_gbps, 1),
+        "decode_frac_of_stream_read": round(achieved / stream_gbps, 4),
         "bytes": {"decode": dec_b, "cache_write": wr_b},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
