@@ -22,18 +22,22 @@
 // a row never leaves its lanes and a workgroup needs no combine step. Rows are the
 // columns of the same MFMA tiles the decode kernel uses:
 //   S = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q^T rows
-//               of this wave from LDS;
-//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, A = V^T by the transposing LDS
-//               read, B = the lane's own probabilities (bf16).
+//               of this wave (in registers with 4 or 8 waves, else LDS);
+//   O^T += V^T P^T  A = V^T by the transposing LDS read, B = the lane's own
+//               probabilities (bf16): v_mfma_f32_16x16x16_bf16 per tile, or
+//               v_mfma_f32_16x16x32_bf16 per pair of tiles (below).
 // Lane (c, gq) holds S[token 4 gq + r][row c]: the causal mask compares the
-// token with the position of row c.
+// token with the position of row c (skipped on tiles every row sees whole).
 //
 // Tiles. The workgroup walks its token range in 16-token tiles; all waves
 // use every tile, so the tile is loaded once, cooperatively (each lane one
 // or more 16-byte chunks of K and of V), and staged in LDS. Each lane keeps
-// a ring of NB tiles of its chunks in registers (NB - 1 in flight), and the
-// LDS copy is double-buffered, so one workgroup barrier per tile orders
+// a ring of NB slots of its chunks in registers (NB - 1 in flight), and the
+// LDS copy is double-buffered, so one workgroup barrier per slot orders
 // both the staging before the reads and the reads before the next overwrite.
+// With at least twice as many lanes as a tile has chunks, a slot holds two
+// consecutive tiles (one per half of the workgroup) consumed as one 32-token
+// step.
 // fp8 codes are widened to bf16 while staging (exact); the scales are folded
 // into the score scale and the output (ToPG §2: fp32 accumulation; ToPG §3:
 // fp8 KV).
