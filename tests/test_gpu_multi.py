@@ -67,7 +67,7 @@ def test_multi_matches_oracle(lib, name, partition):
     compare(got, ref, *BF16_TOL)
 
 
-@pytest.mark.parametrize("name", ["spec_verify_mixed", "long_bs128"])
+@pytest.mark.parametrize("name", ["spec_verify_mixed", "long_bs128", "verify16_70b", "chunk_prefill"])
 def test_multi_fp8_matches_oracle(lib, name):
     got, ref = _run(name, 0, "fp8")
     compare(got, ref, *FP8_TOL)
