@@ -112,14 +112,19 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     constexpr int LPR = D / EPL;             // chunks per token row
     constexpr int CHUNKS = kTile * LPR;      // chunks per tile (of K, and of V)
     constexpr int LANES = 64 * W;
-    // Tiles per ring slot: with at least twice as many lanes as a tile has
-    // chunks, the two halves of the workgroup load two consecutive tiles at
-    // once (one chunk of each per lane), which doubles the bytes in flight
-    // at no register cost: every wave of the workgroup steps through the
-    // same tiles, so the tiles in flight per workgroup are what hides the
-    // memory latency. One barrier then stages both.
-    constexpr int TPS = LANES >= 2 * CHUNKS ? 2 : 1;
-    constexpr int NI = TPS > 1 ? 1 : (CHUNKS + LANES - 1) / LANES;  // chunks per lane and slot
+    // Tiles per ring slot. Every wave of the workgroup steps through the same
+    // tiles, so what a slot holds is what hides latency and what one barrier
+    // stages; two consecutive tiles are consumed as one 32-token step.
+    //   mode 0: at least twice as many lanes as a tile has chunks: the two
+    //           halves of the workgroup load one tile each (one chunk a lane);
+    //   mode 1: exactly as many lanes as chunks, 4 or more waves: each lane
+    //           loads one chunk of each tile (the ring then has 2 slots, so
+    //           the registers stay those of 4 slots of one tile);
+    //   mode 2: fewer lanes (1 or 2 waves): one tile a slot, several chunks
+    //           a lane.
+    constexpr int MODE = LANES >= 2 * CHUNKS ? 0 : ((W >= 4 && LANES == CHUNKS) ? 1 : 2);
+    constexpr int TPS = MODE == 2 ? 1 : 2;
+    constexpr int NI = MODE == 0 ? 1 : (MODE == 1 ? 2 : (CHUNKS + LANES - 1) / LANES);  // chunks a lane loads per slot
     constexpr int SROWS = TPS * kTile;       // token rows staged per LDS buffer
     constexpr int RS = D + 8;                // LDS row stride of q and K rows, bf16 elements
     // V rows: 16 more elements. A transposing read takes 4 rows x 32 bytes
@@ -272,22 +277,36 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
     const int bs_mask = (1 << a.block_size_log2) - 1;
     const float qk = a.qk_scale_log2;
 
-    // Chunk i of this lane. One tile per slot: id k = tid + 64 W i -> token
-    // row k / LPR, chunk k % LPR. Two: lanes [0, CHUNKS) load the slot's
-    // first tile and [CHUNKS, 2 CHUNKS) its second (id k = tid % CHUNKS);
-    // my_ts is that tile (wave-uniform, as CHUNKS is a multiple of 64).
-    const int my_ts = TPS > 1 ? min((int)threadIdx.x / CHUNKS, TPS - 1) : 0;
+    // Chunk i of this lane: tile cts[i] of the slot, chunk id cid[i] within
+    // the tile (token row cid / LPR, 16-byte piece cid % LPR). The tile is
+    // wave-uniform: CHUNKS is a multiple of 64.
     uint32_t coff[NI];
     bool cown[NI];
-    int cid[NI];
+    int cid[NI], cts[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int k = TPS > 1 ? (int)threadIdx.x - my_ts * CHUNKS : (int)threadIdx.x + LANES * i;
-        cown[i] = TPS > 1 ? (int)threadIdx.x < TPS * CHUNKS : k < CHUNKS;
-        const int kk = cown[i] ? k : 0;
+        const int tid = (int)threadIdx.x;
+        int k, ts;
+        bool own;
+        if constexpr (MODE == 0) {
+            ts = min(tid / CHUNKS, TPS - 1);
+            k = tid - ts * CHUNKS;
+            own = tid < TPS * CHUNKS;
+        } else if constexpr (MODE == 1) {
+            ts = i;
+            k = tid;
+            own = true;
+        } else {
+            ts = 0;
+            k = tid + LANES * i;
+            own = k < CHUNKS;
+        }
+        cown[i] = own;
+        cts[i] = ts;
+        const int kk = own ? k : 0;
         cid[i] = kk;
         // a lane past the tile's chunks reads past every descriptor (zeros)
-        coff[i] = cown[i] ? (uint32_t)(kk / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(kk % LPR) : 0x7fffffffu;
+        coff[i] = own ? (uint32_t)(kk / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(kk % LPR) : 0x7fffffffu;
     }
     const int nslots = (ntiles + TPS - 1) / TPS;
 
@@ -317,26 +336,27 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
             return (int64_t)b;
         };
 
-        // loads of ring slot sl: this lane's tile of it is sl * TPS + my_ts
+        // loads of ring slot sl: chunk i of this lane belongs to tile sl * TPS + cts[i]
         auto issue = [&](int sl, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
-            const int t = sl * TPS + my_ts;
-            const int64_t blk = block_of(t);
-            __builtin_amdgcn_sched_barrier(0);
-            const bool live = t < ntiles;
-            const int t0 = t_begin + (live ? t : ntiles - 1) * kTile;
-            const uint32_t rowb = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
-            const int valid = min(t_end - t0, kTile);
-            const uint32_t nbytes = live ? rowb + (uint32_t)valid * a.slot_bytes : 0u;
-            const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
-            const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) kr[i] = buf_load_b128_stream(rk, coff[i], rowb);
-#pragma unroll
-            for (int i = 0; i < NI; ++i) vr[i] = buf_load_b128_stream(rv, coff[i], rowb);
+            for (int i = 0; i < NI; ++i) {
+                const int t = sl * TPS + cts[i];
+                const int64_t blk = block_of(t);
+                __builtin_amdgcn_sched_barrier(0);
+                const bool live = t < ntiles;
+                const int t0 = t_begin + (live ? t : ntiles - 1) * kTile;
+                const uint32_t rowb = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
+                const int valid = min(t_end - t0, kTile);
+                const uint32_t nbytes = live ? rowb + (uint32_t)valid * a.slot_bytes : 0u;
+                const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
+                const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
+                kr[i] = buf_load_b128_stream(rk, coff[i], rowb);
+                vr[i] = buf_load_b128_stream(rv, coff[i], rowb);
+            }
         };
 
-        auto stage = [&](uint16_t* dst, int rs, const u32x4& w, int k) {
-            const int row = my_ts * kTile + k / LPR, ch = k % LPR;
+        auto stage = [&](uint16_t* dst, int rs, const u32x4& w, int ts, int k) {
+            const int row = ts * kTile + k / LPR, ch = k % LPR;
             if constexpr (!FP8) {
                 *reinterpret_cast<u32x4*>(dst + row * rs + ch * 8) = w;
             } else {
@@ -477,8 +497,8 @@ __global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 if (cown[i]) {
-                    stage(ks, RS, kr[i], cid[i]);
-                    stage(vs, RSV, vr[i], cid[i]);
+                    stage(ks, RS, kr[i], cts[i], cid[i]);
+                    stage(vs, RSV, vr[i], cts[i], cid[i]);
                 }
             }
             __syncthreads();  // the slot is in LDS; the other buffer's readers are done
@@ -583,10 +603,13 @@ __global__ __launch_bounds__(256) void pa_multi_merge_kernel(MultiArgs a) {
 
 template <int D, bool FP8, int W>
 hipError_t launch_w(const MultiArgs& a, hipStream_t s) {
-    constexpr int NB = W == 1 ? 2 : 4;
-    // as in the kernel: tiles per ring slot, query rows' LDS reused by the K/V buffers at 4 or 8 waves
-    constexpr int LPR = D / (FP8 ? 16 : 8);
-    constexpr int TPS = 64 * W >= 2 * kTile * LPR ? 2 : 1;
+    // as in the kernel: tiles per ring slot (two unless 1 or 2 waves fall
+    // short of a tile's chunks; a 2-slot ring when each lane loads one chunk
+    // of each), query rows' LDS reused by the K/V buffers at 4 or 8 waves
+    constexpr int CHUNKS = kTile * (D / (FP8 ? 16 : 8));
+    constexpr int MODE = 64 * W >= 2 * CHUNKS ? 0 : ((W >= 4 && 64 * W == CHUNKS) ? 1 : 2);
+    constexpr int TPS = MODE == 2 ? 1 : 2;
+    constexpr int NB = (W == 1 || MODE == 1) ? 2 : 4;
     const size_t q_elems = (size_t)16 * W * (D + 8);
     const size_t kv_elems = (size_t)2 * TPS * kTile * (D + 8) + (size_t)2 * TPS * kTile * (D + 16);
     const size_t lds = (W >= 4 ? (q_elems > kv_elems ? q_elems : kv_elems) : q_elems + kv_elems) * sizeof(uint16_t);

@@ -108,6 +108,13 @@ SPECS: Dict[str, WorkloadSpec] = {
 }
 ORDER: List[str] = ["tiny", "llama7b_mha", "llama70b_gqa", "long_splitk", "mixed_batch"]
 
+# The MQA extreme of the 70B layer (Tutorial §4.4: one KV head for all query
+# heads), for the wide-group route of pa_decode (g = 64).
+SPECS["mqa_70b"] = WorkloadSpec(
+    name="mqa_70b", num_seqs=128, num_q_heads=64, num_kv_heads=1, head_dim=128, block_size=16,
+    context=("const", 4096), seed=1006,
+    description="batch 128, 64/1 heads (MQA), D 128, bs 16, ctx 4096")
+
 # A batch for the shared-prefix (cascade) decode beyond the five above: every
 # request starts with the same long system prompt (Tutorial §4.3 names the
 # shared system prompt as prefix caching's case), on the 70B layer shape.
