@@ -584,21 +584,27 @@ __global__ __launch_bounds__(256) void pa_multi_merge_kernel(MultiArgs a) {
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int pos = L - n + r;
     const int np = pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
+    // lane owns elements lane * PER .. lane * PER + PER - 1 of the row; one
+    // pass over the partitions accumulates l and o together
+    constexpr int PER = D / 64;
     const float* ml = a.part_ml + wid * a.num_partitions * 2;
-    const float* po = a.part_o + wid * a.num_partitions * D;
+    const float* po = a.part_o + wid * a.num_partitions * D + lane * PER;
     float M = -INFINITY;
     for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    for (int d = lane; d < D; d += 64) {
-        float Lsum = 0.0f, O = 0.0f;
-        if (M != -INFINITY) {
-            for (int p = 0; p < np; ++p) {
-                const float f = state_weight(ml[2 * p], M);
-                Lsum += ml[2 * p + 1] * f;
-                O += po[(int64_t)p * D + d] * f;
-            }
-        }
-        a.out[wid * D + d] = f32_to_bf16_rne(Lsum > 0.0f ? O / Lsum : 0.0f);
+    float Lsum = 0.0f;
+    float O[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) O[e] = 0.0f;
+#pragma unroll 4
+    for (int p = 0; p < np; ++p) {
+        const float f = state_weight(ml[2 * p], M);
+        Lsum = fmaf(ml[2 * p + 1], f, Lsum);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) O[e] = fmaf(po[(int64_t)p * D + e], f, O[e]);
     }
+    uint16_t* dst = a.out + wid * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_rne(Lsum > 0.0f ? O[e] / Lsum : 0.0f);
 }
 
 template <int D, bool FP8, int W>
