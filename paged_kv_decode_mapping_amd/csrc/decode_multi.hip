@@ -104,7 +104,7 @@ struct MultiItem {
 };
 
 template <int D, bool FP8, int W, int NB>
-__global__ __launch_bounds__(64 * W) void pa_multi_kernel(MultiArgs a) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ? 4 : 1))) void pa_multi_kernel(MultiArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int NQK = D / 32;
     constexpr int NPV = D / 16;
