@@ -62,7 +62,7 @@
 // workgroup makes a long item slow, and a long item started last would
 // stretch the whole launch.
 #include "pa_cascade.h"
-#include "pa_epilogue.h"
+#include "pa_merge.h"
 
 namespace pa {
 namespace {
@@ -547,14 +547,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     }
 }
 
-// One wave per (query row, query head): log-sum-exp merge of the partitions
-// that hold tokens the row attends to (positions 0..p).
-template <int D>
-__global__ __launch_bounds__(256) void pa_multi_merge_kernel(MultiArgs a) {
-    const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int lane = (int)(threadIdx.x & 63);
-    const int64_t total = (int64_t)a.num_query_rows * a.num_q_heads;
-    if (wid >= total) return;
+// One workgroup of 64 * W threads per (query row, query head): log-sum-exp
+// merge of the partitions that hold tokens the row attends to (positions
+// 0..p).
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void pa_multi_merge_kernel(MultiArgs a) {
+    __shared__ __align__(16) float red[merge_lds_floats<D, W>()];
+    const int64_t wid = (int64_t)blockIdx.x;  // query row * Hq + query head
     const int qrow = (int)(wid / a.num_q_heads);
     // the sequence of this query row: the last i with query_start[i] <= qrow
     int seq, q0, n;
@@ -584,27 +583,23 @@ __global__ __launch_bounds__(256) void pa_multi_merge_kernel(MultiArgs a) {
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int pos = L - n + r;
     const int np = pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
-    // lane owns elements lane * PER .. lane * PER + PER - 1 of the row; one
-    // pass over the partitions accumulates l and o together
-    constexpr int PER = D / 64;
-    const float* ml = a.part_ml + wid * a.num_partitions * 2;
-    const float* po = a.part_o + wid * a.num_partitions * D + lane * PER;
-    float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    float Lsum = 0.0f;
-    float O[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) O[e] = 0.0f;
-#pragma unroll 4
-    for (int p = 0; p < np; ++p) {
-        const float f = state_weight(ml[2 * p], M);
-        Lsum = fmaf(ml[2 * p + 1], f, Lsum);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) O[e] = fmaf(po[(int64_t)p * D + e], f, O[e]);
-    }
-    uint16_t* dst = a.out + wid * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_rne(Lsum > 0.0f ? O[e] / Lsum : 0.0f);
+    merge_row<D, W>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np,
+                    nullptr, nullptr, 0, a.out + wid * D, red);
+}
+
+template <int D, int W>
+void launch_merge_w(const MultiArgs& a, int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL((pa_multi_merge_kernel<D, W>), dim3((unsigned)rows), dim3(64 * W), 0, s, a);
+}
+
+template <int D>
+void launch_multi_merge(const MultiArgs& a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.num_query_rows * a.num_q_heads;
+    const int w = merge_waves(D, a.num_partitions);
+    if (w <= 1) launch_merge_w<D, 1>(a, rows, s);
+    else if (w == 2) launch_merge_w<D, 2>(a, rows, s);
+    else if (w == 4) launch_merge_w<D, 4>(a, rows, s);
+    else launch_merge_w<D, 8>(a, rows, s);
 }
 
 template <int D, bool FP8, int W>
@@ -639,10 +634,8 @@ hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, h
     if (head_dim == 64) e = fp8 ? launch_df<64, true>(a, waves, s) : launch_df<64, false>(a, waves, s);
     else e = fp8 ? launch_df<128, true>(a, waves, s) : launch_df<128, false>(a, waves, s);
     if (e != hipSuccess || a.num_partitions == 1 || a.cascade.group_start != nullptr) return e;
-    const int64_t waves_total = (int64_t)a.num_query_rows * a.num_q_heads;
-    const dim3 grid((unsigned)((waves_total * 64 + 255) / 256));
-    if (head_dim == 64) hipLaunchKernelGGL(pa_multi_merge_kernel<64>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(pa_multi_merge_kernel<128>, grid, dim3(256), 0, s, a);
+    if (head_dim == 64) launch_multi_merge<64>(a, s);
+    else launch_multi_merge<128>(a, s);
     return hipGetLastError();
 }
 

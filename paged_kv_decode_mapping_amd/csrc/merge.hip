@@ -10,50 +10,35 @@
 // not describe the split; the partitioned evaluation is the flash-decoding
 // form of the tiling TGI «TGI技术解析» §5.2 describes for Flash Attention.
 #include "pa_cascade.h"
-#include "pa_epilogue.h"
+#include "pa_merge.h"
 
 namespace pa {
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(64) void pa_merge_kernel(MergeArgs a) {
-    constexpr int PER = D / 64;
+// One workgroup of 64 * W threads per (sequence, query head) row.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void pa_merge_kernel(MergeArgs a) {
+    __shared__ __align__(16) float red[merge_lds_floats<D, W>()];
     const int row = (int)blockIdx.x;  // seq * Hq + q head
     const int seq = row / a.num_q_heads;
     int ctx = a.context_lens[seq];
     ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
     const int np = (ctx + a.partition_tokens - 1) / a.partition_tokens;
     if (np <= 1) return;  // the decode kernel stored the output itself
-    const int lane = (int)threadIdx.x;
     const float* ml = a.part_ml + (int64_t)row * a.num_partitions * 2;
-    const float* po = a.part_o + (int64_t)row * a.num_partitions * D + lane * PER;
-    float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.0f;
-    float O[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) O[e] = 0.0f;
-#pragma unroll 4
-    for (int p = 0; p < np; ++p) {
-        const float f = state_weight(ml[2 * p], M);
-        L = fmaf(ml[2 * p + 1], f, L);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) O[e] = fmaf(po[(int64_t)p * D + e], f, O[e]);
-    }
-    uint16_t* dst = a.out + (int64_t)row * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_rne(L > 0.0f ? O[e] / L : 0.0f);
+    const float* po = a.part_o + (int64_t)row * a.num_partitions * D;
+    merge_row<D, W>(ml, po, np, nullptr, nullptr, 0, a.out + (int64_t)row * D, red);
 }
 
 // Cascade merge: one workgroup per (sequence, query head). A sequence with
 // prefix tokens combines the prefix pass's states over them (partitions of
-// prefix_partition_tokens) with the suffix pass's states over the rest
-// (partitions of partition_tokens; none when nothing follows the prefix).
-// A sequence without any is an ordinary decode row: merged here only when
-// its context was split, as in pa_merge_kernel.
-template <int D>
-__global__ __launch_bounds__(64) void pa_cascade_merge_kernel(CascadeMergeArgs a) {
-    constexpr int PER = D / 64;
+// prefix_partition_tokens) with the suffix pass's states over the rest; a
+// sequence without them merges its suffix partitions as pa_merge_kernel
+// does, and one with a single unshared partition was finished by the
+// suffix pass.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void pa_cascade_merge_kernel(CascadeMergeArgs a) {
+    __shared__ __align__(16) float red[merge_lds_floats<D, W>()];
     const int row = (int)blockIdx.x;  // seq * Hq + q head
     const int seq = row / a.num_q_heads;
     int ctx = a.context_lens[seq];
@@ -62,48 +47,45 @@ __global__ __launch_bounds__(64) void pa_cascade_merge_kernel(CascadeMergeArgs a
     const int npp = (shared + a.prefix_partition_tokens - 1) / a.prefix_partition_tokens;
     const int nps = (ctx - shared + a.partition_tokens - 1) / a.partition_tokens;
     if (shared == 0 && nps <= 1) return;  // the suffix pass stored the output itself
-    const int lane = (int)threadIdx.x;
-    const float* pml = a.pre_ml + (int64_t)row * a.prefix_partitions * 2;
-    const float* pmo = a.pre_o + (int64_t)row * a.prefix_partitions * D + lane * PER;
-    const float* sml = a.part_ml + (int64_t)row * a.num_partitions * 2;
-    const float* smo = a.part_o + (int64_t)row * a.num_partitions * D + lane * PER;
-    float M = -INFINITY;
-    for (int p = 0; p < npp; ++p) M = fmaxf(M, pml[2 * p]);
-    for (int p = 0; p < nps; ++p) M = fmaxf(M, sml[2 * p]);
-    float L = 0.0f;
-    float O[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) O[e] = 0.0f;
-    for (int p = 0; p < npp; ++p) {
-        const float f = state_weight(pml[2 * p], M);
-        L = fmaf(pml[2 * p + 1], f, L);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) O[e] = fmaf(pmo[(int64_t)p * D + e], f, O[e]);
-    }
-    for (int p = 0; p < nps; ++p) {
-        const float f = state_weight(sml[2 * p], M);
-        L = fmaf(sml[2 * p + 1], f, L);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) O[e] = fmaf(smo[(int64_t)p * D + e], f, O[e]);
-    }
-    uint16_t* dst = a.out + (int64_t)row * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_rne(L > 0.0f ? O[e] / L : 0.0f);
+    merge_row<D, W>(a.pre_ml + (int64_t)row * a.prefix_partitions * 2,
+                    a.pre_o + (int64_t)row * a.prefix_partitions * D, npp,
+                    a.part_ml + (int64_t)row * a.num_partitions * 2,
+                    a.part_o + (int64_t)row * a.num_partitions * D, nps, a.out + (int64_t)row * D, red);
+}
+
+template <int D, int W>
+void launch_w(const MergeArgs& a, int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL((pa_merge_kernel<D, W>), dim3((unsigned)rows), dim3(64 * W), 0, s, a);
+}
+
+template <int D, int W>
+void launch_w(const CascadeMergeArgs& a, int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL((pa_cascade_merge_kernel<D, W>), dim3((unsigned)rows), dim3(64 * W), 0, s, a);
+}
+
+template <int D, class Args>
+void launch_rows(const Args& a, int64_t rows, int waves, hipStream_t s) {
+    if (waves <= 1) launch_w<D, 1>(a, rows, s);
+    else if (waves == 2) launch_w<D, 2>(a, rows, s);
+    else if (waves == 4) launch_w<D, 4>(a, rows, s);
+    else launch_w<D, 8>(a, rows, s);
 }
 
 }  // namespace
 
 hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_q_heads));
-    if (a.head_dim == 64) hipLaunchKernelGGL(pa_cascade_merge_kernel<64>, grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL(pa_cascade_merge_kernel<128>, grid, dim3(64), 0, s, a);
+    const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+    const int w = merge_waves(a.head_dim, (int64_t)a.prefix_partitions + a.num_partitions);
+    if (a.head_dim == 64) launch_rows<64>(a, rows, w, s);
+    else launch_rows<128>(a, rows, w, s);
     return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_q_heads));
-    if (a.head_dim == 64) hipLaunchKernelGGL(pa_merge_kernel<64>, grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL(pa_merge_kernel<128>, grid, dim3(64), 0, s, a);
+    const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+    const int w = merge_waves(a.head_dim, a.num_partitions);
+    if (a.head_dim == 64) launch_rows<64>(a, rows, w, s);
+    else launch_rows<128>(a, rows, w, s);
     return hipGetLastError();
 }
 

@@ -148,6 +148,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
         off = p.items_off + align_up((size_t)S * Hkv * p.num_partitions * 4 * sizeof(int32_t), 256);
     }
     if (p.num_partitions > 1) {
+        if ((int64_t)Tq * Hq >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;  // merge grid: one workgroup per row
         const size_t prow = (size_t)Tq * Hq * p.num_partitions;
         p.partials = true;
         p.ml_off = off;
@@ -265,6 +266,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
         off = p.items_off + align_up((size_t)p.num_workgroups * 4 * sizeof(int32_t), 256);
     }
     if (p.num_partitions > 1) {
+        if ((int64_t)S * Hq >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;  // merge grid: one workgroup per row
         const size_t rows = (size_t)S * Hq * p.num_partitions;
         p.partials = true;
         p.ml_off = off;
@@ -302,6 +304,7 @@ int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
     // the suffix pass runs on the decode kernels (at most 16 query heads per KV head)
     if (p.multi) return PA_ERR_UNSUPPORTED;
     if (p.num_partitions >= 32768 || Hkv / p.heads_per_unit >= 65536) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)S * Hq >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;  // merge grid: one workgroup per row
     p.scheduled = true;
     p.partials = true;
     size_t off = kHeaderBytes;
