@@ -595,7 +595,7 @@ void launch_merge_w(const MultiArgs& a, int64_t rows, hipStream_t s) {
 template <int D>
 void launch_multi_merge(const MultiArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.num_query_rows * a.num_q_heads;
-    const int w = merge_waves(D, a.num_partitions);
+    const int w = merge_waves(D, a.num_partitions, rows);
     if (w <= 1) launch_merge_w<D, 1>(a, rows, s);
     else if (w == 2) launch_merge_w<D, 2>(a, rows, s);
     else if (w == 4) launch_merge_w<D, 4>(a, rows, s);

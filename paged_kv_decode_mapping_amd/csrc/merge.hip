@@ -75,7 +75,7 @@ void launch_rows(const Args& a, int64_t rows, int waves, hipStream_t s) {
 
 hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
-    const int w = merge_waves(a.head_dim, (int64_t)a.prefix_partitions + a.num_partitions);
+    const int w = merge_waves(a.head_dim, (int64_t)a.prefix_partitions + a.num_partitions, rows);
     if (a.head_dim == 64) launch_rows<64>(a, rows, w, s);
     else launch_rows<128>(a, rows, w, s);
     return hipGetLastError();
@@ -83,7 +83,7 @@ hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
-    const int w = merge_waves(a.head_dim, a.num_partitions);
+    const int w = merge_waves(a.head_dim, a.num_partitions, rows);
     if (a.head_dim == 64) launch_rows<64>(a, rows, w, s);
     else launch_rows<128>(a, rows, w, s);
     return hipGetLastError();

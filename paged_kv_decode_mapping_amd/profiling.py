@@ -51,11 +51,12 @@ def kernel_source_hash(plan: Optional[dict] = None) -> str:
     variants = [plan["variant"]] if plan else sorted(KERNEL_SOURCES)
     files += [KERNEL_SOURCES[v] for v in variants]
     if plan is None or plan.get("scheduled"):
-        files.append("schedule.hip")
+        files += ["schedule.hip", "pa_cascade.h"]
         structs.append("ScheduleArgs")
     if plan is None or plan.get("num_partitions", 1) > 1:
-        files.append("merge.hip")
+        files += ["merge.hip", "pa_merge.h", "pa_cascade.h"]
         structs.append("MergeArgs")
+    files = list(dict.fromkeys(files))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_decode_mapping_amd", "csrc")
     for f in files:

@@ -80,6 +80,8 @@ def test_multi_small_partitions_and_ragged_tiles(lib):
     compare(got, ref, *BF16_TOL)
     got, ref = _run("chunk_prefill", 48)
     compare(got, ref, *BF16_TOL)
+    got, ref = _run("long_bs128", 16)  # more than a hundred partitions per row: the widest merge
+    compare(got, ref, *BF16_TOL)
 
 
 def test_multi_one_token_equals_decode_oracle(lib):

@@ -79,6 +79,24 @@ def test_split_and_waves_agree_with_oracle(lib, name, partition, waves, variant)
     compare(host_bits(out), ref, *BF16_TOL)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("partitions", [2, 12, 24, 48, 100, 200])
+def test_merge_of_many_partitions(lib, D, partitions):
+    """The merge takes 1, 2, 4 or 8 waves per output row by the number of
+    partition states (at 32-token partitions these counts reach each width
+    for both head sizes, 200 takes several passes of the widest); rows
+    ending inside a partition, and a short one that is not split."""
+    P = 32
+    w = W.make_workload("mixed_batch", num_seqs=3, head_dim=D,
+                        context=("list", [partitions * P - 5, (partitions // 2) * P + 1, 7]))
+    ref = _oracle(w)
+    d = DeviceWorkload(w)
+    note(f"merge D={D} partitions={partitions}")
+    out = d.decode(partition_tokens=P, variant="mfma")
+    torch.cuda.synchronize()
+    compare(host_bits(out), ref, *BF16_TOL)
+
+
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_decode_is_deterministic(lib, variant):
     """Repeat runs are bit-identical, and the device-built schedule (items in
