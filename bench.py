@@ -171,7 +171,7 @@ def bench_graph(args, w, q, k_cache, v_cache, tables, ctx, new_k, new_v, slots, 
         pa.pa_cache_write(new_k, new_v, slots, k_cache, v_cache, k_scale, v_scale)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
                      workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                     prefetch=args.prefetch, schedule=args.schedule)
+                     prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
 
     def timed(fn, n):
         torch.cuda.synchronize()
@@ -497,6 +497,7 @@ def main() -> int:
     ap.add_argument("--check", action="store_true", help="compare sampled outputs with the oracle")
     ap.add_argument("--prefetch", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
+    ap.add_argument("--heads-per-tile", type=int, default=0, help="KV heads per MFMA tile (0 = the plan's choice)")
     ap.add_argument("--op", choices=["step", "copy_blocks", "multi", "graph", "stream", "cascade"], default="step",
                     help="step: cache write + decode (the default measurement); copy_blocks: time "
                          "pa_copy_blocks on the workload's pool; multi: time pa_decode_multi with "
@@ -571,7 +572,7 @@ def main() -> int:
     plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
                                  w.max_blocks_per_seq, pa.PA_KV_BF16 if args.kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
                                  partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                                 prefetch=args.prefetch, schedule=args.schedule)
+                                 prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
     log(f"plan {plan}")
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -589,7 +590,7 @@ def main() -> int:
             ev[1].record(stream)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
                      workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                     prefetch=args.prefetch, schedule=args.schedule)
+                     prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
         if ev is not None:
             ev[2].record(stream)
 
@@ -632,7 +633,7 @@ def main() -> int:
         units = np.random.default_rng(9).choice(s.num_seqs * s.num_kv_heads, 32, replace=False)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
                      workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                     prefetch=args.prefetch, schedule=args.schedule)
+                     prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
         got = out.cpu().view(torch.int16).numpy().view(np.uint16)
         kvd = oracle.KV_BF16 if args.kv == "bf16" else oracle.KV_FP8_E4M3FN
         if args.kv == "fp8" and kq is None:
