@@ -132,6 +132,49 @@ def test_full_size_mixed_batch_sampled(lib, schedule):
     compare(got, ref, *BF16_TOL)
 
 
+@pytest.mark.parametrize("name", ["llama7b_mha", "llama70b_gqa", "long_splitk", "mixed_batch"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_full_size_step_sampled(lib, name, kv):
+    """One step at the workload's full size, as the benchmark launches it:
+    the cache write of the step's new tokens, then the decode with the
+    library's own plan. The written rows must match the oracle's scatter
+    bit for bit; the decode is checked on a sample of (sequence, KV head)
+    units (the longest and the shortest context included) that the oracle
+    computes one by one. fp8 caches are the oracle's quantisation of the
+    whole pool (scales amax / 448)."""
+    w = W.make_workload(name)
+    s = w.spec
+    ks = vs = 1.0
+    kc, vc, kvd, tol = w.k_cache, w.v_cache, oracle.KV_BF16, BF16_TOL
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
+    d = DeviceWorkload(w, kc, vc)
+    note(f"full-size step {name} {kv} plan={pa.pa_decode_get_plan(*_sizes(w), pa.PA_KV_BF16 if kv == 'bf16' else pa.PA_KV_FP8_E4M3FN)}")
+    pa.pa_cache_write(d.new_k, d.new_v, d.slot_mapping, d.k_cache, d.v_cache, ks, vs)
+    out = host_bits(d.decode(k_scale=ks, v_scale=vs))
+    torch.cuda.synchronize()
+
+    # the host caches take the same write before the reference decode
+    oracle.cache_write(w.new_k, w.new_v, w.slot_mapping, kc, vc, kv_dtype=kvd, k_scale=ks, v_scale=vs)
+    slots = w.slot_mapping[w.slot_mapping >= 0]
+    idx = torch.from_numpy(slots).cuda()
+    for dev_cache, host_cache in ((d.k_cache, kc), (d.v_cache, vc)):
+        rows = dev_cache.view(-1, s.num_kv_heads, s.head_dim)[idx].cpu()
+        rows = rows.numpy() if kv == "fp8" else rows.view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(rows, host_cache.reshape(-1, s.num_kv_heads, s.head_dim)[slots])
+
+    rng = np.random.default_rng(11)
+    units = np.unique(np.concatenate([rng.choice(s.num_seqs * s.num_kv_heads, 24, replace=False),
+                                      [int(np.argmax(w.context_lens)) * s.num_kv_heads + s.num_kv_heads - 1,
+                                       int(np.argmin(w.context_lens)) * s.num_kv_heads]]))
+    ref = oracle.decode_workload(w, units=units, kv_dtype=kvd, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+    g = s.group
+    got = np.stack([out[u // s.num_kv_heads, (u % s.num_kv_heads) * g:(u % s.num_kv_heads + 1) * g] for u in units])
+    compare(got, ref, *tol)
+
+
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_edge_contexts(lib, variant):
     """ctx 0 (zeros), 1 (V exactly), exact multiples of the tile and block,
