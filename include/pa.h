@@ -135,7 +135,9 @@ typedef struct pa_decode_plan {
  *   k_scale,       fp8 only: finite and > 0 (ignored for bf16)
  *   v_scale
  * Pointers must be 16-byte aligned; head_dim in {64, 128}; block_size a
- * power of two in [1, 1024]. num_tokens == 0 returns PA_OK with no launch.
+ * power of two in [1, 1024]. num_tokens == 0 returns PA_OK with no launch;
+ * num_tokens * num_kv_heads * head_dim / 8 must stay below 2^32 - 256 (one
+ * launch), else PA_ERR_UNSUPPORTED.
  */
 int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                    void* k_cache, void* v_cache,

@@ -20,7 +20,6 @@
 namespace pa {
 namespace {
 
-constexpr int kCopyThreads = 256;
 constexpr int kUnroll = 8;
 
 __global__ __launch_bounds__(kCopyThreads) void pa_copy_blocks_kernel(CopyBlocksArgs a) {

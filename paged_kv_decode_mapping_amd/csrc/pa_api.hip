@@ -135,7 +135,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     p.num_partitions = (int)((cap + P - 1) / P);
     if (p.num_partitions < 1) p.num_partitions = 1;
     p.num_workgroups = (int64_t)S * Hkv * rb * p.num_partitions;
-    if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if (!pa::grid_fits(p.num_workgroups, 64 * p.waves)) return PA_ERR_UNSUPPORTED;
     // Split contexts (long or ragged ones): take items longest first from the
     // device work list. A workgroup here is one cooperative tile stream, so a
     // long item started last would stretch the launch (measured: 8 queries
@@ -148,7 +148,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
         off = p.items_off + align_up((size_t)S * Hkv * p.num_partitions * 4 * sizeof(int32_t), 256);
     }
     if (p.num_partitions > 1) {
-        if ((int64_t)Tq * Hq >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;  // merge grid: one workgroup per row
+        if (!pa::grid_fits((int64_t)Tq * Hq, 512)) return PA_ERR_UNSUPPORTED;  // merge grid: a workgroup of <= 8 waves per row
         const size_t prow = (size_t)Tq * Hq * p.num_partitions;
         p.partials = true;
         p.ml_off = off;
@@ -251,7 +251,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     p.num_partitions = (int)((cap + P - 1) / P);
     if (p.num_partitions < 1) p.num_partitions = 1;
     p.num_workgroups = units * p.num_partitions;
-    if (p.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if (!pa::grid_fits(p.num_workgroups, 64 * p.waves)) return PA_ERR_UNSUPPORTED;
     if (o.schedule < -1 || o.schedule > 1) return PA_ERR_SHAPE;
     // Device work list: by default only when contexts are split. Then most
     // (sequence, partition) pairs of a ragged batch are empty and the real
@@ -266,7 +266,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
         off = p.items_off + align_up((size_t)p.num_workgroups * 4 * sizeof(int32_t), 256);
     }
     if (p.num_partitions > 1) {
-        if ((int64_t)S * Hq >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;  // merge grid: one workgroup per row
+        if (!pa::grid_fits((int64_t)S * Hq, 512)) return PA_ERR_UNSUPPORTED;  // merge grid: a workgroup of <= 8 waves per row
         const size_t rows = (size_t)S * Hq * p.num_partitions;
         p.partials = true;
         p.ml_off = off;
@@ -304,7 +304,7 @@ int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
     // the suffix pass runs on the decode kernels (at most 16 query heads per KV head)
     if (p.multi) return PA_ERR_UNSUPPORTED;
     if (p.num_partitions >= 32768 || Hkv / p.heads_per_unit >= 65536) return PA_ERR_UNSUPPORTED;
-    if ((int64_t)S * Hq >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;  // merge grid: one workgroup per row
+    if (!pa::grid_fits((int64_t)S * Hq, 512)) return PA_ERR_UNSUPPORTED;  // merge grid: a workgroup of <= 8 waves per row
     p.scheduled = true;
     p.partials = true;
     size_t off = kHeaderBytes;
@@ -332,7 +332,7 @@ int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
         q.partition_tokens = (int)P;
         q.num_partitions = (int)((cap + P - 1) / P);
         q.num_workgroups = units * q.num_partitions;
-        if (q.num_workgroups >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+        if (!pa::grid_fits(q.num_workgroups, 64 * q.waves)) return PA_ERR_UNSUPPORTED;
         q.scheduled = false;
         q.partials = true;
         q.items_off = 0;
@@ -500,7 +500,10 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
     if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0) return PA_ERR_ALIGN;
-    if (num_tokens * num_kv_heads * (head_dim / 8) >= (int64_t(1) << 40)) return PA_ERR_SHAPE;
+    // one thread per 16-byte chunk in a single launch, whose grid counts
+    // work-items in 32 bits; divided, not multiplied, so that nothing overflows
+    const int64_t chunks_per_token = (int64_t)num_kv_heads * (head_dim / 8);
+    if (num_tokens > ((int64_t(1) << 32) - 256) / chunks_per_token) return PA_ERR_UNSUPPORTED;
     if (pa::debug_validate_enabled()) {
         const int vs = pa_check_cache_write_inputs(slot_mapping, num_tokens, block_size, num_blocks, stream);
         if (vs != PA_OK) return vs;
@@ -529,7 +532,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
     if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_UNSUPPORTED;
-    if (num_pairs >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if (!pa::grid_fits(num_pairs, pa::kCopyThreads)) return PA_ERR_UNSUPPORTED;
     if (num_pairs == 0) return PA_OK;
     if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
     if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;

@@ -147,6 +147,15 @@ struct LaunchShape {
     int heads_per_unit; // MFMA kernel: adjacent KV heads sharing one 16-row tile (1, 2 or 4)
 };
 
+// A dispatch counts its work-items in 32 bits: the plans refuse
+// (PA_ERR_UNSUPPORTED, before any launch) a grid of 2^32 work-items or more
+// rather than let it wrap.
+inline bool grid_fits(int64_t blocks, int64_t threads_per_block) {
+    return blocks >= 0 && blocks <= ((int64_t(1) << 32) - 1) / threads_per_block;
+}
+
+constexpr int kCopyThreads = 256;  // pa_copy_blocks: threads per block pair
+
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, bool fp8, const LaunchShape& ls, hipStream_t s);

@@ -156,6 +156,7 @@ def _cw(lib, **kw):
     (dict(T=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(kvd=3), -5), (dict(D=80), -3),
     (dict(bs=12), -3), (dict(k=None), -1), (dict(slots=None), -1), (dict(kc=A + 4), -4),
     (dict(slots=A + 4), -4), (dict(kvd=2, ks=-1.0), -5), (dict(kvd=2, vs=float("inf")), -5),
+    (dict(T=1 << 62, Hkv=1 << 30, D=128), -3), (dict(T=(1 << 32) // 8 // 2, Hkv=2, D=64), -3),
 ])
 def test_cache_write_rejects_bad_arguments(lib, kw, code):
     assert _cw(lib, **kw) == code
@@ -278,7 +279,7 @@ def _copy(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(n=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(kvd=5), -5), (dict(D=32), -3),
     (dict(bs=24), -3), (dict(k=None), -1), (dict(m=None), -1), (dict(v=A + 4), -4), (dict(m=A + 4), -4),
-    (dict(n=1 << 31), -3),
+    (dict(n=1 << 31), -3), (dict(n=1 << 24), -3),
 ])
 def test_copy_blocks_rejects_bad_arguments(lib, kw, code):
     assert _copy(lib, **kw) == code
@@ -294,3 +295,28 @@ def test_copy_blocks_zero_pairs_is_a_no_op(lib):
 ])
 def test_probe_rejects_bad_arguments(lib, args, code):
     assert lib.pa_probe_stream_read(*args, None) == code
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,kw", [
+    (1 << 22, 8, 8, dict()),                       # VALU, 8 waves: 2^25 workgroups x 512 threads
+    (1 << 23, 32, 8, dict(heads_per_tile=2)),      # MFMA, 4 waves: 2^25 x 256
+    (1 << 20, 4096, 4, dict(partition_tokens=-1)),  # MQA-like groups on the multi-row kernel
+])
+def test_plans_refuse_grids_beyond_32_bit_work_items(lib, S, Hq, Hkv, kw):
+    """A dispatch counts work-items in 32 bits: such plans are refused before
+    any launch instead of wrapping."""
+    kw = dict(dict(partition_tokens=-1), **kw)
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_decode_get_plan(S, Hq, Hkv, 64, 16, 7, **kw)
+    assert e.value.status == -3
+
+
+def test_split_plan_refuses_grids_beyond_32_bit_work_items(lib):
+    # 2^24 sequences x 64 heads, 2 partitions: 2^31 decode workgroups, and
+    # 2^30 merge rows of up to 512 threads each
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_decode_get_plan(1 << 24, 64, 64, 64, 16, 8, partition_tokens=64, variant="mfma", heads_per_tile=1)
+    assert e.value.status == -3
+    # the largest grids that fit are still planned
+    p = pa.pa_decode_get_plan(1 << 16, 8, 2, 64, 16, 7, partition_tokens=-1)
+    assert p["num_workgroups"] * 64 * p["waves_per_group"] < 1 << 32
