@@ -175,6 +175,37 @@ def test_full_size_step_sampled(lib, name, kv):
     compare(got, ref, *tol)
 
 
+@pytest.mark.parametrize("bs", [32, 64, 256, 1024])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_other_block_sizes(lib, bs, kv):
+    """Block sizes other than the workloads' 16 and 128 (any power of two from
+    16 to 1024 is accepted): cache write bit-exact, decode on both kernels,
+    unsplit and split, with contexts ending inside, at and just past a block."""
+    ctx = [1, 17, bs - 1, bs, bs + 1, 2 * bs + 300, 40]
+    w = W.make_workload("long_splitk", num_seqs=len(ctx), context=("list", ctx), block_size=bs)
+    ks = vs = 1.0
+    kc, vc, kvd, tol = w.k_cache, w.v_cache, oracle.KV_BF16, BF16_TOL
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
+    d = DeviceWorkload(w, kc, vc)
+    note(f"block size {bs} {kv}: cache write")
+    pa.pa_cache_write(d.new_k, d.new_v, d.slot_mapping, d.k_cache, d.v_cache, ks, vs)
+    torch.cuda.synchronize()
+    oracle.cache_write(w.new_k, w.new_v, w.slot_mapping, kc, vc, kv_dtype=kvd, k_scale=ks, v_scale=vs)
+    for dev_cache, host_cache in ((d.k_cache, kc), (d.v_cache, vc)):
+        got = dev_cache.cpu().numpy() if kv == "fp8" else host_bits(dev_cache)
+        assert np.array_equal(got, host_cache)
+    ref = _oracle(w, kv_dtype=kvd, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+    for variant in ("valu", "mfma"):
+        for part in (-1, 48, 512):
+            note(f"block size {bs} {kv} {variant} partition={part}")
+            got = host_bits(d.decode(k_scale=ks, v_scale=vs, variant=variant, partition_tokens=part))
+            torch.cuda.synchronize()
+            compare(got, ref, *tol)
+
+
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_edge_contexts(lib, variant):
     """ctx 0 (zeros), 1 (V exactly), exact multiples of the tile and block,
