@@ -206,6 +206,40 @@ def test_other_block_sizes(lib, bs, kv):
             compare(got, ref, *tol)
 
 
+@pytest.mark.parametrize("g", [2, 3, 5, 6, 7, 12, 16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_group_sizes(lib, g, D, kv):
+    """GQA groups the named workloads do not have, powers of two or not: every
+    kernel and packing that takes the shape (the VALU kernel up to 4 query
+    heads per KV head, the matrix kernel up to 16, two KV heads per tile up
+    to 8), unsplit and split."""
+    Hkv = 4
+    ctx = [1, 33, 200, 517, 1000]
+    w = W.make_workload("tiny", num_seqs=len(ctx), context=("list", ctx), num_q_heads=g * Hkv,
+                        num_kv_heads=Hkv, head_dim=D)
+    ks = vs = 1.0
+    kc, vc, kvd, tol = w.k_cache, w.v_cache, oracle.KV_BF16, BF16_TOL
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
+    ref = _oracle(w, kv_dtype=kvd, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+    d = DeviceWorkload(w, kc, vc)
+    shapes = [dict(variant="auto")]
+    if g <= 4:
+        shapes.append(dict(variant="valu"))
+    shapes.append(dict(variant="mfma", heads_per_tile=1))
+    if g <= 8:
+        shapes.append(dict(variant="mfma", heads_per_tile=2))
+    for opts in shapes:
+        for part in (-1, 48):
+            note(f"group {g} D {D} {kv} {opts} partition={part}")
+            got = host_bits(d.decode(k_scale=ks, v_scale=vs, partition_tokens=part, **opts))
+            torch.cuda.synchronize()
+            compare(got, ref, *tol)
+
+
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_edge_contexts(lib, variant):
     """ctx 0 (zeros), 1 (V exactly), exact multiples of the tile and block,
