@@ -240,6 +240,37 @@ def test_group_sizes(lib, g, D, kv):
             compare(got, ref, *tol)
 
 
+@pytest.mark.parametrize("g", [1, 8])
+@pytest.mark.parametrize("scale", [0.0, 1.0, 8.0, 64.0])
+def test_extreme_logits_and_a_moving_max(lib, g, scale):
+    """The online softmax under stress: scores up to a few thousand (a nearly
+    one-hot softmax), scale 0 (the mean of V), and for the first query head
+    of every group keys aligned with its query and growing with the position,
+    so that its running maximum moves on every tile and every rescale path
+    runs. Both kernels where they apply, unsplit and split."""
+    Hkv, D = 4, 128
+    ctx = [1, 16, 17, 300, 1000]
+    w = W.make_workload("tiny", num_seqs=len(ctx), context=("list", ctx), num_q_heads=g * Hkv,
+                        num_kv_heads=Hkv, head_dim=D)
+    kc = w.k_cache.copy()
+    q32 = W.bf16_bits_to_f32(w.q)
+    bs = w.spec.block_size
+    for i, L in enumerate(ctx):
+        for j in range(L):
+            b, o = w.block_tables[i, j // bs], j % bs
+            for h in range(Hkv):
+                kc[b, o, h] = W._to_bf16_bits(q32[i, h * g] * np.float32(0.5 * (j + 1) / L))
+    ref = oracle.decode(w.q, kc, w.v_cache, w.block_tables, w.context_lens, scale)
+    d = DeviceWorkload(w, kc, w.v_cache)
+    for variant in (["valu", "mfma"] if g <= 4 else ["mfma"]):
+        for part in (-1, 48):
+            note(f"extreme logits g={g} scale={scale} {variant} partition={part}")
+            got = host_bits(pa.pa_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, scale,
+                                         variant=variant, partition_tokens=part))
+            torch.cuda.synchronize()
+            compare(got, ref, *BF16_TOL)
+
+
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 def test_edge_contexts(lib, variant):
     """ctx 0 (zeros), 1 (V exactly), exact multiples of the tile and block,
