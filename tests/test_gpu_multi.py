@@ -35,6 +35,13 @@ CASES = {
     "mha_multi": ("llama7b_mha", dict(num_seqs=3, context=("list", [512, 1000, 33])), [6, 2, 33]),
     # 128 rows per KV head: one 8-wave workgroup
     "verify16_70b": ("llama70b_gqa", dict(num_seqs=2, context=("list", [300, 2000])), [16, 9]),
+    # groups and block sizes the named workloads do not have
+    "g3_bs32": ("tiny", dict(num_seqs=3, context=("list", [40, 300, 1000]), num_q_heads=12, num_kv_heads=4,
+                             head_dim=128, block_size=32), [3, 7, 16]),
+    "g12_bs1024": ("long_splitk", dict(num_seqs=2, context=("list", [1100, 2500]), num_q_heads=96, block_size=1024),
+                   [5, 16]),
+    "g6_d64_bs64": ("tiny", dict(num_seqs=3, context=("list", [64, 65, 500]), num_q_heads=12, num_kv_heads=2,
+                                 block_size=64), [1, 11, 4]),
 }
 
 
@@ -67,7 +74,8 @@ def test_multi_matches_oracle(lib, name, partition):
     compare(got, ref, *BF16_TOL)
 
 
-@pytest.mark.parametrize("name", ["spec_verify_mixed", "long_bs128", "verify16_70b", "chunk_prefill"])
+@pytest.mark.parametrize("name", ["spec_verify_mixed", "long_bs128", "verify16_70b", "chunk_prefill",
+                                  "g3_bs32", "g12_bs1024", "g6_d64_bs64"])
 def test_multi_fp8_matches_oracle(lib, name):
     got, ref = _run(name, 0, "fp8")
     compare(got, ref, *FP8_TOL)
