@@ -49,13 +49,23 @@ def _step_inputs(w, n_real, step):
 
 
 @pytest.mark.parametrize("partition", [-1, 64])
-def test_captured_step_replays_match_eager(lib, partition):
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_captured_step_replays_match_eager(lib, partition, kv):
     w = W.make_workload("mixed_batch", num_seqs=12,
                         context=("list", [16, 100, 511, 512, 513, 900, 1000, 40, 2000, 77, 300, 1]))
     s = w.spec
     n_real = 10
     dev = torch.device("cuda")
-    kc_g, vc_g = dev_bf16(w.k_cache), dev_bf16(w.v_cache)   # the graph's caches
+    ks = vs = 1.0
+    kc0, vc0 = w.k_cache, w.v_cache
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc0, vc0 = oracle.quantize_pool(kc0, ks), oracle.quantize_pool(vc0, vs)
+
+    def dev_cache(a):
+        return torch.from_numpy(a).cuda() if kv == "fp8" else dev_bf16(a)
+
+    kc_g, vc_g = dev_cache(kc0), dev_cache(vc0)   # the graph's caches
     kc_e, vc_e = kc_g.clone(), vc_g.clone()                 # the eager reference's caches
     S, MB = BUCKET, w.max_blocks_per_seq
     st_q = torch.zeros((S, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device=dev)
@@ -65,7 +75,8 @@ def test_captured_step_replays_match_eager(lib, partition):
     st_nk = torch.zeros((S, s.num_kv_heads, s.head_dim), dtype=torch.bfloat16, device=dev)
     st_nv = torch.zeros_like(st_nk)
     st_out = torch.zeros_like(st_q)
-    need = pa.pa_decode_workspace_size(S, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, MB,
+    kvd = pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN
+    need = pa.pa_decode_workspace_size(S, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, MB, kvd,
                                        partition_tokens=partition)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
@@ -80,8 +91,9 @@ def test_captured_step_replays_match_eager(lib, partition):
         return ctx, tables, q, slots, nk, nv
 
     def step_on(kc, vc, out):
-        pa.pa_cache_write(st_nk, st_nv, st_slots, kc, vc)
-        pa.pa_decode(st_q, kc, vc, st_tab, st_ctx, w.scale, out, workspace=ws, partition_tokens=partition)
+        pa.pa_cache_write(st_nk, st_nv, st_slots, kc, vc, ks, vs)
+        pa.pa_decode(st_q, kc, vc, st_tab, st_ctx, w.scale, out, workspace=ws, partition_tokens=partition,
+                     k_scale=ks, v_scale=vs)
 
     # warm up on a side stream (as torch asks before capture), on scratch caches
     load(0)
@@ -115,6 +127,12 @@ def test_captured_step_replays_match_eager(lib, partition):
         assert torch.equal(vc_g.view(torch.int16), vc_e.view(torch.int16))
         assert np.all(got[n_real:] == 0)  # padding sequences
         if step == 2:
-            kh, vh = host_bits(kc_g), host_bits(vc_g)
-            ref = oracle.decode(q, kh, vh, tables, ctx, w.scale)
-            compare(got, ref, 1e-2, 1e-3)
+            if kv == "fp8":
+                kh, vh = kc_g.cpu().numpy(), vc_g.cpu().numpy()
+                ref = oracle.decode(q, kh, vh, tables, ctx, w.scale, kv_dtype=oracle.KV_FP8_E4M3FN,
+                                    k_scale=ks, v_scale=vs)
+                compare(got, ref, 5e-2, 5e-3)
+            else:
+                kh, vh = host_bits(kc_g), host_bits(vc_g)
+                ref = oracle.decode(q, kh, vh, tables, ctx, w.scale)
+                compare(got, ref, 1e-2, 1e-3)
