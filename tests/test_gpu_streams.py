@@ -2,11 +2,12 @@
 the work-list builder, the decode kernel and the merge of a split decode)
 goes to the stream the caller names, not to the current or default stream.
 
-The named stream is held back behind an event that another stream records
-after a bounded spin kernel; a copy of the output taken meanwhile on a third
-stream, ordered after the current stream, must still show the sentinel the
-output was filled with, and once the named stream drains the output must
-match the oracle.
+A graph capture is begun on a side stream, the current stream is set back to
+the default one, and the calls are made naming the side stream. Work on the
+named stream is captured, not run: after the capture the output must still
+hold the sentinel it was filled with (a launch on any other stream would
+have run at once, or failed while the side stream captures). Replaying the
+graph must then give the oracle's result.
 """
 import numpy as np
 import pytest
@@ -20,8 +21,7 @@ from _gpu_util import DeviceWorkload, compare, host_bits, note
 
 pytestmark = pytest.mark.gpu
 
-SPIN_CYCLES = 50_000_000  # one spinning wave: tens of milliseconds, bounded
-SENTINEL = 0x7FC1         # a bf16 NaN pattern that a decode never stores
+SENTINEL = 0x7FC1  # a bf16 NaN pattern that a decode never stores
 
 
 @pytest.fixture(scope="module")
@@ -42,31 +42,35 @@ def test_launches_follow_the_given_stream(lib, partition):
     need = pa.pa_decode_workspace_size(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
                                        w.max_blocks_per_seq, partition_tokens=partition)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
-    out = torch.full(tuple(d.q.shape), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    torch.cuda.synchronize()
+    out = torch.empty(tuple(d.q.shape), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
 
-    blocker, side, probe = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
-    gate = torch.cuda.Event()
-    with torch.cuda.stream(blocker):
-        torch.cuda._sleep(SPIN_CYCLES)
-        gate.record(blocker)
-    side.wait_event(gate)
-    note(f"stream argument: write + decode on a gated side stream, partition={partition}")
-    pa.pa_cache_write(d.new_k, d.new_v, d.slot_mapping, d.k_cache, d.v_cache, stream=side)
-    pa.pa_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, w.scale, out, workspace=ws,
-                 partition_tokens=partition, stream=side)
-    # ordered after the current (default) stream, not after `side`: a launch
-    # that went to the current stream instead would be complete by then
-    probe.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(probe):
-        early = out.clone()
-        done = torch.cuda.Event()
-        done.record(probe)
-    done.synchronize()
+    def calls():
+        pa.pa_cache_write(d.new_k, d.new_v, d.slot_mapping, d.k_cache, d.v_cache, stream=side)
+        pa.pa_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, w.scale, out, workspace=ws,
+                     partition_tokens=partition, stream=side)
+
+    # warm-up on the side stream (the new tokens go to free slots, so
+    # writing them twice changes nothing the decode reads)
+    side.wait_stream(torch.cuda.current_stream())
+    calls()
     side.synchronize()
-    torch.cuda.synchronize()
 
-    assert np.all(host_bits(early) == SENTINEL), "a launch ran before the stream it was given was released"
+    out.view(torch.int16).fill_(SENTINEL)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note(f"stream argument: calls naming a capturing side stream, partition={partition}")
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+    assert torch.cuda.current_stream() != side
+    calls()  # the current stream is not the side stream here
+    with torch.cuda.stream(side):
+        graph.capture_end()
+    torch.cuda.synchronize()
+    assert np.all(host_bits(out) == SENTINEL), "a launch did not go to the stream it was given"
+
+    graph.replay()
+    torch.cuda.synchronize()
     compare(host_bits(out), ref, 1e-2, 1e-3)
     rows = d.k_cache.view(-1, s.num_kv_heads, s.head_dim)[d.slot_mapping].cpu().view(torch.int16).numpy()
     assert np.array_equal(rows.view(np.uint16), kc_h.reshape(-1, s.num_kv_heads, s.head_dim)[w.slot_mapping])
