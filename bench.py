@@ -230,8 +230,7 @@ def bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b: int, k_scale: floa
     qs = torch.from_numpy(mq.query_start).to(dev)
     maxq = int(qlens.max())
     kvd = pa.PA_KV_BF16 if kv_b == 2 else pa.PA_KV_FP8_E4M3FN
-    need = pa.pa_decode_multi_workspace_size(s.num_seqs, mq.num_tokens, maxq, s.num_q_heads, s.num_kv_heads,
-                                             s.head_dim, s.block_size, w.max_blocks_per_seq, kvd, args.partition)
+    need = pa.pa_decode_multi_workspace_size(q, k_cache, tables, maxq, args.partition)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
 
@@ -318,12 +317,10 @@ def bench_cascade(args, w, k_cache, v_cache, kv_b: int, k_scale: float, v_scale:
     plen = torch.from_numpy(b.prefix_lens).to(dev)
     gst = torch.from_numpy(b.group_start).to(dev)
     kvd = pa.PA_KV_BF16 if kv_b == 2 else pa.PA_KV_FP8_E4M3FN
-    need = pa.pa_decode_cascade_workspace_size(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
-                                               w.max_blocks_per_seq, b.num_groups, b.max_group_size,
-                                               b.prefix_tables.shape[1], kvd, partition_tokens=args.partition)
+    need = pa.pa_decode_cascade_workspace_size(q, k_cache, tables, ptab, b.max_group_size,
+                                               partition_tokens=args.partition)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
-                                 w.max_blocks_per_seq, kvd, partition_tokens=args.partition)
+    plan = pa.pa_decode_get_plan(q, k_cache, tables, partition_tokens=args.partition)
     ws_d = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     out_d = torch.empty_like(q)
@@ -493,6 +490,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama70b_gqa")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16")
+    ap.add_argument("--layout", choices=["page", "head_major"], default="page",
+                    help="pool layout: the page's [block, row, KV head, d] order, or head-major "
+                         "[block, KV head, row, d] passed through strides")
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
@@ -564,6 +564,15 @@ def main() -> int:
         k_cache, v_cache = kc8, vc8
         if not args.no_cpu_baseline:
             kq, vq = kc8.cpu().numpy(), vc8.cpu().numpy()
+    if args.layout == "head_major":
+        # the same logical pool stored [N, Hkv, bs, D]: each (block, KV head)
+        # tile is one contiguous run; passed as the permuted [N, bs, Hkv, D] view
+        def to_head_major(t):
+            hm = torch.empty((t.shape[0], t.shape[2], t.shape[1], t.shape[3]), dtype=t.dtype, device=dev)
+            hm.copy_(t.permute(0, 2, 1, 3))
+            return hm.permute(0, 2, 1, 3)
+        k_cache, v_cache = to_head_major(k_cache), to_head_major(v_cache)
+        torch.cuda.synchronize()
     kv_b = 2 if args.kv == "bf16" else 1
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, w, k_cache, v_cache, kv_b, kq, vq)
@@ -571,8 +580,7 @@ def main() -> int:
         return bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b, k_scale, v_scale, kq, vq)
     if args.op == "cascade":
         return bench_cascade(args, w, k_cache, v_cache, kv_b, k_scale, v_scale, kq, vq)
-    plan = pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
-                                 w.max_blocks_per_seq, pa.PA_KV_BF16 if args.kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
+    plan = pa.pa_decode_get_plan(q, k_cache, tables,
                                  partition_tokens=args.partition, variant=args.variant, waves=args.waves,
                                  prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
     log(f"plan {plan}")
@@ -657,7 +665,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": f"{s.name}: {s.description}",
-            "kv_cache": args.kv,
+            "kv_cache": args.kv, "layout": args.layout,
             "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
             "head_dim": s.head_dim, "block_size": s.block_size,
             "context_tokens": int(w.context_lens.sum()), "new_tokens": int(len(w.slot_mapping)),

@@ -6,10 +6,12 @@
 // index block * block_size + offset. For an fp8 cache every element becomes
 // the e4m3fn code of x / scale (Tutorial §3.1 "量化基础", symmetric_quantize).
 //
-// One thread moves one 16-byte chunk (8 elements) of one (token, KV head)
-// row of K and the same chunk of V; consecutive threads cover consecutive
-// chunks, so the loads are fully coalesced and each destination row is
-// written by D / 8 neighbouring threads.
+// One thread moves one 8-element chunk of one (token, KV head) row of K and
+// the same chunk of V (16 bytes read; 16 bytes written for bf16, 8 for fp8);
+// consecutive threads cover consecutive chunks of a row, so each source and
+// destination row is read and written by D / 8 neighbouring threads. Source
+// rows and cache rows are addressed through their strides (any layout of
+// the pool: the page's [block, row, KV head, d] order or a head-major one).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -18,20 +20,25 @@ namespace {
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteArgs a) {
+    constexpr int ESZ = FP8 ? 1 : 2;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int chunks_per_row = a.head_dim / 8;
     const int64_t per_token = (int64_t)a.num_kv_heads * chunks_per_row;
     if (gid >= a.num_tokens * per_token) return;
     const int64_t t = gid / per_token;
-    const int64_t rem = gid - t * per_token;
+    const int h = (int)((gid - t * per_token) / chunks_per_row);
+    const int ch = (int)(gid - t * per_token - (int64_t)h * chunks_per_row);
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0 || slot >= a.num_slots) return;  // padding, or outside the pool
-    const int64_t dst = slot * per_token + rem;   // in 8-element chunks
-    const u32x4 kw = reinterpret_cast<const u32x4*>(a.k)[gid];
-    const u32x4 vw = reinterpret_cast<const u32x4*>(a.v)[gid];
+    const int64_t blk = slot >> a.block_size_log2;
+    const uint32_t row = (uint32_t)(slot & ((1 << a.block_size_log2) - 1));
+    // byte offset of this 8-element chunk in the caches
+    const int64_t dst = blk * a.cache.block + (int64_t)row * a.cache.token + (int64_t)h * a.cache.head + ch * 8 * ESZ;
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(a.k + t * a.k_token + (int64_t)h * a.k_head + 8 * ch);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v + t * a.v_token + (int64_t)h * a.v_head + 8 * ch);
     if constexpr (!FP8) {
-        reinterpret_cast<u32x4*>(a.k_cache)[dst] = kw;
-        reinterpret_cast<u32x4*>(a.v_cache)[dst] = vw;
+        *reinterpret_cast<u32x4*>(a.k_cache + dst) = kw;
+        *reinterpret_cast<u32x4*>(a.v_cache + dst) = vw;
     } else {
         u32x2 kc, vc;
 #pragma unroll
@@ -50,8 +57,8 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteArgs a) {
             kc[i] = kk;
             vc[i] = vv;
         }
-        reinterpret_cast<u32x2*>(a.k_cache)[dst] = kc;
-        reinterpret_cast<u32x2*>(a.v_cache)[dst] = vc;
+        *reinterpret_cast<u32x2*>(a.k_cache + dst) = kc;
+        *reinterpret_cast<u32x2*>(a.v_cache + dst) = vc;
     }
 }
 

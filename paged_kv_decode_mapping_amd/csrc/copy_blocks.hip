@@ -9,7 +9,9 @@
 // duplication: for each (src, dst) pair, block dst of K and of V becomes a
 // byte-for-byte copy of block src (all rows, all KV heads).
 //
-// Workgroup p copies pair p's block in both caches: each thread moves
+// A block is one contiguous byte range (the block dimension outermost in
+// memory, whatever the order of the other three). Workgroup p copies pair
+// p's block in both caches: each thread moves
 // 16-byte chunks t, t + 256, ..., issuing kUnroll loads of K and of V before
 // their stores so that enough bytes are in flight. The data is read once and
 // written once, so loads and stores are marked non-temporal. Pairs with a
@@ -28,10 +30,10 @@ __global__ __launch_bounds__(kCopyThreads) void pa_copy_blocks_kernel(CopyBlocks
     const int64_t dst = a.pairs[2 * p + 1];
     if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks) return;
     const int64_t chunks = a.block_bytes / 16;
-    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k_cache + src * a.block_bytes);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_cache + src * a.block_bytes);
-    u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + dst * a.block_bytes);
-    u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + dst * a.block_bytes);
+    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k_cache + src * a.block_stride);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_cache + src * a.block_stride);
+    u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + dst * a.block_stride);
+    u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + dst * a.block_stride);
     for (int64_t base = threadIdx.x; base < chunks; base += (int64_t)kUnroll * kCopyThreads) {
         u32x4 k[kUnroll], v[kUnroll];
 #pragma unroll

@@ -115,8 +115,8 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             const int qi = col % TPH;
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
             if (qi < g)
-                w = *reinterpret_cast<const u32x4*>(
-                    a.q + ((int64_t)wi.seq * a.num_q_heads + (kvh0 + col / TPH) * g + qi) * D + 8 * d8);
+                w = *reinterpret_cast<const u32x4*>(a.q + (int64_t)wi.seq * a.q_seq +
+                                                    (int64_t)((kvh0 + col / TPH) * g + qi) * a.q_head + 8 * d8);
             *reinterpret_cast<u32x4*>(qs + col * RS + 8 * d8) = w;
         }
         __syncthreads();
@@ -130,13 +130,16 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
 
         const int span = wi.t_end - wi.t_begin;
         const int ntiles = span > 0 ? (span + TPH - 1) / TPH : 0;
-        const uint32_t head_off = (uint32_t)kvh0 * a.head_bytes;
+        // The unit's first KV head is folded into each tile's descriptor base,
+        // so a row's bytes start at a multiple of the row stride from it
+        // (with HP > 1 the HP heads of a row are adjacent in memory).
+        const int64_t head_off = (int64_t)kvh0 * a.cache.head;
         // per-lane byte offset inside a tile (the same for K and V), fixed for
         // the whole item: load i of lane l covers token i * RPI + l / LPC,
         // bytes 16 (l % LPC) of its HP-head chunk; the i * RPI tokens go into
         // the wave-uniform offset
-        const uint32_t roff = (uint32_t)(lane / LPC) * a.slot_bytes + head_off + 16u * (uint32_t)(lane % LPC);
-        const uint32_t rstep = (uint32_t)RPI * a.slot_bytes;
+        const uint32_t roff = (uint32_t)(lane / LPC) * a.cache.token + 16u * (uint32_t)(lane % LPC);
+        const uint32_t rstep = (uint32_t)RPI * a.cache.token;
         const int bs_mask = (1 << a.block_size_log2) - 1;
         const float qk = a.qk_scale_log2;
 
@@ -156,11 +159,12 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         auto issue = [&](int t, int64_t blk, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
             const bool live = t < t_stop;
             const int t0 = wi.t_begin + (live ? t : t_stop - 1) * TPH;
-            const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
+            const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.cache.token;
             const int valid = min(wi.t_end - t0, TPH);
-            const uint32_t nbytes = live ? row0 + (uint32_t)valid * a.slot_bytes : 0u;
-            const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
-            const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
+            const uint32_t nbytes = live ? row0 + (uint32_t)valid * a.cache.token : 0u;
+            const int64_t base = blk * a.cache.block + head_off;
+            const auto rk = make_rsrc(a.k_cache + base, nbytes);
+            const auto rv = make_rsrc(a.v_cache + base, nbytes);
 #pragma unroll
             for (int i = 0; i < NI; ++i) kb[i] = buf_load_b128_stream(rk, roff, row0 + i * rstep);
 #pragma unroll

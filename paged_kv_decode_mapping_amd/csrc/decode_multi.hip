@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     // kernels do, made every iteration here wait for a load issued one
     // iteration earlier: all waves of a workgroup step through the tiles
     // together, so nothing hid that wait.) They go out before the query rows.
-    const auto tab_rsrc = make_rsrc(a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq,
+    const auto tab_rsrc = make_rsrc(a.block_tables + (int64_t)it.seq * a.table_stride,
                                     (uint32_t)a.max_blocks_per_seq * 4u);
     const int e_last = (t_begin + max(ntiles - 1, 0) * kTile) >> a.block_size_log2;
     auto table_load = [&](int base) {
@@ -240,7 +240,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         qv[k] = u32x4{0u, 0u, 0u, 0u};
         if (rho < rows) {
             const int r = rho / g, hh = rho - (rho / g) * g;
-            qv[k] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh) * D + 8 * d8);
+            qv[k] = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(it.q0 + r) * a.q_row +
+                                                    (int64_t)(it.kvh * g + hh) * a.q_head + 8 * d8);
         }
     }
 
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
 #pragma unroll
     for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint32_t head_off = (uint32_t)it.kvh * a.head_bytes;
+    const int64_t head_off = (int64_t)it.kvh * a.cache.head;  // folded into each tile's descriptor base
     const int bs_mask = (1 << a.block_size_log2) - 1;
     const float qk = a.qk_scale_log2;
 
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         const int kk = own ? k : 0;
         cid[i] = kk;
         // a lane past the tile's chunks reads past every descriptor (zeros)
-        coff[i] = own ? (uint32_t)(kk / LPR) * a.slot_bytes + head_off + 16u * (uint32_t)(kk % LPR) : 0x7fffffffu;
+        coff[i] = own ? (uint32_t)(kk / LPR) * a.cache.token + 16u * (uint32_t)(kk % LPR) : 0x7fffffffu;
     }
     const int nslots = (ntiles + TPS - 1) / TPS;
 
@@ -345,11 +346,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
                 __builtin_amdgcn_sched_barrier(0);
                 const bool live = t < ntiles;
                 const int t0 = t_begin + (live ? t : ntiles - 1) * kTile;
-                const uint32_t rowb = (uint32_t)(t0 & bs_mask) * a.slot_bytes;
+                const uint32_t rowb = (uint32_t)(t0 & bs_mask) * a.cache.token;
                 const int valid = min(t_end - t0, kTile);
-                const uint32_t nbytes = live ? rowb + (uint32_t)valid * a.slot_bytes : 0u;
-                const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
-                const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
+                const uint32_t nbytes = live ? rowb + (uint32_t)valid * a.cache.token : 0u;
+                const int64_t base = blk * a.cache.block + head_off;
+                const auto rk = make_rsrc(a.k_cache + base, nbytes);
+                const auto rv = make_rsrc(a.v_cache + base, nbytes);
                 kr[i] = buf_load_b128_stream(rk, coff[i], rowb);
                 vr[i] = buf_load_b128_stream(rv, coff[i], rowb);
             }
@@ -528,12 +530,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     const int r = my_rho / g, hh = my_rho - (my_rho / g) * g;
     const int64_t row = (int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh;
     if (a.num_partitions == 1 && !prefix_pass) {
+        uint16_t* dst = a.out + (int64_t)(it.q0 + r) * a.out_row + (int64_t)(it.kvh * g + hh) * a.out_head;
         const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
 #pragma unroll
         for (int j = 0; j < NPV; ++j) {
             const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[j][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[j][1] * inv) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[j][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[j][3] * inv) << 16);
-            *reinterpret_cast<u32x2*>(a.out + row * D + 16 * j + 4 * gq) = u32x2{lo, hi};
+            *reinterpret_cast<u32x2*>(dst + 16 * j + 4 * gq) = u32x2{lo, hi};
         }
     } else {
         const int64_t prow = row * a.num_partitions + it.part;
@@ -583,8 +586,9 @@ __global__ __launch_bounds__(64 * W) void pa_multi_merge_kernel(MultiArgs a) {
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int pos = L - n + r;
     const int np = pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
+    const int head = (int)(wid - (int64_t)qrow * a.num_q_heads);
     merge_row<D, W>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np,
-                    nullptr, nullptr, 0, a.out + wid * D, red);
+                    nullptr, nullptr, 0, a.out + (int64_t)qrow * a.out_row + (int64_t)head * a.out_head, red);
 }
 
 template <int D, int W>

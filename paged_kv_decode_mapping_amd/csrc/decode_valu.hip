@@ -79,7 +79,7 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
             if (h < g) {
-                const uint16_t* qp = a.q + ((int64_t)wi.seq * a.num_q_heads + wi.kvh * g + h) * D + c * EPL;
+                const uint16_t* qp = a.q + (int64_t)wi.seq * a.q_seq + (int64_t)(wi.kvh * g + h) * a.q_head + c * EPL;
 #pragma unroll
                 for (int e = 0; e < EPL; e += 8) {
                     const u32x4 w = *reinterpret_cast<const u32x4*>(qp + e);
@@ -106,11 +106,12 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
 
         const int span = wi.t_end - wi.t_begin;
         const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;
-        // per-lane byte offsets inside a tile, fixed for the whole item
+        // per-lane byte offsets inside a tile, fixed for the whole item; the
+        // KV head is folded into each tile's descriptor base
         uint32_t lane_off[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            lane_off[i] = (uint32_t)(i * RPI + r_in) * a.slot_bytes + (uint32_t)wi.kvh * a.head_bytes + (uint32_t)c * 16u;
+        for (int i = 0; i < NI; ++i) lane_off[i] = (uint32_t)(i * RPI + r_in) * a.cache.token + (uint32_t)c * 16u;
+        const int64_t head_off = (int64_t)wi.kvh * a.cache.head;
         const int bs_mask = (1 << a.block_size_log2) - 1;
         const float qk = a.qk_scale_log2;
 
@@ -128,10 +129,11 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
             // the descriptor ends at the tile's last valid row: rows past the
             // context read as zero, so V needs no masking code
             const int valid = min(wi.t_end - t0, kTile);
-            const uint32_t nbytes = live ? (row0 + (uint32_t)valid) * a.slot_bytes : 0u;
-            const auto rk = make_rsrc(a.k_cache + blk * a.block_bytes, nbytes);
-            const auto rv = make_rsrc(a.v_cache + blk * a.block_bytes, nbytes);
-            const uint32_t soff = row0 * a.slot_bytes;
+            const uint32_t nbytes = live ? (row0 + (uint32_t)valid) * a.cache.token : 0u;
+            const int64_t base = blk * a.cache.block + head_off;
+            const auto rk = make_rsrc(a.k_cache + base, nbytes);
+            const auto rv = make_rsrc(a.v_cache + base, nbytes);
+            const uint32_t soff = row0 * a.cache.token;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 kb[i] = buf_load_b128_stream(rk, lane_off[i], soff);

@@ -21,13 +21,15 @@ __global__ __launch_bounds__(64 * W) void pa_merge_kernel(MergeArgs a) {
     __shared__ __align__(16) float red[merge_lds_floats<D, W>()];
     const int row = (int)blockIdx.x;  // seq * Hq + q head
     const int seq = row / a.num_q_heads;
+    const int head = row - seq * a.num_q_heads;
     int ctx = a.context_lens[seq];
     ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
     const int np = (ctx + a.partition_tokens - 1) / a.partition_tokens;
     if (np <= 1) return;  // the decode kernel stored the output itself
     const float* ml = a.part_ml + (int64_t)row * a.num_partitions * 2;
     const float* po = a.part_o + (int64_t)row * a.num_partitions * D;
-    merge_row<D, W>(ml, po, np, nullptr, nullptr, 0, a.out + (int64_t)row * D, red);
+    merge_row<D, W>(ml, po, np, nullptr, nullptr, 0, a.out + (int64_t)seq * a.out_seq + (int64_t)head * a.out_head,
+                    red);
 }
 
 // Cascade merge: one workgroup per (sequence, query head). A sequence with
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(64 * W) void pa_cascade_merge_kernel(CascadeMergeAr
     __shared__ __align__(16) float red[merge_lds_floats<D, W>()];
     const int row = (int)blockIdx.x;  // seq * Hq + q head
     const int seq = row / a.num_q_heads;
+    const int head = row - seq * a.num_q_heads;
     int ctx = a.context_lens[seq];
     ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
     const int shared = cascade_shared(a.cascade, seq, ctx, a.block_size_log2);
@@ -50,7 +53,8 @@ __global__ __launch_bounds__(64 * W) void pa_cascade_merge_kernel(CascadeMergeAr
     merge_row<D, W>(a.pre_ml + (int64_t)row * a.prefix_partitions * 2,
                     a.pre_o + (int64_t)row * a.prefix_partitions * D, npp,
                     a.part_ml + (int64_t)row * a.num_partitions * 2,
-                    a.part_o + (int64_t)row * a.num_partitions * D, nps, a.out + (int64_t)row * D, red);
+                    a.part_o + (int64_t)row * a.num_partitions * D, nps,
+                    a.out + (int64_t)seq * a.out_seq + (int64_t)head * a.out_head, red);
 }
 
 template <int D, int W>

@@ -1,6 +1,7 @@
 // pa_api.hip -- the C ABI of libpa: argument checks, launch planning and
 // kernel dispatch. Host code only; nothing here reads device memory or
 // synchronises (unless PA_DEBUG_VALIDATE asks for the checks of validate.hip).
+// The pa_tensor arguments are read by pa_abi.h.
 //
 // Pages cited (titles as printed at the top of each page):
 //   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
@@ -10,9 +11,8 @@
 #include <cmath>
 #include <cstring>
 
-#include "../../include/pa.h"
+#include "pa_abi.h"
 #include "pa_device.h"
-#include "pa_internal.h"
 
 namespace {
 
@@ -34,13 +34,8 @@ int current_cu_count() {
     return n;
 }
 
-bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
-int log2i(int64_t x) {
-    int r = 0;
-    while ((int64_t(1) << r) < x) ++r;
-    return r;
-}
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+using pa::abi::is_pow2;
+using pa::abi::log2i;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
@@ -66,13 +61,11 @@ int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32
                 int32_t kv_dtype) {
     if (S < 0 || Hq <= 0 || Hkv <= 0 || MB <= 0 || bs <= 0 || D <= 0) return PA_ERR_SHAPE;
     if (Hq % Hkv != 0) return PA_ERR_SHAPE;
-    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
+    if (kv_dtype != PA_DTYPE_BF16 && kv_dtype != PA_DTYPE_FP8_E4M3FN) return PA_ERR_DTYPE;
     if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
     if (g > 1024) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(bs) || bs < pa::kTile || bs > 1024) return PA_ERR_UNSUPPORTED;
-    const int64_t esz = kv_dtype == PA_KV_BF16 ? 2 : 1;
-    if ((int64_t)bs * Hkv * D * esz >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
     if ((int64_t)MB * bs >= (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -160,8 +153,10 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     return PA_OK;
 }
 
+// heads_adjacent: a token row's KV heads are one contiguous run (the head
+// stride is head_dim), which packing several KV heads into a tile needs.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB, int32_t kv_dtype,
-              const pa_decode_opts* opts, Plan* plan) {
+              bool heads_adjacent, const pa_decode_opts* opts, Plan* plan) {
     int st = check_sizes(S, Hq, Hkv, D, bs, MB, kv_dtype);
     if (st != PA_OK) return st;
     pa_decode_opts o{};
@@ -219,10 +214,10 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
         int hp = 1;
         if (o.heads_per_tile != 0) {
             hp = o.heads_per_tile;
-            if (g * hp > 16 || Hkv % hp != 0) return PA_ERR_UNSUPPORTED;
-        } else if (g <= 8 && Hkv % 2 == 0 && (kv_dtype == PA_KV_BF16 ? g >= 4 : g >= 5)) {
+            if (g * hp > 16 || Hkv % hp != 0 || (hp > 1 && !heads_adjacent)) return PA_ERR_UNSUPPORTED;
+        } else if (g <= 8 && Hkv % 2 == 0 && heads_adjacent && (kv_dtype == PA_DTYPE_BF16 ? g >= 4 : g >= 5)) {
             hp = 2;
-            if (o.prefetch_tiles == 0) p.depth = kv_dtype == PA_KV_BF16 ? 3 : 2;
+            if (o.prefetch_tiles == 0) p.depth = kv_dtype == PA_DTYPE_BF16 ? 3 : 2;
         }
         p.heads_per_unit = hp;
     } else if (o.heads_per_tile > 1) {
@@ -242,7 +237,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     int groups_per_cu = 2;
     if (p.variant == PA_VARIANT_MFMA) {
         const int base = p.depth <= 2 ? 4 : (p.depth == 3 ? 3 : 2);
-        const int wpe = (p.heads_per_unit > 1 && kv_dtype == PA_KV_BF16 && base > 2) ? base - 1 : base;
+        const int wpe = (p.heads_per_unit > 1 && kv_dtype == PA_DTYPE_BF16 && base > 2) ? base - 1 : base;
         groups_per_cu = wpe * 4 / p.waves > 1 ? wpe * 4 / p.waves : 1;
     }
     st = choose_partition(units, cap, o.partition_tokens, groups_per_cu, &P);
@@ -294,9 +289,10 @@ struct CascadePlan {
 };
 
 int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB, int32_t kv_dtype,
-                      int32_t G, int32_t maxg, int32_t PMB, const pa_decode_opts* opts, CascadePlan* out) {
+                      bool heads_adjacent, int32_t G, int32_t maxg, int32_t PMB, const pa_decode_opts* opts,
+                      CascadePlan* out) {
     CascadePlan c;
-    int st = make_plan(S, Hq, Hkv, D, bs, MB, kv_dtype, opts, &c.suffix);
+    int st = make_plan(S, Hq, Hkv, D, bs, MB, kv_dtype, heads_adjacent, opts, &c.suffix);
     if (st != PA_OK) return st;
     if (G < 0 || maxg < 0 || PMB < 0) return PA_ERR_SHAPE;
     if (G >= (int64_t(1) << 30) || (int64_t)PMB * bs >= (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
@@ -352,23 +348,92 @@ int32_t last_block_id(int64_t num_blocks) {
     return (int32_t)((num_blocks > INT32_MAX ? (int64_t)INT32_MAX + 1 : num_blocks) - 1);
 }
 
+bool scales_ok(int kv_dtype, float k_scale, float v_scale) {
+    return kv_dtype != PA_DTYPE_FP8_E4M3FN ||
+           (std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f);
+}
+
+int check_workspace(size_t need, const void* workspace, size_t workspace_bytes) {
+    if (need == 0) return PA_OK;
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+// What a decode-family call reads from its tensors: the query rows (and the
+// output rows, for the calls that run), the paged caches, the tables and
+// the context lengths.
+struct Geom {
+    pa::abi::Rows q{}, out{};
+    pa::abi::Cache cache{};
+    const uint8_t* v_cache = nullptr;
+    pa::abi::Table tables{};
+    const int32_t* context_lens = nullptr;
+    int32_t S = 0, Hq = 0, Hkv = 0, D = 0, bs = 0, MB = 0;
+    int64_t N = 0;
+};
+
+// The shapes a plan needs: q [S (or query rows), Hq, D], the K cache and
+// the tables [S, MB]. num_seqs is the tables' row count. need_data: the
+// call runs (a plan reads shapes, types and strides only).
+int plan_geom(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* block_tables, Geom* g,
+              bool need_data = false) {
+    int st = pa::abi::rows(q, false, &g->q, need_data);
+    if (st != PA_OK) return st;
+    st = pa::abi::cache(k_cache, &g->cache, need_data);
+    if (st != PA_OK) return st;
+    st = pa::abi::table(block_tables, &g->tables, need_data);
+    if (st != PA_OK) return st;
+    g->S = (int32_t)g->tables.rows;
+    g->Hq = g->q.heads;
+    g->D = g->q.dim;
+    g->Hkv = g->cache.Hkv;
+    g->bs = g->cache.bs;
+    g->MB = g->tables.cols;
+    g->N = g->cache.N;
+    if (g->D != g->cache.D) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+// Everything a running call needs: plan_geom, the V cache (same layout),
+// context_lens [S] and out (q's shape, written).
+int run_geom(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* block_tables,
+             const pa_tensor* context_lens, const pa_tensor* out, Geom* g) {
+    int st = plan_geom(q, k_cache, block_tables, g, true);
+    if (st != PA_OK) return st;
+    st = pa::abi::caches(k_cache, v_cache, &g->cache);
+    if (st != PA_OK) return st;
+    g->v_cache = static_cast<const uint8_t*>(v_cache->data);
+    int64_t n = 0;
+    st = pa::abi::vec(context_lens, PA_DTYPE_I32, &g->context_lens, &n);
+    if (st != PA_OK) return st;
+    if (n != g->S) return PA_ERR_SHAPE;
+    st = pa::abi::rows(out, true, &g->out);
+    if (st != PA_OK) return st;
+    if (g->out.rows != g->q.rows || g->out.heads != g->q.heads || g->out.dim != g->q.dim) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
 // Arguments of the multi-row kernel for a plan made by make_multi_plan
-// (partials at the plan's workspace offsets when it splits).
-pa::MultiArgs multi_args(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
-                         float scale, void* out, int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv,
-                         int32_t D, int32_t bs, int32_t MB, int64_t num_blocks, int32_t kv_dtype, float k_scale,
-                         float v_scale, void* workspace) {
-    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
-    const int64_t esz = fp8 ? 1 : 2;
+// (partials at the plan's workspace offsets when it splits). `tables` and
+// `S` are the pass's own: the batch's, or the prefix groups' in a cascade.
+pa::MultiArgs multi_args(const Plan& p, const Geom& g, const pa::abi::Table& tables, int32_t S,
+                         const int32_t* query_start, int32_t Tq, int32_t maxq, float scale, int32_t kv_dtype,
+                         float k_scale, float v_scale, void* workspace) {
+    const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3FN;
     pa::MultiArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
+    a.q = static_cast<const uint16_t*>(g.q.data);
+    a.k_cache = g.cache.data;
+    a.v_cache = g.v_cache;
+    a.block_tables = tables.data;
+    a.table_stride = tables.stride;
+    a.context_lens = g.context_lens;
     a.query_start = query_start;
-    a.out = static_cast<uint16_t*>(out);
+    a.out = static_cast<uint16_t*>(g.out.data);
+    a.q_row = g.q.s_row;
+    a.q_head = g.q.s_head;
+    a.out_row = g.out.s_row;
+    a.out_head = g.out.s_head;
     if (p.partials) {
         char* ws = static_cast<char*>(workspace);
         a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
@@ -377,67 +442,63 @@ pa::MultiArgs multi_args(const Plan& p, const void* q, const void* k_cache, cons
     a.num_seqs = S;
     a.num_query_rows = Tq;
     a.max_query_len = maxq;
-    a.num_q_heads = Hq;
-    a.num_kv_heads = Hkv;
-    a.group = Hq / Hkv;
-    a.block_size_log2 = log2i(bs);
-    a.max_blocks_per_seq = MB;
+    a.num_q_heads = g.Hq;
+    a.num_kv_heads = g.Hkv;
+    a.group = g.Hq / g.Hkv;
+    a.block_size_log2 = log2i(g.bs);
+    a.max_blocks_per_seq = tables.cols;
     a.partition_tokens = p.partition_tokens;
     a.num_partitions = p.num_partitions;
     a.row_blocks = p.row_blocks;
-    a.last_block = last_block_id(num_blocks);
-    a.head_bytes = (uint32_t)(D * esz);
-    a.slot_bytes = (uint32_t)((int64_t)Hkv * D * esz);
-    a.block_bytes = (uint32_t)((int64_t)bs * Hkv * D * esz);
+    a.last_block = last_block_id(g.N);
+    a.cache = g.cache.lay;
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
     return a;
 }
 
 // Launch the multi-row kernel for a plan made by make_multi_plan.
-int run_multi(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
-              float scale, void* out, int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv,
-              int32_t D, int32_t bs, int32_t MB, int64_t num_blocks, int32_t kv_dtype, float k_scale,
-              float v_scale, void* workspace, void* stream) {
-    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
-    pa::MultiArgs a = multi_args(p, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out, S,
-                                 Tq, maxq, Hq, Hkv, D, bs, MB, num_blocks, kv_dtype, k_scale, v_scale, workspace);
+int run_multi(const Plan& p, const Geom& g, const int32_t* query_start, int32_t Tq, int32_t maxq, float scale,
+              int32_t kv_dtype, float k_scale, float v_scale, void* workspace, void* stream) {
+    pa::MultiArgs a =
+        multi_args(p, g, g.tables, g.S, query_start, Tq, maxq, scale, kv_dtype, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.scheduled) {
         char* ws = static_cast<char*>(workspace);
         pa::ScheduleArgs sa{};
-        sa.context_lens = context_lens;
+        sa.context_lens = g.context_lens;
         sa.items = reinterpret_cast<int4*>(ws + p.items_off);
         sa.item_count = reinterpret_cast<int*>(ws);
-        sa.num_seqs = S;
-        sa.num_kv_heads = Hkv;
+        sa.num_seqs = g.S;
+        sa.num_kv_heads = g.Hkv;
         sa.partition_tokens = p.partition_tokens;
         sa.num_partitions = p.num_partitions;
-        sa.max_context = MB * bs;
+        sa.max_context = g.MB * g.bs;
         if (pa::launch_schedule(sa, s) != hipSuccess) return PA_ERR_LAUNCH;
         a.items = sa.items;
         a.item_count = sa.item_count;
     }
-    const hipError_t e = pa::launch_multi(a, D, fp8, p.waves, s);
+    const hipError_t e = pa::launch_multi(a, g.D, kv_dtype == PA_DTYPE_FP8_E4M3FN, p.waves, s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 // Arguments of the decode kernels for a plan made by make_plan (partials
 // and work list at the plan's workspace offsets).
-pa::DecodeArgs decode_args(const Plan& p, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                           int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB,
-                           int64_t num_blocks, int32_t kv_dtype, float k_scale, float v_scale, void* workspace) {
-    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
-    const int64_t esz = fp8 ? 1 : 2;
+pa::DecodeArgs decode_args(const Plan& p, const Geom& g, float scale, int32_t kv_dtype, float k_scale,
+                           float v_scale, void* workspace) {
+    const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3FN;
     pa::DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.out = static_cast<uint16_t*>(out);
+    a.q = static_cast<const uint16_t*>(g.q.data);
+    a.k_cache = g.cache.data;
+    a.v_cache = g.v_cache;
+    a.block_tables = g.tables.data;
+    a.table_stride = g.tables.stride;
+    a.context_lens = g.context_lens;
+    a.out = static_cast<uint16_t*>(g.out.data);
+    a.q_seq = g.q.s_row;
+    a.q_head = g.q.s_head;
+    a.out_seq = g.out.s_row;
+    a.out_head = g.out.s_head;
     char* ws = static_cast<char*>(workspace);
     if (p.partials) {
         a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
@@ -447,19 +508,17 @@ pa::DecodeArgs decode_args(const Plan& p, const void* q, const void* k_cache, co
         a.item_count = reinterpret_cast<int*>(ws);
         a.items = reinterpret_cast<const int4*>(ws + p.items_off);
     }
-    a.num_seqs = S;
-    a.num_q_heads = Hq;
-    a.num_kv_heads = Hkv;
-    a.group = Hq / Hkv;
-    a.units_per_seq = Hkv / p.heads_per_unit;
-    a.block_size_log2 = log2i(bs);
-    a.max_blocks_per_seq = MB;
+    a.num_seqs = g.S;
+    a.num_q_heads = g.Hq;
+    a.num_kv_heads = g.Hkv;
+    a.group = g.Hq / g.Hkv;
+    a.units_per_seq = g.Hkv / p.heads_per_unit;
+    a.block_size_log2 = log2i(g.bs);
+    a.max_blocks_per_seq = g.MB;
     a.partition_tokens = p.partition_tokens;
     a.num_partitions = p.num_partitions;
-    a.last_block = last_block_id(num_blocks);
-    a.head_bytes = (uint32_t)(D * esz);
-    a.slot_bytes = (uint32_t)((int64_t)Hkv * D * esz);
-    a.block_bytes = (uint32_t)((int64_t)bs * Hkv * D * esz);
+    a.last_block = last_block_id(g.N);
+    a.cache = g.cache.lay;
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
     return a;
@@ -481,80 +540,127 @@ pa::ScheduleArgs schedule_args(const Plan& p, const pa::DecodeArgs& a, const int
     return sa;
 }
 
+int decode_plan(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* block_tables,
+                const pa_decode_opts* opts, Geom* g, Plan* p) {
+    int st = plan_geom(q, k_cache, block_tables, g);
+    if (st != PA_OK) return st;
+    if (g->q.rows != g->S) return PA_ERR_SHAPE;
+    return make_plan(g->S, g->Hq, g->Hkv, g->D, g->bs, g->MB, g->cache.dtype, g->cache.heads_adjacent, opts, p);
+}
+
+// The cascade's group tensors: none (NULL or zero groups), or
+// prefix_tables [G, PMB], prefix_lens [G], group_start [G + 1].
+struct Groups {
+    pa::abi::Table prefix{};
+    const int32_t* prefix_lens = nullptr;
+    const int32_t* group_start = nullptr;
+    int32_t G = 0, PMB = 0;
+};
+
+int group_geom(const pa_tensor* prefix_tables, const pa_tensor* prefix_lens, const pa_tensor* group_start,
+               bool need_arrays, Groups* gr) {
+    if (prefix_tables == nullptr) return PA_OK;
+    int st = pa::abi::table(prefix_tables, &gr->prefix, need_arrays);
+    if (st != PA_OK) return st;
+    gr->G = (int32_t)gr->prefix.rows;
+    gr->PMB = gr->prefix.cols;
+    if (!need_arrays) return PA_OK;
+    if (gr->G == 0) return PA_OK;
+    int64_t n = 0;
+    st = pa::abi::vec(prefix_lens, PA_DTYPE_I32, &gr->prefix_lens, &n);
+    if (st != PA_OK) return st;
+    if (n != gr->G) return PA_ERR_SHAPE;
+    st = pa::abi::vec(group_start, PA_DTYPE_I32, &gr->group_start, &n);
+    if (st != PA_OK) return st;
+    if (n != (int64_t)gr->G + 1) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
-                   void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                   int32_t block_size, int64_t num_blocks, int32_t kv_dtype, float k_scale,
-                   float v_scale, void* stream) {
-    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
-    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_UNSUPPORTED;
-    if (kv_dtype == PA_KV_FP8_E4M3FN &&
-        (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
-        return PA_ERR_DTYPE;
-    if (num_tokens == 0) return PA_OK;
-    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0) return PA_ERR_ALIGN;
-    // one thread per 16-byte chunk in a single launch, whose grid counts
+int pa_cache_write(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping, const pa_tensor* k_cache,
+                   const pa_tensor* v_cache, float k_scale, float v_scale, void* stream) {
+    pa::abi::Rows kr, vr;
+    pa::abi::Cache c;
+    int st = pa::abi::rows(k, false, &kr);
+    if (st != PA_OK) return st;
+    st = pa::abi::rows(v, false, &vr);
+    if (st != PA_OK) return st;
+    st = pa::abi::caches(k_cache, v_cache, &c);
+    if (st != PA_OK) return st;
+    const int64_t* slots = nullptr;
+    int64_t T = 0;
+    st = pa::abi::vec(slot_mapping, PA_DTYPE_I64, &slots, &T);
+    if (st != PA_OK) return st;
+    if (kr.rows != T || vr.rows != T || kr.heads != c.Hkv || vr.heads != c.Hkv || kr.dim != c.D || vr.dim != c.D)
+        return PA_ERR_SHAPE;
+    if (!scales_ok(c.dtype, k_scale, v_scale)) return PA_ERR_DTYPE;
+    if (T == 0) return PA_OK;
+    // one thread per 8-element chunk in a single launch, whose grid counts
     // work-items in 32 bits; divided, not multiplied, so that nothing overflows
-    const int64_t chunks_per_token = (int64_t)num_kv_heads * (head_dim / 8);
-    if (num_tokens > ((int64_t(1) << 32) - 256) / chunks_per_token) return PA_ERR_UNSUPPORTED;
+    const int64_t chunks_per_token = (int64_t)c.Hkv * (c.D / 8);
+    if (T > ((int64_t(1) << 32) - 256) / chunks_per_token) return PA_ERR_UNSUPPORTED;
     if (pa::debug_validate_enabled()) {
-        const int vs = pa_check_cache_write_inputs(slot_mapping, num_tokens, block_size, num_blocks, stream);
+        const int vs = pa_check_cache_write_inputs(slot_mapping, k_cache, stream);
         if (vs != PA_OK) return vs;
     }
     pa::CacheWriteArgs a{};
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.slot_mapping = slot_mapping;
-    a.k_cache = static_cast<uint8_t*>(k_cache);
-    a.v_cache = static_cast<uint8_t*>(v_cache);
-    a.num_tokens = num_tokens;
-    a.num_slots = num_blocks * block_size;
-    a.num_kv_heads = num_kv_heads;
-    a.head_dim = head_dim;
-    a.k_scale = kv_dtype == PA_KV_FP8_E4M3FN ? k_scale : 1.0f;
-    a.v_scale = kv_dtype == PA_KV_FP8_E4M3FN ? v_scale : 1.0f;
+    a.k = static_cast<const uint16_t*>(kr.data);
+    a.v = static_cast<const uint16_t*>(vr.data);
+    a.k_token = kr.s_row;
+    a.k_head = kr.s_head;
+    a.v_token = vr.s_row;
+    a.v_head = vr.s_head;
+    a.slot_mapping = slots;
+    a.k_cache = c.data;
+    a.v_cache = static_cast<uint8_t*>(v_cache->data);
+    a.num_tokens = T;
+    a.num_slots = c.N * c.bs;
+    a.num_kv_heads = c.Hkv;
+    a.head_dim = c.D;
+    a.block_size_log2 = log2i(c.bs);
+    a.cache = c.lay;
+    a.k_scale = c.dtype == PA_DTYPE_FP8_E4M3FN ? k_scale : 1.0f;
+    a.v_scale = c.dtype == PA_DTYPE_FP8_E4M3FN ? v_scale : 1.0f;
     const hipError_t e =
-        pa::launch_cache_write(a, kv_dtype == PA_KV_FP8_E4M3FN, static_cast<hipStream_t>(stream));
+        pa::launch_cache_write(a, c.dtype == PA_DTYPE_FP8_E4M3FN, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
-                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                   int32_t kv_dtype, void* stream) {
-    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
-    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3FN) return PA_ERR_DTYPE;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_UNSUPPORTED;
-    if (!pa::grid_fits(num_pairs, pa::kCopyThreads)) return PA_ERR_UNSUPPORTED;
-    if (num_pairs == 0) return PA_OK;
-    if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
-    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(block_mapping) & 7u) != 0) return PA_ERR_ALIGN;
+int pa_copy_blocks(const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* block_mapping,
+                   void* stream) {
+    pa::abi::Cache c;
+    int st = pa::abi::caches(k_cache, v_cache, &c);
+    if (st != PA_OK) return st;
+    st = pa::abi::basic(block_mapping, 2, PA_DTYPE_I64);
+    if (st != PA_OK) return st;
+    if (block_mapping->shape[1] != 2) return PA_ERR_SHAPE;
+    const int64_t n = block_mapping->shape[0];
+    if (n > 1 && block_mapping->stride[0] != 2) return PA_ERR_LAYOUT;
+    if (!c.blocks_contiguous) return PA_ERR_LAYOUT;
+    if (!pa::grid_fits(n, pa::kCopyThreads) || n >= (int64_t(1) << 31)) return PA_ERR_UNSUPPORTED;
+    if (n == 0) return PA_OK;
+    if (!pa::abi::aligned(block_mapping->data, 8)) return PA_ERR_ALIGN;
     pa::CopyBlocksArgs a{};
-    a.k_cache = static_cast<uint8_t*>(k_cache);
-    a.v_cache = static_cast<uint8_t*>(v_cache);
-    a.pairs = block_mapping;
-    a.num_pairs = num_pairs;
-    a.num_blocks = num_blocks;
-    a.block_bytes = (int64_t)block_size * num_kv_heads * head_dim * (kv_dtype == PA_KV_BF16 ? 2 : 1);
+    a.k_cache = c.data;
+    a.v_cache = static_cast<uint8_t*>(v_cache->data);
+    a.pairs = static_cast<const int64_t*>(block_mapping->data);
+    a.num_pairs = n;
+    a.num_blocks = c.N;
+    a.block_stride = c.lay.block;
+    a.block_bytes = c.block_bytes;
     const hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int32_t max_blocks_per_seq, int32_t kv_dtype,
+int pa_decode_get_plan(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* block_tables,
                        const pa_decode_opts* opts, pa_decode_plan* plan) {
     if (!plan) return PA_ERR_NULL;
+    Geom g;
     Plan p;
-    const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                             max_blocks_per_seq, kv_dtype, opts, &p);
+    const int st = decode_plan(q, k_cache, block_tables, opts, &g, &p);
     if (st != PA_OK) return st;
     plan->variant = p.variant;
     plan->waves_per_group = p.waves;
@@ -568,233 +674,215 @@ int pa_decode_get_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     return PA_OK;
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                                int32_t kv_dtype, const pa_decode_opts* opts) {
+size_t pa_decode_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* block_tables,
+                                const pa_decode_opts* opts) {
+    Geom g;
     Plan p;
-    if (make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                  kv_dtype, opts, &p) != PA_OK)
-        return 0;
+    if (decode_plan(q, k_cache, block_tables, opts, &g, &p) != PA_OK) return 0;
     return p.workspace;
 }
 
-int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-              const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
-              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-              int32_t max_blocks_per_seq, int64_t num_blocks, int32_t kv_dtype, float k_scale,
-              float v_scale, void* workspace, size_t workspace_bytes, const pa_decode_opts* opts,
+int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+              const pa_tensor* block_tables, const pa_tensor* context_lens, float scale, const pa_tensor* out,
+              float k_scale, float v_scale, void* workspace, size_t workspace_bytes, const pa_decode_opts* opts,
               void* stream) {
-    Plan p;
-    int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                       kv_dtype, opts, &p);
+    Geom g;
+    int st = run_geom(q, k_cache, v_cache, block_tables, context_lens, out, &g);
     if (st != PA_OK) return st;
-    if (num_blocks <= 0) return PA_ERR_SHAPE;
+    if (g.q.rows != g.S) return PA_ERR_SHAPE;
+    Plan p;
+    st = make_plan(g.S, g.Hq, g.Hkv, g.D, g.bs, g.MB, g.cache.dtype, g.cache.heads_adjacent, opts, &p);
+    if (st != PA_OK) return st;
     if (!std::isfinite(scale)) return PA_ERR_SHAPE;
-    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
-    if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
-        return PA_ERR_DTYPE;
-    if (num_seqs == 0) return PA_OK;
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
-        return PA_ERR_ALIGN;
-    if (p.workspace > 0) {
-        if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
-    }
+    const int kvd = g.cache.dtype;
+    if (!scales_ok(kvd, k_scale, v_scale)) return PA_ERR_DTYPE;
+    if (g.S == 0) return PA_OK;
+    st = check_workspace(p.workspace, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
     if (pa::debug_validate_enabled()) {
-        const int vs = pa_check_decode_inputs(block_tables, context_lens, num_seqs, block_size,
-                                              max_blocks_per_seq, num_blocks, stream);
+        const int vs = pa_check_decode_inputs(block_tables, context_lens, k_cache, stream);
         if (vs != PA_OK) return vs;
     }
-    if (p.multi)
-        return run_multi(p, q, k_cache, v_cache, block_tables, context_lens, nullptr, scale, out, num_seqs,
-                         num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                         num_blocks, kv_dtype, k_scale, v_scale, workspace, stream);
-    pa::DecodeArgs a = decode_args(p, q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
-                                   num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                                   num_blocks, kv_dtype, k_scale, v_scale, workspace);
+    if (p.multi) return run_multi(p, g, nullptr, g.S, 1, scale, kvd, k_scale, v_scale, workspace, stream);
+    pa::DecodeArgs a = decode_args(p, g, scale, kvd, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (p.scheduled) {
-        const pa::ScheduleArgs sa = schedule_args(p, a, context_lens, max_blocks_per_seq * block_size);
+        const pa::ScheduleArgs sa = schedule_args(p, a, g.context_lens, g.MB * g.bs);
         e = pa::launch_schedule(sa, s);
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
     const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit};
-    e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, ls, s)
-                                     : pa::launch_decode_valu(a, head_dim, fp8, ls, s);
+    const bool fp8 = kvd == PA_DTYPE_FP8_E4M3FN;
+    e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, g.D, fp8, ls, s)
+                                     : pa::launch_decode_valu(a, g.D, fp8, ls, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
     if (p.num_partitions > 1) {
         pa::MergeArgs m{};
-        m.context_lens = context_lens;
+        m.context_lens = g.context_lens;
         m.part_ml = a.part_ml;
         m.part_o = a.part_o;
         m.out = a.out;
-        m.num_seqs = num_seqs;
-        m.num_q_heads = num_q_heads;
-        m.head_dim = head_dim;
+        m.out_seq = a.out_seq;
+        m.out_head = a.out_head;
+        m.num_seqs = g.S;
+        m.num_q_heads = g.Hq;
+        m.head_dim = g.D;
         m.partition_tokens = p.partition_tokens;
         m.num_partitions = p.num_partitions;
-        m.max_context = max_blocks_per_seq * block_size;
+        m.max_context = g.MB * g.bs;
         e = pa::launch_merge(m, s);
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
     return PA_OK;
 }
 
-size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                                        int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
-                                        int32_t kv_dtype, const pa_decode_opts* opts) {
+size_t pa_decode_cascade_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* block_tables,
+                                        const pa_tensor* prefix_tables, int32_t max_group_size,
+                                        const pa_decode_opts* opts) {
+    Geom g;
+    Groups gr;
+    if (plan_geom(q, k_cache, block_tables, &g) != PA_OK || g.q.rows != g.S) return 0;
+    if (group_geom(prefix_tables, nullptr, nullptr, false, &gr) != PA_OK) return 0;
     CascadePlan c;
-    if (make_cascade_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                          kv_dtype, num_groups, max_group_size, max_prefix_blocks, opts, &c) != PA_OK)
+    if (make_cascade_plan(g.S, g.Hq, g.Hkv, g.D, g.bs, g.MB, g.cache.dtype, g.cache.heads_adjacent, gr.G,
+                          max_group_size, gr.PMB, opts, &c) != PA_OK)
         return 0;
     return c.workspace;
 }
 
-int pa_decode_cascade(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                      const int32_t* context_lens, const int32_t* prefix_tables, const int32_t* prefix_lens,
-                      const int32_t* group_start, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                      int64_t num_blocks, int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
-                      int32_t kv_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+int pa_decode_cascade(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* prefix_tables,
+                      const pa_tensor* prefix_lens, const pa_tensor* group_start, float scale, const pa_tensor* out,
+                      int32_t max_group_size, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
                       const pa_decode_opts* opts, void* stream) {
-    CascadePlan c;
-    int st = make_cascade_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                               kv_dtype, num_groups, max_group_size, max_prefix_blocks, opts, &c);
+    Geom g;
+    int st = run_geom(q, k_cache, v_cache, block_tables, context_lens, out, &g);
     if (st != PA_OK) return st;
-    if (num_blocks <= 0) return PA_ERR_SHAPE;
+    if (g.q.rows != g.S) return PA_ERR_SHAPE;
+    Groups gr;
+    st = group_geom(prefix_tables, prefix_lens, group_start, true, &gr);
+    if (st != PA_OK) return st;
+    CascadePlan c;
+    st = make_cascade_plan(g.S, g.Hq, g.Hkv, g.D, g.bs, g.MB, g.cache.dtype, g.cache.heads_adjacent, gr.G,
+                           max_group_size, gr.PMB, opts, &c);
+    if (st != PA_OK) return st;
     if (!std::isfinite(scale)) return PA_ERR_SHAPE;
-    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
-    if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
-        return PA_ERR_DTYPE;
-    if (num_seqs == 0) return PA_OK;
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
-    if (c.has_prefix && (!prefix_tables || !prefix_lens || !group_start)) return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
-    const auto mis4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
-    if (mis4(block_tables) || mis4(context_lens) || mis4(prefix_tables) || mis4(prefix_lens) || mis4(group_start))
-        return PA_ERR_ALIGN;
+    const int kvd = g.cache.dtype;
+    if (!scales_ok(kvd, k_scale, v_scale)) return PA_ERR_DTYPE;
+    if (g.S == 0) return PA_OK;
     if (!workspace || workspace_bytes < c.workspace) return PA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
     if (pa::debug_validate_enabled()) {
-        int vs = pa_check_decode_inputs(block_tables, context_lens, num_seqs, block_size, max_blocks_per_seq,
-                                        num_blocks, stream);
+        int vs = pa_check_decode_inputs(block_tables, context_lens, k_cache, stream);
         if (vs == PA_OK && c.has_prefix)
-            vs = pa_check_cascade_inputs(prefix_tables, prefix_lens, group_start, num_groups, max_group_size,
-                                         max_prefix_blocks, num_seqs, block_size, num_blocks, stream);
+            vs = pa_check_cascade_inputs(prefix_tables, prefix_lens, group_start, max_group_size, g.S, k_cache,
+                                         stream);
         if (vs != PA_OK) return vs;
     }
     pa::CascadeGroups groups{};
     if (c.has_prefix) {
-        groups.group_start = group_start;
-        groups.prefix_lens = prefix_lens;
-        groups.num_groups = num_groups;
+        groups.group_start = gr.group_start;
+        groups.prefix_lens = gr.prefix_lens;
+        groups.num_groups = gr.G;
         groups.max_group_size = max_group_size;
-        groups.max_prefix_tokens = max_prefix_blocks * block_size;
-        groups.max_context = max_blocks_per_seq * block_size;
+        groups.max_prefix_tokens = gr.PMB * g.bs;
+        groups.max_context = g.MB * g.bs;
     }
     const Plan& p = c.suffix;
-    const pa::DecodeArgs a = decode_args(p, q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
-                                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                                         num_blocks, kv_dtype, k_scale, v_scale, workspace);
+    const pa::DecodeArgs a = decode_args(p, g, scale, kvd, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool fp8 = kvd == PA_DTYPE_FP8_E4M3FN;
     // 1. suffix work list
-    pa::ScheduleArgs sa = schedule_args(p, a, context_lens, max_blocks_per_seq * block_size);
+    pa::ScheduleArgs sa = schedule_args(p, a, g.context_lens, g.MB * g.bs);
     sa.cascade = groups;
     if (pa::launch_schedule(sa, s) != hipSuccess) return PA_ERR_LAUNCH;
     // 2. prefix pass: each group's prefix once for all its members
     pa::MultiArgs m{};
     if (c.has_prefix) {
-        m = multi_args(c.prefix, q, k_cache, v_cache, prefix_tables, context_lens, nullptr, scale, out,
-                       num_groups, num_seqs, max_group_size, num_q_heads, num_kv_heads, head_dim, block_size,
-                       max_prefix_blocks, num_blocks, kv_dtype, k_scale, v_scale, workspace);
+        m = multi_args(c.prefix, g, gr.prefix, gr.G, nullptr, g.S, max_group_size, scale, kvd, k_scale, v_scale,
+                       workspace);
         m.cascade = groups;
-        if (pa::launch_multi(m, head_dim, fp8, c.prefix.waves, s) != hipSuccess) return PA_ERR_LAUNCH;
+        if (pa::launch_multi(m, g.D, fp8, c.prefix.waves, s) != hipSuccess) return PA_ERR_LAUNCH;
     }
     // 3. suffix pass
     const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit};
-    const hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, head_dim, fp8, ls, s)
-                                                      : pa::launch_decode_valu(a, head_dim, fp8, ls, s);
+    const hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, g.D, fp8, ls, s)
+                                                      : pa::launch_decode_valu(a, g.D, fp8, ls, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
     // 4. merge both passes' states
     pa::CascadeMergeArgs mg{};
-    mg.context_lens = context_lens;
+    mg.context_lens = g.context_lens;
     mg.cascade = groups;
     mg.pre_ml = m.part_ml;
     mg.pre_o = m.part_o;
     mg.part_ml = a.part_ml;
     mg.part_o = a.part_o;
     mg.out = a.out;
-    mg.num_seqs = num_seqs;
-    mg.num_q_heads = num_q_heads;
-    mg.head_dim = head_dim;
+    mg.out_seq = a.out_seq;
+    mg.out_head = a.out_head;
+    mg.num_seqs = g.S;
+    mg.num_q_heads = g.Hq;
+    mg.head_dim = g.D;
     mg.prefix_partition_tokens = c.has_prefix ? c.prefix.partition_tokens : 1;
     mg.prefix_partitions = c.has_prefix ? c.prefix.num_partitions : 0;
     mg.partition_tokens = p.partition_tokens;
     mg.num_partitions = p.num_partitions;
-    mg.max_context = max_blocks_per_seq * block_size;
+    mg.max_context = g.MB * g.bs;
     mg.block_size_log2 = a.block_size_log2;
     return pa::launch_cascade_merge(mg, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
-                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t kv_dtype,
-                                      int32_t partition_tokens) {
-    if (check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype) != PA_OK)
-        return 0;
+size_t pa_decode_multi_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* block_tables,
+                                      int32_t max_query_len, int32_t partition_tokens) {
+    Geom g;
+    if (plan_geom(q, k_cache, block_tables, &g) != PA_OK) return 0;
+    if (g.q.rows > INT32_MAX) return 0;
+    if (check_sizes(g.S, g.Hq, g.Hkv, g.D, g.bs, g.MB, g.cache.dtype) != PA_OK) return 0;
     Plan p;
-    if (make_multi_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                        block_size, max_blocks_per_seq, partition_tokens, &p) != PA_OK)
+    if (make_multi_plan(g.S, (int32_t)g.q.rows, max_query_len, g.Hq, g.Hkv, g.D, g.bs, g.MB, partition_tokens, &p) !=
+        PA_OK)
         return 0;
     return p.workspace;
 }
 
-int pa_decode_multi(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                    const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
-                    int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                    int64_t num_blocks, int32_t kv_dtype, float k_scale, float v_scale, void* workspace,
-                    size_t workspace_bytes, int32_t partition_tokens, void* stream) {
-    int st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype);
+int pa_decode_multi(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                    const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* query_start,
+                    float scale, const pa_tensor* out, int32_t max_query_len, float k_scale, float v_scale,
+                    void* workspace, size_t workspace_bytes, int32_t partition_tokens, void* stream) {
+    Geom g;
+    int st = run_geom(q, k_cache, v_cache, block_tables, context_lens, out, &g);
     if (st != PA_OK) return st;
-    if (num_query_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
-    if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_SHAPE;
-    const bool fp8 = kv_dtype == PA_KV_FP8_E4M3FN;
-    if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
-        return PA_ERR_DTYPE;
+    const int32_t* qs = nullptr;
+    int64_t nqs = 0;
+    st = pa::abi::vec(query_start, PA_DTYPE_I32, &qs, &nqs);
+    if (st != PA_OK) return st;
+    if (nqs != (int64_t)g.S + 1) return PA_ERR_SHAPE;
+    st = check_sizes(g.S, g.Hq, g.Hkv, g.D, g.bs, g.MB, g.cache.dtype);
+    if (st != PA_OK) return st;
+    const int32_t Tq = (int32_t)g.q.rows;
+    if (max_query_len < 0) return PA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+    const int kvd = g.cache.dtype;
+    if (!scales_ok(kvd, k_scale, v_scale)) return PA_ERR_DTYPE;
     Plan p;
-    st = make_multi_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                         block_size, max_blocks_per_seq, partition_tokens, &p);
+    st = make_multi_plan(g.S, Tq, max_query_len, g.Hq, g.Hkv, g.D, g.bs, g.MB, partition_tokens, &p);
     if (st != PA_OK) return st;
-    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out) return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
-        (reinterpret_cast<uintptr_t>(query_start) & 3u))
-        return PA_ERR_ALIGN;
-    if (p.workspace > 0) {
-        if (!workspace || workspace_bytes < p.workspace) return PA_ERR_WORKSPACE;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
-    }
+    if (g.S == 0 || Tq == 0 || max_query_len == 0) return PA_OK;
+    st = check_workspace(p.workspace, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
     if (pa::debug_validate_enabled()) {
-        const int vs = pa_check_decode_inputs(block_tables, context_lens, num_seqs, block_size,
-                                              max_blocks_per_seq, num_blocks, stream);
+        const int vs = pa_check_multi_inputs(block_tables, context_lens, query_start, max_query_len, k_cache, stream);
         if (vs != PA_OK) return vs;
     }
-    return run_multi(p, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out, num_seqs,
-                     num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
-                     max_blocks_per_seq, num_blocks, kv_dtype, k_scale, v_scale, workspace, stream);
+    return run_multi(p, g, qs, Tq, max_query_len, scale, kvd, k_scale, v_scale, workspace, stream);
 }
 
 int pa_probe_stream_read(const void* buf, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream) {
     if (bytes < 0 || (bytes & 15) != 0) return PA_ERR_SHAPE;
     if (bytes == 0) return PA_OK;
     if (!buf || !sink) return PA_ERR_NULL;
-    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return PA_ERR_ALIGN;
+    if (!pa::abi::aligned(buf, 16) || !pa::abi::aligned(sink, 4)) return PA_ERR_ALIGN;
     const int cus = current_cu_count();
     if (cus <= 0) return PA_ERR_DEVICE;
     const hipError_t e = pa::launch_probe_read(buf, bytes, nontemporal != 0, sink, cus, static_cast<hipStream_t>(stream));
@@ -812,16 +900,18 @@ const char* pa_strerror(int status) {
         case PA_ERR_NULL: return "a required pointer is NULL";
         case PA_ERR_SHAPE: return "a size is out of range or inconsistent";
         case PA_ERR_UNSUPPORTED: return "valid but not supported by the kernels";
-        case PA_ERR_ALIGN: return "a pointer is not suitably aligned";
-        case PA_ERR_DTYPE: return "unknown kv dtype or bad fp8 scale";
+        case PA_ERR_ALIGN: return "a device address is not suitably aligned";
+        case PA_ERR_DTYPE: return "wrong element type, or a bad fp8 scale";
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
-        case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a copy";
         case PA_ERR_DEVICE: return "the current HIP device could not be queried";
         case PA_ERR_PRECONDITION: return "a device-side input violates a precondition (slots, tables or lengths)";
+        case PA_ERR_LAYOUT: return "unsupported strides (innermost dimension not contiguous, not 16-byte multiples, "
+                                   "overlapping, or a block too large)";
         default: return "unknown status";
     }
 }
 
-int pa_version(void) { return 100; }
+int pa_version(void) { return 200; }
 
 }  // extern "C"

@@ -48,7 +48,7 @@ __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const flo
         const int64_t row = (int64_t)seq * a.num_q_heads + hq;
         if (final_out) {
             const float y = (L > 0.0f) ? (O * a.v_scale) / L : 0.0f;
-            a.out[row * D + d] = f32_to_bf16_rne(y);
+            a.out[(int64_t)seq * a.out_seq + (int64_t)hq * a.out_head + d] = f32_to_bf16_rne(y);
         } else {
             const int64_t prow = row * a.num_partitions + part;
             a.part_o[prow * D + d] = O * a.v_scale;
@@ -145,11 +145,11 @@ struct TableReader {
     int last_block;
 };
 
-__device__ __forceinline__ TableReader make_table_reader(const int32_t* block_tables, int max_blocks_per_seq,
-                                                         int block_size_log2, int last_block, int seq,
-                                                         int t_begin, int last_tile, int tile_tokens = kTile) {
+__device__ __forceinline__ TableReader make_table_reader(const int32_t* block_tables, int64_t table_stride,
+                                                         int max_blocks_per_seq, int block_size_log2, int last_block,
+                                                         int seq, int t_begin, int last_tile, int tile_tokens = kTile) {
     TableReader r;
-    r.rsrc = make_rsrc(block_tables + (int64_t)seq * max_blocks_per_seq, (uint32_t)max_blocks_per_seq * 4u);
+    r.rsrc = make_rsrc(block_tables + (int64_t)seq * table_stride, (uint32_t)max_blocks_per_seq * 4u);
     r.t_begin = t_begin;
     r.last_tile = last_tile;
     r.tile_tokens = tile_tokens;
@@ -160,8 +160,8 @@ __device__ __forceinline__ TableReader make_table_reader(const int32_t* block_ta
 
 __device__ __forceinline__ TableReader make_table_reader(const DecodeArgs& a, const WorkItem& wi, int last_tile,
                                                          int tile_tokens = kTile) {
-    return make_table_reader(a.block_tables, a.max_blocks_per_seq, a.block_size_log2, a.last_block, wi.seq,
-                             wi.t_begin, last_tile, tile_tokens);
+    return make_table_reader(a.block_tables, a.table_stride, a.max_blocks_per_seq, a.block_size_log2, a.last_block,
+                             wi.seq, wi.t_begin, last_tile, tile_tokens);
 }
 
 // Start fetching the table entry of tile t (an index within the item).

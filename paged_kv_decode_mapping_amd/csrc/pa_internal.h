@@ -20,24 +20,34 @@ struct CascadeGroups {
     int32_t max_context;           // members' table rows: max_blocks_per_seq * block_size
 };
 
+// Where a paged cache's rows are: element (block b, row r, KV head h, d)
+// sits at byte b * block + r * token + h * head + d * element size from the
+// cache's base (Tutorial §4.2's pool order [N, bs, Hkv, D] has token =
+// Hkv * D * e and head = D * e; a head-major pool has token = D * e, head =
+// bs * D * e). K and V share it.
+struct CacheLayout {
+    int64_t block;                 // bytes between physical blocks
+    uint32_t token;                // bytes between rows of a block (>= D * e)
+    uint32_t head;                 // bytes between KV heads of a row
+};
+
 // Arguments of the decode kernels, passed by value.
 struct DecodeArgs {
-    const uint16_t* q;             // [S, Hq, D] bf16
-    const uint8_t* k_cache;        // [N, bs, Hkv, D] bf16 or e4m3fn
+    const uint16_t* q;             // [S, Hq, D] bf16, element strides q_seq, q_head
+    const uint8_t* k_cache;        // [N, bs, Hkv, D] bf16 or e4m3fn, at `cache`
     const uint8_t* v_cache;
-    const int32_t* block_tables;   // [S, MB]
+    const int32_t* block_tables;   // [S, MB], row stride table_stride
     const int32_t* context_lens;   // [S]
-    uint16_t* out;                 // [S, Hq, D] bf16
+    uint16_t* out;                 // [S, Hq, D] bf16, element strides out_seq, out_head
     float* part_ml;                // [S, Hq, P, 2] (max in log2 units, sum), split only
     float* part_o;                 // [S, Hq, P, D] unnormalised outputs, split only
+    int64_t q_seq, q_head, out_seq, out_head, table_stride;
     int32_t num_seqs, num_q_heads, num_kv_heads, group;
     int32_t units_per_seq;         // work units per sequence: KV heads / heads per unit
     int32_t block_size_log2, max_blocks_per_seq;
     int32_t partition_tokens, num_partitions;
     int32_t last_block;            // min(num_blocks, 2^31) - 1: the largest usable block id
-    uint32_t block_bytes;          // bytes of one physical block
-    uint32_t slot_bytes;           // bytes of one token row (all KV heads)
-    uint32_t head_bytes;           // bytes of one KV head's row
+    CacheLayout cache;
     float qk_scale_log2;           // scale * k_scale * log2(e)
     float v_scale;                 // 1 for bf16
     // Device schedule (null = direct grid, one workgroup per item):
@@ -64,42 +74,46 @@ struct MergeArgs {
     const int32_t* context_lens;
     const float* part_ml;
     const float* part_o;
-    uint16_t* out;
+    uint16_t* out;                 // [S, Hq, D], element strides out_seq, out_head
+    int64_t out_seq, out_head;
     int32_t num_seqs, num_q_heads, head_dim, partition_tokens, num_partitions;
     int32_t max_context;           // max_blocks_per_seq * block_size
 };
 
 struct CacheWriteArgs {
-    const uint16_t* k;             // [T, Hkv, D]
-    const uint16_t* v;
+    const uint16_t* k;             // [T, Hkv, D], element strides k_token, k_head
+    const uint16_t* v;             // [T, Hkv, D], element strides v_token, v_head
     const int64_t* slot_mapping;   // [T]
-    uint8_t* k_cache;              // [N, bs, Hkv, D]
+    uint8_t* k_cache;              // [N, bs, Hkv, D] at `cache`
     uint8_t* v_cache;
+    int64_t k_token, k_head, v_token, v_head;
     int64_t num_tokens;
     int64_t num_slots;             // N * bs
-    int32_t num_kv_heads, head_dim;
+    int32_t num_kv_heads, head_dim, block_size_log2;
+    CacheLayout cache;
     float k_scale, v_scale;        // fp8 only
 };
 
 // Arguments of the multi-row kernel (several query tokens per sequence,
 // or more than 16 query heads per KV head), passed by value.
 struct MultiArgs {
-    const uint16_t* q;             // [num_query_rows, Hq, D] bf16
-    const uint8_t* k_cache;        // [N, bs, Hkv, D] bf16 or e4m3fn
+    const uint16_t* q;             // [num_query_rows, Hq, D] bf16, element strides q_row, q_head
+    const uint8_t* k_cache;        // [N, bs, Hkv, D] bf16 or e4m3fn, at `cache`
     const uint8_t* v_cache;
-    const int32_t* block_tables;   // [S, MB]
+    const int32_t* block_tables;   // [S, MB], row stride table_stride
     const int32_t* context_lens;   // [S]
     const int32_t* query_start;    // [S + 1]; null = one query token per sequence (row = seq)
-    uint16_t* out;                 // [num_query_rows, Hq, D] bf16
+    uint16_t* out;                 // [num_query_rows, Hq, D] bf16, element strides out_row, out_head
     float* part_ml;                // [num_query_rows, Hq, P, 2], split only
     float* part_o;                 // [num_query_rows, Hq, P, D], split only
+    int64_t q_row, q_head, out_row, out_head, table_stride;
     int32_t num_seqs, num_query_rows, max_query_len;
     int32_t num_q_heads, num_kv_heads, group;
     int32_t block_size_log2, max_blocks_per_seq;
     int32_t partition_tokens, num_partitions;
     int32_t row_blocks;            // blocks of 16 * waves rows per (sequence, KV head)
     int32_t last_block;
-    uint32_t block_bytes, slot_bytes, head_bytes;
+    CacheLayout cache;
     float qk_scale_log2, v_scale;
     // Device work list (null = direct grid): the decode work list of
     // (sequence, KV head, partition) items, longest first; workgroup b takes
@@ -124,7 +138,8 @@ struct CascadeMergeArgs {
     const float* pre_o;            // [S, Hq, prefix_partitions, D]
     const float* part_ml;          // [S, Hq, num_partitions, 2]
     const float* part_o;           // [S, Hq, num_partitions, D]
-    uint16_t* out;
+    uint16_t* out;                 // [S, Hq, D], element strides out_seq, out_head
+    int64_t out_seq, out_head;
     int32_t num_seqs, num_q_heads, head_dim;
     int32_t prefix_partition_tokens, prefix_partitions;
     int32_t partition_tokens, num_partitions;
@@ -132,11 +147,12 @@ struct CascadeMergeArgs {
 };
 
 struct CopyBlocksArgs {
-    uint8_t* k_cache;              // [N, bs, Hkv, D]
-    uint8_t* v_cache;
+    uint8_t* k_cache;              // [N, bs, Hkv, D]: block b is the byte range
+    uint8_t* v_cache;              //   [b * block_stride, b * block_stride + block_bytes)
     const int64_t* pairs;          // [num_pairs][2] (src, dst)
     int64_t num_pairs;
     int64_t num_blocks;
+    int64_t block_stride;          // bytes between blocks
     int64_t block_bytes;           // bs * Hkv * D * element size (a multiple of 16)
 };
 

@@ -17,6 +17,11 @@
 //   decode:      every context length is in [0, max_blocks_per_seq *
 //                block_size], and the table entries that cover it (the first
 //                ceil(ctx / block_size) of the row) name blocks inside the pool;
+//   multi-token: those of decode, and each sequence's query tokens are some
+//                of its cached ones (query_start rises from 0 by n_i with
+//                0 <= n_i <= min(max_query_len, context length)): Tutorial
+//                §5.1 verifies drafts that were appended to the cache and
+//                §6.2's chunks attend over what is already cached;
 //   cascade:     the group offsets rise from >= 0 to <= num_seqs, no group
 //                has more than max_group_size sequences, every prefix length
 //                is a whole number of blocks within its table row, and the
@@ -27,8 +32,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/pa.h"
-#include "pa_internal.h"
+#include "pa_abi.h"
 
 namespace {
 
@@ -40,6 +44,56 @@ int copy_to_host(std::vector<T>& dst, const T* src, int64_t n, hipStream_t s) {
         return PA_ERR_LAUNCH;
     if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_LAUNCH;
     return PA_OK;
+}
+
+// A table [rows, cols] with row stride `stride` into a dense host copy.
+int copy_table(std::vector<int32_t>& dst, const pa::abi::Table& t, hipStream_t s) {
+    dst.resize((size_t)t.rows * t.cols);
+    if (t.rows == 0 || t.cols == 0) return PA_OK;
+    if (hipMemcpy2DAsync(dst.data(), (size_t)t.cols * 4, t.data, (size_t)t.stride * 4, (size_t)t.cols * 4,
+                         (size_t)t.rows, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return PA_ERR_LAUNCH;
+    if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_LAUNCH;
+    return PA_OK;
+}
+
+// Context lengths within their table rows, covering entries inside the pool.
+int check_tables(const std::vector<int32_t>& ctx, const std::vector<int32_t>& table, int64_t S, int32_t MB,
+                 int32_t bs, int64_t N) {
+    const int64_t cap = (int64_t)MB * bs;
+    for (int64_t i = 0; i < S; ++i) {
+        const int64_t c = ctx[(size_t)i];
+        if (c < 0 || c > cap) return PA_ERR_PRECONDITION;
+        const int64_t nb = (c + bs - 1) / bs;
+        const int32_t* row = table.data() + (size_t)i * MB;
+        for (int64_t b = 0; b < nb; ++b)
+            if (row[b] < 0 || row[b] >= N) return PA_ERR_PRECONDITION;
+    }
+    return PA_OK;
+}
+
+// The tables and lengths of a decode-family call: their arguments checked
+// (parse_decode_inputs, no device access), then read to the host.
+int parse_decode_inputs(const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* k_cache,
+                        pa::abi::Table* t, pa::abi::Cache* c, const int32_t** cl) {
+    int st = pa::abi::cache(k_cache, c, false);
+    if (st != PA_OK) return st;
+    st = pa::abi::table(block_tables, t);
+    if (st != PA_OK) return st;
+    int64_t n = 0;
+    st = pa::abi::vec(context_lens, PA_DTYPE_I32, cl, &n);
+    if (st != PA_OK) return st;
+    if (n != t->rows) return PA_ERR_SHAPE;
+    if (n > 0 && t->cols <= 0) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+int read_decode_inputs(const pa::abi::Table& t, const int32_t* cl, hipStream_t s, std::vector<int32_t>* ctx,
+                       std::vector<int32_t>* table) {
+    if (t.rows == 0) return PA_OK;
+    int st = copy_to_host(*ctx, cl, t.rows, s);
+    if (st != PA_OK) return st;
+    return copy_table(*table, t, s);
 }
 
 }  // namespace
@@ -55,15 +109,19 @@ bool debug_validate_enabled() {
 
 extern "C" {
 
-int pa_check_cache_write_inputs(const int64_t* slot_mapping, int64_t num_tokens, int32_t block_size,
-                                int64_t num_blocks, void* stream) {
-    if (num_tokens < 0 || block_size <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
-    if (num_tokens == 0) return PA_OK;
-    if (!slot_mapping) return PA_ERR_NULL;
-    std::vector<int64_t> slots;
-    const int st = copy_to_host(slots, slot_mapping, num_tokens, static_cast<hipStream_t>(stream));
+int pa_check_cache_write_inputs(const pa_tensor* slot_mapping, const pa_tensor* k_cache, void* stream) {
+    pa::abi::Cache c;
+    int st = pa::abi::cache(k_cache, &c, false);
     if (st != PA_OK) return st;
-    const int64_t num_slots = num_blocks * block_size;
+    const int64_t* sm = nullptr;
+    int64_t n = 0;
+    st = pa::abi::vec(slot_mapping, PA_DTYPE_I64, &sm, &n);
+    if (st != PA_OK) return st;
+    if (n == 0) return PA_OK;
+    std::vector<int64_t> slots;
+    st = copy_to_host(slots, sm, n, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+    const int64_t num_slots = c.N * c.bs;
     std::vector<int64_t> used;
     used.reserve(slots.size());
     for (const int64_t s : slots) {
@@ -76,55 +134,87 @@ int pa_check_cache_write_inputs(const int64_t* slot_mapping, int64_t num_tokens,
     return PA_OK;
 }
 
-int pa_check_decode_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                           int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+int pa_check_decode_inputs(const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* k_cache,
                            void* stream) {
-    if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
-    if (num_seqs == 0) return PA_OK;
-    if (!block_tables || !context_lens) return PA_ERR_NULL;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
+    pa::abi::Table t;
+    pa::abi::Cache c;
+    const int32_t* cl = nullptr;
+    int st = parse_decode_inputs(block_tables, context_lens, k_cache, &t, &c, &cl);
+    if (st != PA_OK || t.rows == 0) return st;
     std::vector<int32_t> ctx, table;
-    int st = copy_to_host(ctx, context_lens, num_seqs, s);
+    st = read_decode_inputs(t, cl, static_cast<hipStream_t>(stream), &ctx, &table);
     if (st != PA_OK) return st;
-    st = copy_to_host(table, block_tables, (int64_t)num_seqs * max_blocks_per_seq, s);
+    return check_tables(ctx, table, t.rows, t.cols, c.bs, c.N);
+}
+
+int pa_check_multi_inputs(const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* query_start,
+                          int32_t max_query_len, const pa_tensor* k_cache, void* stream) {
+    if (max_query_len < 0) return PA_ERR_SHAPE;
+    pa::abi::Table t;
+    pa::abi::Cache c;
+    const int32_t* cl = nullptr;
+    int st = parse_decode_inputs(block_tables, context_lens, k_cache, &t, &c, &cl);
     if (st != PA_OK) return st;
-    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
-    for (int32_t i = 0; i < num_seqs; ++i) {
-        const int64_t c = ctx[(size_t)i];
-        if (c < 0 || c > cap) return PA_ERR_PRECONDITION;
-        const int64_t nb = (c + block_size - 1) / block_size;
-        const int32_t* row = table.data() + (size_t)i * max_blocks_per_seq;
-        for (int64_t b = 0; b < nb; ++b)
-            if (row[b] < 0 || row[b] >= num_blocks) return PA_ERR_PRECONDITION;
+    const int32_t* qs = nullptr;
+    int64_t n = 0;
+    st = pa::abi::vec(query_start, PA_DTYPE_I32, &qs, &n);
+    if (st != PA_OK) return st;
+    if (n != t.rows + 1) return PA_ERR_SHAPE;
+    if (t.rows == 0) return PA_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> ctx, table, starts;
+    st = read_decode_inputs(t, cl, s, &ctx, &table);
+    if (st != PA_OK) return st;
+    st = check_tables(ctx, table, t.rows, t.cols, c.bs, c.N);
+    if (st != PA_OK) return st;
+    st = copy_to_host(starts, qs, n, s);
+    if (st != PA_OK) return st;
+    if (starts[0] != 0) return PA_ERR_PRECONDITION;
+    for (int64_t i = 0; i < t.rows; ++i) {
+        const int64_t q = (int64_t)starts[(size_t)i + 1] - starts[(size_t)i];
+        if (q < 0 || q > max_query_len || q > ctx[(size_t)i]) return PA_ERR_PRECONDITION;
     }
     return PA_OK;
 }
 
-int pa_check_cascade_inputs(const int32_t* prefix_tables, const int32_t* prefix_lens, const int32_t* group_start,
-                            int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks, int32_t num_seqs,
-                            int32_t block_size, int64_t num_blocks, void* stream) {
-    if (num_groups < 0 || max_group_size < 0 || max_prefix_blocks < 0 || num_seqs < 0 || block_size <= 0 ||
-        num_blocks <= 0)
-        return PA_ERR_SHAPE;
-    if (num_groups == 0) return PA_OK;
-    if (!group_start || !prefix_lens || (max_prefix_blocks > 0 && !prefix_tables)) return PA_ERR_NULL;
+int pa_check_cascade_inputs(const pa_tensor* prefix_tables, const pa_tensor* prefix_lens, const pa_tensor* group_start,
+                            int32_t max_group_size, int32_t num_seqs, const pa_tensor* k_cache, void* stream) {
+    if (max_group_size < 0 || num_seqs < 0) return PA_ERR_SHAPE;
+    pa::abi::Cache c;
+    int st = pa::abi::cache(k_cache, &c, false);
+    if (st != PA_OK) return st;
+    if (prefix_tables == nullptr) return PA_OK;  // no groups
+    pa::abi::Table t;
+    st = pa::abi::table(prefix_tables, &t);
+    if (st != PA_OK) return st;
+    const int64_t G = t.rows;
+    if (G == 0) return PA_OK;
+    const int32_t *pl = nullptr, *gs = nullptr;
+    int64_t n = 0;
+    st = pa::abi::vec(prefix_lens, PA_DTYPE_I32, &pl, &n);
+    if (st != PA_OK) return st;
+    if (n != G) return PA_ERR_SHAPE;
+    st = pa::abi::vec(group_start, PA_DTYPE_I32, &gs, &n);
+    if (st != PA_OK) return st;
+    if (n != G + 1) return PA_ERR_SHAPE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     std::vector<int32_t> starts, lens, table;
-    int st = copy_to_host(starts, group_start, (int64_t)num_groups + 1, s);
+    st = copy_to_host(starts, gs, G + 1, s);
     if (st != PA_OK) return st;
-    st = copy_to_host(lens, prefix_lens, num_groups, s);
+    st = copy_to_host(lens, pl, G, s);
     if (st != PA_OK) return st;
-    st = copy_to_host(table, prefix_tables, (int64_t)num_groups * max_prefix_blocks, s);
+    st = copy_table(table, t, s);
     if (st != PA_OK) return st;
-    if (starts[0] < 0 || starts[(size_t)num_groups] > num_seqs) return PA_ERR_PRECONDITION;
-    for (int32_t k = 0; k < num_groups; ++k) {
-        const int64_t n = (int64_t)starts[(size_t)k + 1] - starts[(size_t)k];
-        if (n < 0 || n > max_group_size) return PA_ERR_PRECONDITION;
-        const int64_t pl = lens[(size_t)k];
-        if (pl < 0 || pl % block_size != 0 || pl > (int64_t)max_prefix_blocks * block_size) return PA_ERR_PRECONDITION;
-        const int32_t* row = table.data() + (size_t)k * max_prefix_blocks;
-        for (int64_t b = 0; b < pl / block_size; ++b)
-            if (row[b] < 0 || row[b] >= num_blocks) return PA_ERR_PRECONDITION;
+    const int32_t bs = c.bs;
+    if (starts[0] < 0 || starts[(size_t)G] > num_seqs) return PA_ERR_PRECONDITION;
+    for (int64_t k = 0; k < G; ++k) {
+        const int64_t m = (int64_t)starts[(size_t)k + 1] - starts[(size_t)k];
+        if (m < 0 || m > max_group_size) return PA_ERR_PRECONDITION;
+        const int64_t len = lens[(size_t)k];
+        if (len < 0 || len % bs != 0 || len > (int64_t)t.cols * bs) return PA_ERR_PRECONDITION;
+        const int32_t* row = table.data() + (size_t)k * t.cols;
+        for (int64_t b = 0; b < len / bs; ++b)
+            if (row[b] < 0 || row[b] >= c.N) return PA_ERR_PRECONDITION;
     }
     return PA_OK;
 }

@@ -77,8 +77,9 @@ def decode_plan(workload: str, kv: str) -> dict:
     cap = {"const": lambda: ctx[1], "uniform": lambda: ctx[2], "lognormal": lambda: ctx[4],
            "list": lambda: max(ctx[1])}[ctx[0]]()
     mb = -(-int(cap) // s.block_size)
-    return pa.pa_decode_get_plan(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, mb,
-                                 pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN)
+    specs = pa.decode_specs(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, mb,
+                            pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN)
+    return pa.pa_decode_get_plan(*specs)
 
 
 def _plan_or_none(workload: str, kv: str):

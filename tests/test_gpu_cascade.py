@@ -64,11 +64,8 @@ class DeviceCascade:
         merge reads but no pass wrote shows up in the output."""
         b = self.b
         mg = b.max_group_size if max_group_size is None else max_group_size
-        S, Hq, D = b.q.shape
-        need = pa.pa_decode_cascade_workspace_size(
-            S, Hq, b.k_cache.shape[2], D, b.block_size, b.block_tables.shape[1], b.num_groups, mg,
-            b.prefix_tables.shape[1], pa.PA_KV_FP8_E4M3FN if self.fp8 else pa.PA_KV_BF16,
-            partition_tokens=partition_tokens)
+        need = pa.pa_decode_cascade_workspace_size(self.q, self.k_cache, self.block_tables, self.prefix_tables, mg,
+                                                   partition_tokens=partition_tokens)
         assert need > 0
         ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
         return pa.pa_decode_cascade(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
@@ -203,23 +200,25 @@ def test_cascade_argument_errors_and_checks(lib):
     note("cascade argument errors")
     S, Hq, D = b.q.shape
     ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
-    base = [d.q.data_ptr(), d.k_cache.data_ptr(), d.v_cache.data_ptr(), d.block_tables.data_ptr(),
-            d.context_lens.data_ptr(), d.prefix_tables.data_ptr(), d.prefix_lens.data_ptr(),
-            d.group_start.data_ptr(), b.scale, d.q.data_ptr()]
-    sizes = [S, Hq, 2, D, 16, b.block_tables.shape[1], b.num_blocks, 2, b.max_group_size,
-             b.prefix_tables.shape[1], 1, 1.0, 1.0]
+    out = torch.empty_like(d.q)
+    tensors = [d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.prefix_tables, d.prefix_lens,
+               d.group_start]
     o = pa._opts(partition_tokens=-1)
 
-    def call(ptrs=None, ws_ptr=ws.data_ptr(), ws_bytes=1 << 22):
-        p = list(base) if ptrs is None else ptrs
-        return lib.pa_decode_cascade(*p, *sizes, ws_ptr, ws_bytes, pa.ctypes.byref(o), None)
+    def call(descs=None, ws_ptr=ws.data_ptr(), ws_bytes=1 << 22):
+        ds = [pa.desc(t) for t in tensors] if descs is None else descs
+        return lib.pa_decode_cascade(*map(pa._ref, ds), b.scale, pa._ref(pa.desc(out)), b.max_group_size, 1.0, 1.0,
+                                     ws_ptr, ws_bytes, pa.ctypes.byref(o), None)
 
-    for i, code in ((5, pa.PA_ERR_NULL), (6, pa.PA_ERR_NULL), (7, pa.PA_ERR_NULL)):
-        p = list(base)
-        p[i] = None
-        assert call(p) == code
-        p[i] = base[i] + 2
-        assert call(p) == pa.PA_ERR_ALIGN
+    for i in (6, 7):  # with prefix tables, the other two group arrays are required
+        ds = [pa.desc(t) for t in tensors]
+        ds[i].data = None
+        assert call(ds) == pa.PA_ERR_NULL
+        ds[i].data = tensors[i].data_ptr() + 2
+        assert call(ds) == pa.PA_ERR_ALIGN
+    ds = [pa.desc(t) for t in tensors]
+    ds[5].data = tensors[5].data_ptr() + 2
+    assert call(ds) == pa.PA_ERR_ALIGN
     assert call(ws_bytes=256) == pa.PA_ERR_WORKSPACE
     assert call(ws_ptr=None) == pa.PA_ERR_WORKSPACE
     assert call(ws_ptr=ws.data_ptr() + 16) == pa.PA_ERR_ALIGN
@@ -227,7 +226,7 @@ def test_cascade_argument_errors_and_checks(lib):
     # the opt-in checks of the group arrays
     t = lambda a: torch.from_numpy(np.asarray(a, np.int32)).cuda()
     N, pt = b.num_blocks, d.prefix_tables
-    assert pa.pa_check_cascade_inputs(pt, d.prefix_lens, d.group_start, S, 2, N, 16) == pa.PA_OK
+    assert pa.pa_check_cascade_inputs(pt, d.prefix_lens, d.group_start, 2, S, d.k_cache) == pa.PA_OK
     bad_table = b.prefix_tables.copy()
     bad_table[1, 0] = N
     cases = {
@@ -240,4 +239,4 @@ def test_cascade_argument_errors_and_checks(lib):
     }
     for what, (a, l, s, mg) in cases.items():
         note(f"cascade check: {what}")
-        assert pa.pa_check_cascade_inputs(a, l, s, S, mg, N, 16) == pa.PA_ERR_PRECONDITION, what
+        assert pa.pa_check_cascade_inputs(a, l, s, mg, S, d.k_cache) == pa.PA_ERR_PRECONDITION, what

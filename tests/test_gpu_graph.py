@@ -75,9 +75,7 @@ def test_captured_step_replays_match_eager(lib, partition, kv):
     st_nk = torch.zeros((S, s.num_kv_heads, s.head_dim), dtype=torch.bfloat16, device=dev)
     st_nv = torch.zeros_like(st_nk)
     st_out = torch.zeros_like(st_q)
-    kvd = pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN
-    need = pa.pa_decode_workspace_size(S, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, MB, kvd,
-                                       partition_tokens=partition)
+    need = pa.pa_decode_workspace_size(st_q, kc_g, st_tab, partition_tokens=partition)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def load(step):

@@ -136,7 +136,7 @@ def test_decode_mqa_wide_groups(lib, Hq, Hkv, D, partition):
     ref = oracle.decode_workload(w)
     d = DeviceWorkload(w)
     note(f"mqa Hq={Hq} Hkv={Hkv} D={D} partition={partition}")
-    plan = pa.pa_decode_get_plan(w.spec.num_seqs, Hq, Hkv, D, 16, w.max_blocks_per_seq, partition_tokens=partition)
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, partition_tokens=partition)
     assert plan["variant"] == "mfma"
     got = host_bits(d.decode(partition_tokens=partition))
     torch.cuda.synchronize()

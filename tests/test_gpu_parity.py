@@ -15,21 +15,12 @@ import oracle
 import paged_kv_decode_mapping_amd as pa
 from paged_kv_decode_mapping_amd import workloads as W
 
-from _gpu_util import DeviceWorkload, compare, dev_bf16, dev_u8, host_bits, note
+from _gpu_util import REDUCED, DeviceWorkload, compare, dev_bf16, dev_u8, host_bits, note
 
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = (1e-2, 1e-3)
 FP8_TOL = (5e-2, 5e-3)
-
-REDUCED = {
-    "tiny": dict(),
-    "llama7b_mha": dict(num_seqs=3, context=("list", [512, 1000, 2048])),
-    "llama70b_gqa": dict(num_seqs=2, context=("list", [4096, 1234])),
-    "long_splitk": dict(num_seqs=2, context=("list", [5000, 2049])),
-    "mixed_batch": dict(num_seqs=10, context=("list", [16, 100, 511, 512, 513, 900, 3000, 40, 8192, 77])),
-}
-
 
 @pytest.fixture(scope="module")
 def lib(gpu):
@@ -50,15 +41,10 @@ def test_decode_matches_oracle(lib, name, variant):
             d.decode(variant=variant)
         return
     ref = _oracle(w)
-    note(f"decode {name} variant={variant} plan={pa.pa_decode_get_plan(*_sizes(w), variant=variant)}")
+    note(f"decode {name} variant={variant} plan={pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, variant=variant)}")
     out = d.decode(variant=variant)
     torch.cuda.synchronize()
     compare(host_bits(out), ref, *BF16_TOL)
-
-
-def _sizes(w):
-    s = w.spec
-    return (s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, w.max_blocks_per_seq)
 
 
 @pytest.mark.parametrize("name", ["tiny", "long_splitk", "mixed_batch"])
@@ -134,14 +120,16 @@ def test_full_size_mixed_batch_sampled(lib, schedule):
 
 @pytest.mark.parametrize("name", ["llama7b_mha", "llama70b_gqa", "long_splitk", "mixed_batch"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_full_size_step_sampled(lib, name, kv):
+@pytest.mark.parametrize("layout", ["page", "head_major"])
+def test_full_size_step_sampled(lib, name, kv, layout):
     """One step at the workload's full size, as the benchmark launches it:
     the cache write of the step's new tokens, then the decode with the
     library's own plan. The written rows must match the oracle's scatter
     bit for bit; the decode is checked on a sample of (sequence, KV head)
     units (the longest and the shortest context included) that the oracle
     computes one by one. fp8 caches are the oracle's quantisation of the
-    whole pool (scales amax / 448)."""
+    whole pool (scales amax / 448). Both pool layouts: the page's
+    [block, row, KV head, d] order and a head-major one."""
     w = W.make_workload(name)
     s = w.spec
     ks = vs = 1.0
@@ -150,8 +138,8 @@ def test_full_size_step_sampled(lib, name, kv):
         ks, vs = w.fp8_scales
         kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
         kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
-    d = DeviceWorkload(w, kc, vc)
-    note(f"full-size step {name} {kv} plan={pa.pa_decode_get_plan(*_sizes(w), pa.PA_KV_BF16 if kv == 'bf16' else pa.PA_KV_FP8_E4M3FN)}")
+    d = DeviceWorkload(w, kc, vc, layout=layout)
+    note(f"full-size step {name} {kv} {layout} plan={pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables)}")
     pa.pa_cache_write(d.new_k, d.new_v, d.slot_mapping, d.k_cache, d.v_cache, ks, vs)
     out = host_bits(d.decode(k_scale=ks, v_scale=vs))
     torch.cuda.synchronize()
@@ -161,7 +149,8 @@ def test_full_size_step_sampled(lib, name, kv):
     slots = w.slot_mapping[w.slot_mapping >= 0]
     idx = torch.from_numpy(slots).cuda()
     for dev_cache, host_cache in ((d.k_cache, kc), (d.v_cache, vc)):
-        rows = dev_cache.view(-1, s.num_kv_heads, s.head_dim)[idx].cpu()
+        bs = s.block_size
+        rows = dev_cache[idx // bs, idx % bs].cpu()  # [T, Hkv, D] through either layout
         rows = rows.numpy() if kv == "fp8" else rows.view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(rows, host_cache.reshape(-1, s.num_kv_heads, s.head_dim)[slots])
 

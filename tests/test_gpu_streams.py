@@ -39,8 +39,7 @@ def test_launches_follow_the_given_stream(lib, partition):
     oracle.cache_write(w.new_k, w.new_v, w.slot_mapping, kc_h, vc_h)
     ref = oracle.decode(w.q, kc_h, vc_h, w.block_tables, w.context_lens, w.scale)
 
-    need = pa.pa_decode_workspace_size(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
-                                       w.max_blocks_per_seq, partition_tokens=partition)
+    need = pa.pa_decode_workspace_size(d.q, d.k_cache, d.block_tables, partition_tokens=partition)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty(tuple(d.q.shape), dtype=torch.bfloat16, device="cuda")
     side = torch.cuda.Stream()
@@ -74,3 +73,29 @@ def test_launches_follow_the_given_stream(lib, partition):
     compare(host_bits(out), ref, 1e-2, 1e-3)
     rows = d.k_cache.view(-1, s.num_kv_heads, s.head_dim)[d.slot_mapping].cpu().view(torch.int16).numpy()
     assert np.array_equal(rows.view(np.uint16), kc_h.reshape(-1, s.num_kv_heads, s.head_dim)[w.slot_mapping])
+
+
+def test_binding_allocations_follow_the_named_stream(lib):
+    """With stream= and neither workspace nor out given, the binding
+    allocates both on that stream. Right after the call, the current stream
+    allocates blocks of the same sizes and overwrites them: had the
+    workspace or out come from the current stream's pool and been released
+    on return, those blocks could be handed out again and overwritten while
+    the side stream's work list, partials and merge still use them."""
+    w = W.make_workload("long_splitk", num_seqs=2, context=("list", [32768, 20000]))
+    d = DeviceWorkload(w)
+    ref = oracle.decode_workload(w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    need = pa.pa_decode_workspace_size(d.q, d.k_cache, d.block_tables, partition_tokens=512)
+    assert need > 0
+    note("binding allocations on the named stream")
+    for _ in range(3):
+        out = pa.pa_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, w.scale,
+                           partition_tokens=512, stream=side)
+        junk_ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+        junk_out = torch.full(tuple(out.shape), float("nan"), dtype=torch.bfloat16, device="cuda")
+        side.synchronize()
+        torch.cuda.synchronize()
+        compare(host_bits(out), ref, 1e-2, 1e-3)
+        del junk_ws, junk_out

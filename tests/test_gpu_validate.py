@@ -33,6 +33,11 @@ def debug_validate():
         os.environ["PA_DEBUG_VALIDATE"] = old
 
 
+def _pool(N, bs, Hkv=2, D=64):
+    """The shape of a pool (the checks read its block count and block size)."""
+    return pa.TensorSpec((N, bs, Hkv, D), pa.PA_DTYPE_BF16)
+
+
 SMALL = {
     "tiny": dict(),
     "mixed_batch": dict(num_seqs=10, context=("list", [16, 100, 511, 512, 513, 900, 3000, 40, 8192, 77])),
@@ -46,8 +51,8 @@ def test_generated_workloads_pass(lib, name):
     d = DeviceWorkload(w)
     note(f"checks accept {name}")
     bs = w.spec.block_size
-    assert pa.pa_check_cache_write_inputs(d.slot_mapping, w.num_blocks, bs) == pa.PA_OK
-    assert pa.pa_check_decode_inputs(d.block_tables, d.context_lens, w.num_blocks, bs) == pa.PA_OK
+    assert pa.pa_check_cache_write_inputs(d.slot_mapping, d.k_cache) == pa.PA_OK
+    assert pa.pa_check_decode_inputs(d.block_tables, d.context_lens, d.k_cache) == pa.PA_OK
 
 
 def test_bad_slots_are_reported(lib):
@@ -59,9 +64,9 @@ def test_bad_slots_are_reported(lib):
     for what, slots in cases.items():
         note(f"slot check: {what}")
         t = torch.tensor(slots, dtype=torch.int64, device="cuda")
-        assert pa.pa_check_cache_write_inputs(t, N, bs) == pa.PA_ERR_PRECONDITION, what
+        assert pa.pa_check_cache_write_inputs(t, _pool(N, bs)) == pa.PA_ERR_PRECONDITION, what
     ok = torch.tensor([-1, -7, 0, N * bs - 1, 200], dtype=torch.int64, device="cuda")
-    assert pa.pa_check_cache_write_inputs(ok, N, bs) == pa.PA_OK
+    assert pa.pa_check_cache_write_inputs(ok, _pool(N, bs)) == pa.PA_OK
 
 
 def test_bad_tables_and_lengths_are_reported(lib):
@@ -70,7 +75,11 @@ def test_bad_tables_and_lengths_are_reported(lib):
     ctx = np.array([64, 32, 1], dtype=np.int32)  # row 1 never reads its bad tail entries
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     note("decode check: valid tables")
-    assert pa.pa_check_decode_inputs(t(good), t(ctx), N, bs) == pa.PA_OK
+    assert pa.pa_check_decode_inputs(t(good), t(ctx), _pool(N, bs)) == pa.PA_OK
+    # a table that is a view with a row stride wider than its width
+    wide = np.full((3, 9), -5, np.int32)
+    wide[:, :4] = good
+    assert pa.pa_check_decode_inputs(t(wide)[:, :4], t(ctx), _pool(N, bs)) == pa.PA_OK
     bad_tables = good.copy()
     bad_tables[1, 1] = N  # covers tokens 16..31 of a 32-token context
     neg_tables = good.copy()
@@ -79,7 +88,24 @@ def test_bad_tables_and_lengths_are_reported(lib):
                          ("context past the row", good, np.array([65, 32, 1], np.int32)),
                          ("negative context", good, np.array([64, -1, 1], np.int32))]:
         note(f"decode check: {what}")
-        assert pa.pa_check_decode_inputs(t(tab), t(c), N, bs) == pa.PA_ERR_PRECONDITION, what
+        assert pa.pa_check_decode_inputs(t(tab), t(c), _pool(N, bs)) == pa.PA_ERR_PRECONDITION, what
+
+
+def test_bad_query_counts_are_reported(lib):
+    """pa_check_multi_inputs: a sequence's query tokens are among its cached
+    ones, no more than max_query_len of them, and query_start rises from 0."""
+    N, bs = 32, 16
+    tab = np.arange(12, dtype=np.int32).reshape(3, 4)
+    ctx = np.array([64, 3, 20], dtype=np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.int32))).cuda()
+    note("multi check: valid query counts")
+    assert pa.pa_check_multi_inputs(t(tab), t(ctx), t([0, 4, 7, 8]), 4, _pool(N, bs)) == pa.PA_OK
+    for what, qs, maxq in [("more queries than context", [0, 1, 5, 6], 4),
+                           ("more than max_query_len", [0, 5, 6, 7], 4),
+                           ("falling offsets", [0, 4, 3, 5], 4),
+                           ("not starting at 0", [1, 2, 3, 4], 4)]:
+        note(f"multi check: {what}")
+        assert pa.pa_check_multi_inputs(t(tab), t(ctx), t(qs), maxq, _pool(N, bs)) == pa.PA_ERR_PRECONDITION, what
 
 
 def test_debug_switch_stops_hot_path_calls(lib, debug_validate):
