@@ -480,23 +480,194 @@ def bench_copy_blocks(args, w, k_cache, v_cache, kv_b: int, kq=None, vq=None) ->
     return 0
 
 
+# The other named configurations, measured in the same run after the
+# headline one (decode alone, HIP events per launch): the 7B-shaped MHA
+# batch, the long-context batch at its stated 512-token partitions and at
+# the library's own plan, the mixed continuous batch with bf16 and fp8
+# caches, and the 70B-shaped batch with fp8 caches.
+PER_CONFIG = [
+    ("llama7b_mha", "bf16", 0),
+    ("long_splitk", "bf16", 512),
+    ("long_splitk", "bf16", 0),
+    ("mixed_batch", "bf16", 0),
+    ("mixed_batch", "fp8", 0),
+    ("llama70b_gqa", "fp8", 0),
+]
+EVICT_BELOW_BYTES = 1 << 30  # KV smaller than this could stay in the 256 MB Infinity Cache between steps
+MIN_WARMUP_S = 0.2           # clocks ramp during the first ~10 ms of GPU work after host-side set-up
+
+
+class DeviceBatch:
+    """One workload's inputs resident on the device: q, the two caches (bf16,
+    or fp8 codes written by the library's own quantising cache write) in the
+    requested layout, tables, lengths, and the step's new tokens."""
+
+    def __init__(self, w, kv: str, layout: str, dev, host_codes: bool = False):
+        import torch
+        import paged_kv_decode_mapping_amd as pa
+        s = w.spec
+        self.w, self.kv, self.layout = w, kv, layout
+        self.kv_b = 2 if kv == "bf16" else 1
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.q = bf16(w.q)
+        k_cache, v_cache = bf16(w.k_cache), bf16(w.v_cache)
+        self.tables = torch.from_numpy(w.block_tables).to(dev)
+        self.ctx = torch.from_numpy(w.context_lens).to(dev)
+        self.new_k, self.new_v = bf16(w.new_k), bf16(w.new_v)
+        self.slots = torch.from_numpy(w.slot_mapping).to(dev)
+        self.k_scale = self.v_scale = 1.0
+        self.kq = self.vq = None
+        if kv == "fp8":
+            self.k_scale, self.v_scale = w.fp8_scales
+            rows = w.num_blocks * s.block_size
+            all_slots = torch.arange(rows, dtype=torch.int64, device=dev)
+            kc8 = torch.empty((w.num_blocks, s.block_size, s.num_kv_heads, s.head_dim), dtype=torch.uint8,
+                              device=dev)
+            vc8 = torch.empty_like(kc8)
+            pa.pa_cache_write(k_cache.view(rows, s.num_kv_heads, s.head_dim),
+                              v_cache.view(rows, s.num_kv_heads, s.head_dim), all_slots, kc8, vc8,
+                              self.k_scale, self.v_scale)
+            torch.cuda.synchronize()
+            del k_cache, v_cache
+            k_cache, v_cache = kc8, vc8
+            if host_codes:
+                self.kq, self.vq = kc8.cpu().numpy(), vc8.cpu().numpy()
+        if layout == "head_major":
+            # the same logical pool stored [N, Hkv, bs, D]: each (block, KV
+            # head) tile is one contiguous run; passed as the permuted view
+            def to_head_major(t):
+                hm = torch.empty((t.shape[0], t.shape[2], t.shape[1], t.shape[3]), dtype=t.dtype, device=dev)
+                hm.copy_(t.permute(0, 2, 1, 3))
+                return hm.permute(0, 2, 1, 3)
+            k_cache, v_cache = to_head_major(k_cache), to_head_major(v_cache)
+            torch.cuda.synchronize()
+        self.k_cache, self.v_cache = k_cache, v_cache
+
+    def unique_kv_bytes(self) -> int:
+        w = self.w
+        return 2 * w.unique_blocks * w.spec.block_size * w.spec.num_kv_heads * w.spec.head_dim * self.kv_b
+
+
+def time_decode(b: "DeviceBatch", opts: dict, steps: int, warmup: int, evict: bool):
+    """Per-launch decode times (ms, HIP events on the launch stream) after a
+    warm-up of at least `warmup` launches and MIN_WARMUP_S seconds. With
+    evict, a 512 MiB scratch write before each timed launch (outside its
+    events) clears the Infinity Cache, as every other layer's KV would."""
+    import torch
+    import paged_kv_decode_mapping_amd as pa
+    plan = pa.pa_decode_get_plan(b.q, b.k_cache, b.tables, **opts)
+    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=b.q.device)
+    out = torch.empty_like(b.q)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        pa.pa_decode(b.q, b.k_cache, b.v_cache, b.tables, b.ctx, b.w.scale, out, k_scale=b.k_scale,
+                     v_scale=b.v_scale, workspace=ws, **opts)
+
+    warm_up(run, warmup)
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device=b.q.device) if evict else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, e in ev:
+        if scratch is not None:
+            scratch.add_(1)
+        a.record(stream)
+        run()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(e) for a, e in ev]), plan, out
+
+
+def warm_up(fn, n: int) -> None:
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or time.perf_counter() - t0 < MIN_WARMUP_S:
+        fn()
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def fp8_accuracy(b: "DeviceBatch", out, n_units: int = 24) -> dict:
+    """The fp8-KV decode against the float64 oracle on the values before
+    quantisation (the bf16 caches), and against the oracle on the same codes,
+    on sampled (sequence, KV head) units: max and mean absolute error."""
+    import oracle
+    w, s = b.w, b.w.spec
+    rng = np.random.default_rng(9)
+    units = np.unique(np.concatenate([rng.choice(s.num_seqs * s.num_kv_heads, min(n_units, s.num_seqs * s.num_kv_heads),
+                                                 replace=False),
+                                      [int(np.argmax(w.context_lens)) * s.num_kv_heads]]))
+    bits = out.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    g = s.group
+    got = np.stack([bits[u // s.num_kv_heads, (u % s.num_kv_heads) * g:(u % s.num_kv_heads + 1) * g] for u in units])
+    got = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref_v = oracle.decode_workload(w, units=units)
+    ref_c = oracle.decode_workload(w, units=units, kv_dtype=oracle.KV_FP8_E4M3FN, k_cache=b.kq, v_cache=b.vq,
+                                   k_scale=b.k_scale, v_scale=b.v_scale)
+    e_v, e_c = np.abs(got - ref_v), np.abs(got - ref_c)
+    return {"units": int(len(units)), "vs_bf16_values": {"max": round(float(e_v.max()), 6),
+                                                         "mean": round(float(e_v.mean()), 7)},
+            "vs_fp8_codes": {"max": round(float(e_c.max()), 6), "mean": round(float(e_c.mean()), 7)}}
+
+
+def per_config(args, dev, skip) -> list:
+    """Decode of every other named configuration in this run."""
+    import torch
+    from paged_kv_decode_mapping_amd import workloads as W
+    res = []
+    for name, kv, part in PER_CONFIG:
+        if (name, kv, part) == skip:
+            continue
+        t0 = time.time()
+        w = W.make_workload(name)
+        b = DeviceBatch(w, kv, args.layout, dev, host_codes=(kv == "fp8"))
+        evict = b.unique_kv_bytes() < EVICT_BELOW_BYTES
+        ms, plan, out = time_decode(b, dict(partition_tokens=part), max(args.steps, 20), args.warmup, evict)
+        nbytes = decode_bytes(w, b.kv_b)
+        avg = float(ms.mean())
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        entry = {"workload": f"{name}: {w.spec.description}", "kv_cache": kv, "layout": args.layout,
+                 "partition_tokens_asked": part, "plan": plan,
+                 "decode_us": {"avg": round(avg * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                               "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+                 "bytes": nbytes, "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                 "decode_tokens_per_s": round(w.spec.num_seqs / (avg * 1e-3), 1),
+                 "cache_evicted_between_launches": evict}
+        if kv == "fp8":
+            entry["fp8_accuracy"] = fp8_accuracy(b, out)
+        if not args.no_cpu_baseline:
+            entry["cpu_baseline"] = cpu_baseline(w, kv, b.kq, b.vq, min_s=2.0, budget_s=4.0)
+        log(f"per-config {name} {kv} P={part}: {avg * 1e3:.1f} us, {gbps:.0f} GB/s = {gbps / HBM_PEAK_GBPS:.1%} "
+            f"({time.time() - t0:.1f} s)")
+        res.append(entry)
+        del b, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the first ~10 ms of GPU work after the host-side set-up run slow (clocks
-    # ramping): 5 warm-up steps left the fp8 decode at 192 us with a wide
-    # spread, 50 steps 181 us (p90 185)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="warm-up steps (at least; warm-up also lasts at least 0.2 s)")
     ap.add_argument("--workload", default="llama70b_gqa")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16")
     ap.add_argument("--layout", choices=["page", "head_major"], default="page",
                     help="pool layout: the page's [block, row, KV head, d] order, or head-major "
                          "[block, KV head, row, d] passed through strides")
     ap.add_argument("--variant", default="auto")
-    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="tokens per split-K partition (default: the partition the workload names, "
+                         "else the library's plan; -1 = never split)")
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true", help="skip the other configurations")
     ap.add_argument("--prefetch", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
     ap.add_argument("--heads-per-tile", type=int, default=0, help="KV heads per MFMA tile (0 = the plan's choice)")
@@ -531,58 +702,27 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.op == "stream":
         return bench_stream(args, dev)
-    log(f"generating workload {args.workload} ({args.kv} KV)")
+    if args.partition is None:
+        args.partition = W.SPECS[args.workload].partition_tokens if args.workload in W.SPECS else 0
+    log(f"generating workload {args.workload} ({args.kv} KV, {args.layout} layout)")
     t0 = time.time()
     w = W.make_workload(args.workload)
     s = w.spec
     log(f"generated in {time.time() - t0:.1f} s: {s.num_seqs} seqs, pool {w.num_blocks} blocks, "
         f"{w.k_cache.nbytes / 1e9:.2f} GB per cache")
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    q = bf16(w.q)
-    k_cache = bf16(w.k_cache)
-    v_cache = bf16(w.v_cache)
-    tables = torch.from_numpy(w.block_tables).to(dev)
-    ctx = torch.from_numpy(w.context_lens).to(dev)
-    new_k, new_v = bf16(w.new_k), bf16(w.new_v)
-    slots = torch.from_numpy(w.slot_mapping).to(dev)
-    k_scale = v_scale = 1.0
-    kq = vq = None
-    if args.kv == "fp8":
-        k_scale, v_scale = w.fp8_scales
-        # quantise the whole pool on the GPU with the product's own cache write
-        rows = w.num_blocks * s.block_size
-        all_slots = torch.arange(rows, dtype=torch.int64, device=dev)
-        kc8 = torch.empty((w.num_blocks, s.block_size, s.num_kv_heads, s.head_dim), dtype=torch.uint8, device=dev)
-        vc8 = torch.empty_like(kc8)
-        pa.pa_cache_write(k_cache.view(rows, s.num_kv_heads, s.head_dim), v_cache.view(rows, s.num_kv_heads, s.head_dim),
-                          all_slots, kc8, vc8, k_scale, v_scale)
-        torch.cuda.synchronize()
-        del k_cache, v_cache
-        k_cache, v_cache = kc8, vc8
-        if not args.no_cpu_baseline:
-            kq, vq = kc8.cpu().numpy(), vc8.cpu().numpy()
-    if args.layout == "head_major":
-        # the same logical pool stored [N, Hkv, bs, D]: each (block, KV head)
-        # tile is one contiguous run; passed as the permuted [N, bs, Hkv, D] view
-        def to_head_major(t):
-            hm = torch.empty((t.shape[0], t.shape[2], t.shape[1], t.shape[3]), dtype=t.dtype, device=dev)
-            hm.copy_(t.permute(0, 2, 1, 3))
-            return hm.permute(0, 2, 1, 3)
-        k_cache, v_cache = to_head_major(k_cache), to_head_major(v_cache)
-        torch.cuda.synchronize()
-    kv_b = 2 if args.kv == "bf16" else 1
+    b = DeviceBatch(w, args.kv, args.layout, dev, host_codes=(args.kv == "fp8"))
+    q, k_cache, v_cache, tables, ctx = b.q, b.k_cache, b.v_cache, b.tables, b.ctx
+    new_k, new_v, slots, k_scale, v_scale, kq, vq = b.new_k, b.new_v, b.slots, b.k_scale, b.v_scale, b.kq, b.vq
+    kv_b = b.kv_b
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, w, k_cache, v_cache, kv_b, kq, vq)
     if args.op == "multi":
         return bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b, k_scale, v_scale, kq, vq)
     if args.op == "cascade":
         return bench_cascade(args, w, k_cache, v_cache, kv_b, k_scale, v_scale, kq, vq)
-    plan = pa.pa_decode_get_plan(q, k_cache, tables,
-                                 partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                                 prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
+    opts = dict(partition_tokens=args.partition, variant=args.variant, waves=args.waves, prefetch=args.prefetch,
+                schedule=args.schedule, heads_per_tile=args.heads_per_tile)
+    plan = pa.pa_decode_get_plan(q, k_cache, tables, **opts)
     log(f"plan {plan}")
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -599,8 +739,7 @@ def main() -> int:
         if ev is not None:
             ev[1].record(stream)
         pa.pa_decode(q, k_cache, v_cache, tables, ctx, w.scale, out, k_scale=k_scale, v_scale=v_scale,
-                     workspace=ws, partition_tokens=args.partition, variant=args.variant, waves=args.waves,
-                     prefetch=args.prefetch, schedule=args.schedule, heads_per_tile=args.heads_per_tile)
+                     workspace=ws, **opts)
         if ev is not None:
             ev[2].record(stream)
 
@@ -614,19 +753,32 @@ def main() -> int:
         log(f"copy probe: {n} bytes read, {n} bytes written")
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    # the practical read ceiling on this GPU: the library's streaming-read
+    # probe over 2 GiB with the decode kernels' non-temporal loads; run
+    # first, it also brings the clocks up before the warm-up
+    stream_gbps = stream_read_gbps(dev, 2 << 30, 10)
+    log(f"streaming read {stream_gbps:.0f} GB/s")
+
+    t_w = time.perf_counter()
+    warm_up(step, args.warmup)
+    warm_s = time.perf_counter() - t_w
+    evict = b.unique_kv_bytes() < EVICT_BELOW_BYTES
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device=dev) if evict else None
+    log(f"warm-up done ({warm_s * 1e3:.0f} ms); timing {args.steps} steps"
+        + (" (caches evicted between steps)" if evict else ""))
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.add_(1)
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     decode_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    if scratch is not None:  # the scratch writes are not part of the step
+        wall = float((write_ms + decode_ms).sum()) * 1e-3
     ms_per_step = wall * 1e3 / args.steps
     dec_b = decode_bytes(w, kv_b)
     wr_b = write_bytes(w, kv_b)
@@ -635,21 +787,23 @@ def main() -> int:
     step_gbps = (dec_b + wr_b) / (ms_per_step * 1e-3) / 1e9
     log(f"decode avg {dec_avg * 1e3:.1f} us (p10 {np.percentile(decode_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(decode_ms, 90) * 1e3:.1f}), write avg {write_ms.mean() * 1e3:.1f} us, "
-        f"step {ms_per_step * 1e3:.1f} us, decode {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of peak")
+        f"step {ms_per_step * 1e3:.1f} us, decode {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of peak, "
+        f"{achieved / stream_gbps:.1%} of the streaming read")
 
-    # the practical read ceiling on this GPU, for context: the library's
-    # streaming-read probe over 2 GiB with the decode kernels' non-temporal loads
-    stream_gbps = stream_read_gbps(dev, 2 << 30, 10)
-    log(f"streaming read {stream_gbps:.0f} GB/s; decode at {achieved / stream_gbps:.1%} of it")
-
+    acc = fp8_accuracy(b, out) if args.kv == "fp8" else None
+    if acc:
+        log(f"fp8 accuracy {acc}")
     base = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         base = cpu_baseline(w, args.kv, kq, vq)
         log(f"cpu baseline {base}")
-
-    traffic = load_traffic(args.workload, args.kv, plan)
+    traffic = load_traffic(args.workload, args.kv, plan) if args.layout == "page" else None
     tok_s = s.num_seqs / (ms_per_step * 1e-3)
+    head = dict(workload=args.workload, kv=args.kv, part=args.partition)
+    del b, q, k_cache, v_cache, out, ws
+    torch.cuda.empty_cache()
+    others = [] if args.no_per_config else per_config(args, dev, (head["workload"], head["kv"], head["part"]))
     res = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + decode tokens/s",
         "value": round(step_gbps, 2),
@@ -657,6 +811,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_ms": round(warm_s * 1e3, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -677,13 +832,16 @@ def main() -> int:
         "decode_us": {"avg": round(dec_avg * 1e3, 2), "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                       "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
         "cache_write_us": round(float(write_ms.mean()) * 1e3, 2),
+        "cache_evicted_between_steps": evict,
         "stream_read_gbps": round(stream_gbps, 1),
         "decode_frac_of_stream_read": round(achieved / stream_gbps, 4),
         "bytes": {"decode": dec_b, "cache_write": wr_b},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "pa_decode (decode kernel%s)" % (" + merge" if plan["num_partitions"] > 1 else "")},
+        "fp8_accuracy": acc,
         "cpu_baseline": base,
+        "per_config": others,
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -43,8 +43,13 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        # PA_ORACLE_LIB names another build of pa_oracle.c to load instead
+        # (the sanitizer test's instrumented one)
+        path = os.environ.get("PA_ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB_PATH
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]

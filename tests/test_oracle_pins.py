@@ -531,6 +531,21 @@ def test_copy_blocks_rejects_bad_pairs():
         oracle.copy_blocks(kc, vc, [[0, 2], [1, 2]])
 
 
+# ---------------------------------------------------------------- bf16 codec
+
+def test_bf16_decode_all_patterns_match_torch():
+    """Pin: torch's bfloat16 -> float64 over all 65,536 bit patterns (NaN
+    payloads aside: every NaN pattern decodes to a NaN)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert nan.sum() == 2 * 127 and got[0x3F80] == 1.0 and got[0x0001] == 2.0 ** -133
+    assert np.isinf(got[0x7F80]) and got[0xFF80] == -np.inf and math.copysign(1.0, got[0x8000]) == -1.0
+
+
 # ---------------------------------------------------------------- fp8 codec
 
 def test_e4m3fn_decode_all_codes_match_torch():
