@@ -5,9 +5,10 @@
  * pa_tensor: a device address plus element type, shape and element strides.
  * Every call is asynchronous on `stream` (a hipStream_t passed as void*,
  * NULL = the default stream) and returns once its launches are queued. The
- * caller owns every buffer, including the split-K workspace; the library
- * allocates no device memory and keeps no state between calls beyond a
- * per-device CU count.
+ * caller owns every buffer, including the split-K workspace; apart from
+ * pa_decode_no_alloc's static scratch (below) the library allocates no
+ * device memory and keeps no state between calls beyond a per-device CU
+ * count.
  *
  * Pages cited (titles as printed at the top of each page):
  *   Tutorial = «大模型推理优化与加速完全教程» (LLM inference optimisation tutorial)
@@ -80,6 +81,7 @@ extern "C" {
 #define PA_ERR_DEVICE (-8)      /* the current device could not be queried */
 #define PA_ERR_PRECONDITION (-9) /* a device-side input breaks a precondition (checked calls only) */
 #define PA_ERR_LAYOUT (-10)     /* strides outside the layout rules above */
+#define PA_ERR_SCRATCH (-11)    /* pa_decode_no_alloc: the plan needs more than the static scratch */
 
 /* Element types of a pa_tensor. */
 #define PA_DTYPE_BF16 1
@@ -228,6 +230,28 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_c
               const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
               const pa_tensor* out, float k_scale, float v_scale,
               void* workspace, size_t workspace_bytes, const pa_decode_opts* opts, void* stream);
+
+/*
+ * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same operation, arguments and kernels, with the
+ * work list and split-K partials in a static scratch array inside the
+ * library instead of a caller workspace. The array is PA_NO_ALLOC_SCRATCH
+ * bytes per device, allocated by the HIP runtime when the library's code is
+ * loaded on that device and held until the process ends; its address is
+ * looked up once per device, on the first call there. The call allocates
+ * nothing. A plan that needs more (pa_decode_workspace_size above the limit)
+ * returns PA_ERR_SCRATCH before launching. Every call on a device shares
+ * that device's array: calls that may overlap on one device (different
+ * streams without ordering, or concurrent host threads) race on it and give
+ * unspecified results. Nothing in the array needs clearing between calls:
+ * each launch writes every word it later reads.
+ */
+#define PA_NO_ALLOC_SCRATCH ((size_t)32 << 20)
+int pa_decode_no_alloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                       const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                       const pa_tensor* out, float k_scale, float v_scale, const pa_decode_opts* opts,
+                       void* stream);
 
 /*
  * pa_decode_get_plan -- the launch plan pa_decode would use for these

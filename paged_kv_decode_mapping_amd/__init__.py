@@ -30,6 +30,8 @@ PA_ERR_LAUNCH = -7
 PA_ERR_DEVICE = -8
 PA_ERR_PRECONDITION = -9
 PA_ERR_LAYOUT = -10
+PA_ERR_SCRATCH = -11
+PA_NO_ALLOC_SCRATCH = 32 << 20
 PA_DTYPE_BF16 = 1
 PA_DTYPE_FP8_E4M3FN = 2
 PA_DTYPE_I32 = 4
@@ -121,6 +123,7 @@ def load_library(path: Optional[str] = None):
         "pa_cache_write": ([T, T, T, T, T, f32, f32, P], ctypes.c_int),
         "pa_copy_blocks": ([T, T, T, P], ctypes.c_int),
         "pa_decode": ([T, T, T, T, T, f32, T, f32, f32, P, sz, O, P], ctypes.c_int),
+        "pa_decode_no_alloc": ([T, T, T, T, T, f32, T, f32, f32, O, P], ctypes.c_int),
         "pa_decode_get_plan": ([T, T, T, O, ctypes.POINTER(pa_decode_plan)], ctypes.c_int),
         "pa_decode_workspace_size": ([T, T, T, O], sz),
         "pa_decode_multi": ([T, T, T, T, T, T, f32, T, i32, f32, f32, P, sz, i32, P], ctypes.c_int),
@@ -288,6 +291,24 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
                        float(v_scale), ws_ptr, ws_bytes, ctypes.byref(o), _stream_ptr(stream))
     if st != PA_OK:
         raise PAError(st, "pa_decode")
+    return out
+
+
+def pa_decode_no_alloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
+                       k_scale: float = 1.0, v_scale: float = 1.0, partition_tokens: int = 0, variant="auto",
+                       waves: int = 0, prefetch: int = 0, schedule: int = 0, heads_per_tile: int = 0, stream=None):
+    """pa_decode with the library's static scratch as its workspace: no
+    device allocation anywhere, here or in the library (so `out` must be
+    given). Raises PAError (PA_ERR_SCRATCH) when the plan needs more than
+    PA_NO_ALLOC_SCRATCH bytes. Calls that overlap on one device race on the
+    scratch."""
+    lib = load_library()
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
+    d = [desc(t) for t in (q, k_cache, v_cache, block_tables, context_lens, out)]
+    st = lib.pa_decode_no_alloc(*map(_ref, d[:5]), float(scale), _ref(d[5]), float(k_scale), float(v_scale),
+                                ctypes.byref(o), _stream_ptr(stream))
+    if st != PA_OK:
+        raise PAError(st, "pa_decode_no_alloc")
     return out
 
 

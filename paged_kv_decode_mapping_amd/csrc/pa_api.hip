@@ -906,6 +906,7 @@ const char* pa_strerror(int status) {
         case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a copy";
         case PA_ERR_DEVICE: return "the current HIP device could not be queried";
         case PA_ERR_PRECONDITION: return "a device-side input violates a precondition (slots, tables or lengths)";
+        case PA_ERR_SCRATCH: return "the plan needs more workspace than pa_decode_no_alloc's static scratch holds";
         case PA_ERR_LAYOUT: return "unsupported strides (innermost dimension not contiguous, not 16-byte multiples, "
                                    "overlapping, or a block too large)";
         default: return "unknown status";

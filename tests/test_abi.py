@@ -51,7 +51,7 @@ def test_binding_constants_match_the_header():
 
 
 def test_status_strings(lib):
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = pa.strerror(code)
         assert s and s != "unknown status"
     assert pa.strerror(-99) == "unknown status"
