@@ -17,7 +17,9 @@ import os
 from typing import NamedTuple, Optional, Tuple
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
+# PA_LIBRARY names another build of libpa.so to load instead (the sanitizer
+# test's instrumented host code)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(PKG_DIR, "libpa.so")
 
 PA_OK = 0
 PA_ERR_NULL = -1

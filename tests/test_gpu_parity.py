@@ -164,6 +164,42 @@ def test_full_size_step_sampled(lib, name, kv, layout):
     compare(got, ref, *tol)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("layout", ["page", "head_major"])
+def test_full_size_long_contexts_at_512_token_partitions(lib, kv, layout):
+    """The long-context batch as stated: 4 sequences of 32k-128k tokens split
+    into flash-decoding partitions of 512 tokens (up to 256 per row) merged by
+    log-sum-exp, after the step's cache write. Units are sampled over every
+    sequence, each KV head of the 131,072-token one included."""
+    w = W.make_workload("long_splitk")
+    s = w.spec
+    assert s.partition_tokens == 512
+    ks = vs = 1.0
+    kc, vc, kvd, tol = w.k_cache, w.v_cache, oracle.KV_BF16, BF16_TOL
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
+    d = DeviceWorkload(w, kc, vc, layout=layout)
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, partition_tokens=512)
+    assert plan["partition_tokens"] == 512 and plan["num_partitions"] == 256
+    note(f"full-size long_splitk P=512 {kv} {layout} plan={plan}")
+    pa.pa_cache_write(d.new_k, d.new_v, d.slot_mapping, d.k_cache, d.v_cache, ks, vs)
+    out = host_bits(d.decode(k_scale=ks, v_scale=vs, partition_tokens=512))
+    torch.cuda.synchronize()
+    oracle.cache_write(w.new_k, w.new_v, w.slot_mapping, kc, vc, kv_dtype=kvd, k_scale=ks, v_scale=vs)
+    longest = int(np.argmax(w.context_lens))
+    rng = np.random.default_rng(13)
+    units = np.unique(np.concatenate([rng.choice(s.num_seqs * s.num_kv_heads, 12, replace=False),
+                                      np.arange(s.num_seqs) * s.num_kv_heads + np.arange(s.num_seqs) % s.num_kv_heads,
+                                      longest * s.num_kv_heads + np.arange(s.num_kv_heads)]))
+    assert len(set(units // s.num_kv_heads)) == s.num_seqs
+    ref = oracle.decode_workload(w, units=units, kv_dtype=kvd, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+    g = s.group
+    got = np.stack([out[u // s.num_kv_heads, (u % s.num_kv_heads) * g:(u % s.num_kv_heads + 1) * g] for u in units])
+    compare(got, ref, *tol)
+
+
 @pytest.mark.parametrize("bs", [32, 64, 256, 1024])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_other_block_sizes(lib, bs, kv):
