@@ -616,7 +616,8 @@ def fp8_accuracy(b: "DeviceBatch", out, n_units: int = 24) -> dict:
 
 
 def per_config(args, dev, skip) -> list:
-    """Decode of every other named configuration in this run."""
+    """Decode of every other named configuration in this run, in both pool
+    layouts (the page's [block, row, KV head, d] order and head-major)."""
     import torch
     from paged_kv_decode_mapping_amd import workloads as W
     res = []
@@ -625,28 +626,35 @@ def per_config(args, dev, skip) -> list:
             continue
         t0 = time.time()
         w = W.make_workload(name)
-        b = DeviceBatch(w, kv, args.layout, dev, host_codes=(kv == "fp8"))
-        evict = b.unique_kv_bytes() < EVICT_BELOW_BYTES
-        ms, plan, out = time_decode(b, dict(partition_tokens=part), max(args.steps, 20), args.warmup, evict)
-        nbytes = decode_bytes(w, b.kv_b)
-        avg = float(ms.mean())
-        gbps = nbytes / (avg * 1e-3) / 1e9
-        entry = {"workload": f"{name}: {w.spec.description}", "kv_cache": kv, "layout": args.layout,
-                 "partition_tokens_asked": part, "plan": plan,
-                 "decode_us": {"avg": round(avg * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
-                               "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
-                 "bytes": nbytes, "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                 "decode_tokens_per_s": round(w.spec.num_seqs / (avg * 1e-3), 1),
-                 "cache_evicted_between_launches": evict}
-        if kv == "fp8":
-            entry["fp8_accuracy"] = fp8_accuracy(b, out)
-        if not args.no_cpu_baseline:
-            entry["cpu_baseline"] = cpu_baseline(w, kv, b.kq, b.vq, min_s=2.0, budget_s=4.0)
-        log(f"per-config {name} {kv} P={part}: {avg * 1e3:.1f} us, {gbps:.0f} GB/s = {gbps / HBM_PEAK_GBPS:.1%} "
-            f"({time.time() - t0:.1f} s)")
+        nbytes = decode_bytes(w, 2 if kv == "bf16" else 1)
+        entry = {"workload": f"{name}: {w.spec.description}", "kv_cache": kv, "partition_tokens_asked": part,
+                 "bytes": nbytes, "layouts": {}}
+        for layout in ("page", "head_major"):
+            b = DeviceBatch(w, kv, layout, dev, host_codes=(kv == "fp8"))
+            evict = b.unique_kv_bytes() < EVICT_BELOW_BYTES
+            ms, plan, out = time_decode(b, dict(partition_tokens=part), max(args.steps, 20), args.warmup, evict)
+            avg = float(ms.mean())
+            gbps = nbytes / (avg * 1e-3) / 1e9
+            entry["layouts"][layout] = {
+                "plan": plan,
+                "decode_us": {"avg": round(avg * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                              "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+                "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "decode_tokens_per_s": round(w.spec.num_seqs / (avg * 1e-3), 1),
+                "cache_evicted_between_launches": evict}
+            if kv == "fp8" and layout == "page":
+                entry["fp8_accuracy"] = fp8_accuracy(b, out)
+            if not args.no_cpu_baseline and layout == "page":
+                entry["cpu_baseline"] = cpu_baseline(w, kv, b.kq, b.vq, min_s=2.0, budget_s=4.0)
+            log(f"per-config {name} {kv} P={part} {layout}: {avg * 1e3:.1f} us, {gbps:.0f} GB/s = "
+                f"{gbps / HBM_PEAK_GBPS:.1%}")
+            del b, out
+            torch.cuda.empty_cache()
+        best = max(entry["layouts"], key=lambda k: entry["layouts"][k]["frac"])
+        entry["best_layout"] = best
+        entry["best_frac"] = entry["layouts"][best]["frac"]
+        log(f"per-config {name} {kv} P={part}: best {best} ({time.time() - t0:.1f} s)")
         res.append(entry)
-        del b, out
-        torch.cuda.empty_cache()
     return res
 
 

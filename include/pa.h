@@ -118,11 +118,19 @@ typedef struct pa_decode_opts {
     int32_t schedule;         /* 1 = first build the work list on the device
                                  from context_lens: real (sequence, KV head,
                                  partition) items only, longest first, so
-                                 workgroups are dispatched in that order; -1 =
-                                 one workgroup per (sequence, KV head,
-                                 partition) in index order, empty ones
-                                 included; 0 = the work list when the plan
-                                 splits contexts, else -1 */
+                                 workgroups are dispatched in that order; 2 =
+                                 the same order without the builder pass:
+                                 each workgroup ranks its block index among
+                                 the items of context_lens itself (at most
+                                 4096 sequences; PA_ERR_UNSUPPORTED beyond;
+                                 for more than 16 query heads per KV head,
+                                 as 1); -1 = one workgroup per (sequence, KV
+                                 head, partition) in index order, empty ones
+                                 included; 0 = when the plan splits
+                                 contexts, 2 for batches of at most 256
+                                 sequences whose grid holds at most 1024
+                                 (sequence, item) pairs, else 1; when it
+                                 does not split, -1 */
     int32_t heads_per_tile;   /* MFMA kernel: 0 = chosen (2 for bf16 caches
                                  when g is 4..8, 2 for fp8 when g is 5..8,
                                  given an even num_kv_heads and adjacent KV
@@ -130,6 +138,13 @@ typedef struct pa_decode_opts {
                                  adjacent KV heads sharing one 16-row matrix
                                  tile (g * heads_per_tile <= 16, head stride
                                  == head_dim) */
+    int32_t wave_partitions;  /* split contexts, MFMA kernel: 1 = each wave
+                                 of a workgroup takes one whole partition (a
+                                 workgroup covers W consecutive partitions and
+                                 stores W states); -1 = the waves share one
+                                 partition's tiles and combine their states;
+                                 0 = chosen (1 for fp8 caches and partitions
+                                 of at most 512 tokens) */
     int32_t reserved;         /* must be 0 */
 } pa_decode_opts;
 
@@ -141,11 +156,14 @@ typedef struct pa_decode_plan {
     int32_t partition_tokens; /* tokens per partition */
     int32_t num_partitions;   /* partitions per (sequence, KV head); 1 = no split */
     int32_t prefetch_tiles;
-    int32_t scheduled;        /* 1 = device-built work list */
+    int32_t scheduled;        /* 0 = direct grid; 1 = device-built work list;
+                                 2 = longest-first items found by each
+                                 workgroup (no list, no builder pass) */
     int64_t num_workgroups;   /* decode kernel grid size (with a work list, the
                                  ones past its end exit at once) */
     size_t workspace_bytes;   /* bytes of workspace pa_decode needs */
     int32_t heads_per_tile;   /* KV heads per matrix tile (1 for the VALU kernel) */
+    int32_t wave_partitions;  /* 1 = each wave takes its own partition */
 } pa_decode_plan;
 
 /*

@@ -64,7 +64,7 @@ class pa_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("waves_per_group", ctypes.c_int32), ("prefetch_tiles", ctypes.c_int32),
                 ("schedule", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("wave_partitions", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class pa_decode_plan(ctypes.Structure):
@@ -72,7 +72,7 @@ class pa_decode_plan(ctypes.Structure):
                 ("partition_tokens", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("prefetch_tiles", ctypes.c_int32), ("scheduled", ctypes.c_int32),
                 ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("heads_per_tile", ctypes.c_int32)]
+                ("heads_per_tile", ctypes.c_int32), ("wave_partitions", ctypes.c_int32)]
 
 
 class TensorSpec(NamedTuple):
@@ -155,9 +155,10 @@ def strerror(status: int) -> str:
 
 
 def _opts(partition_tokens: int = 0, variant="auto", waves: int = 0, prefetch: int = 0,
-          schedule: int = 0, heads_per_tile: int = 0) -> pa_decode_opts:
+          schedule: int = 0, heads_per_tile: int = 0, wave_partitions: int = 0) -> pa_decode_opts:
     v = _VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    return pa_decode_opts(int(partition_tokens), v, int(waves), int(prefetch), int(schedule), int(heads_per_tile), 0)
+    return pa_decode_opts(int(partition_tokens), v, int(waves), int(prefetch), int(schedule), int(heads_per_tile),
+                          int(wave_partitions), 0)
 
 
 def _dtype_code(t) -> int:
@@ -247,15 +248,17 @@ def _plan_dict(p) -> dict:
     return {"variant": {1: "valu", 2: "mfma"}[p.variant], "waves_per_group": p.waves_per_group,
             "partition_tokens": p.partition_tokens, "num_partitions": p.num_partitions,
             "prefetch_tiles": p.prefetch_tiles, "scheduled": bool(p.scheduled),
+            "self_scheduled": p.scheduled == 2,
             "num_workgroups": p.num_workgroups,
-            "workspace_bytes": p.workspace_bytes, "heads_per_tile": p.heads_per_tile}
+            "workspace_bytes": p.workspace_bytes, "heads_per_tile": p.heads_per_tile,
+            "wave_partitions": bool(p.wave_partitions)}
 
 
 def pa_decode_get_plan(q, k_cache, block_tables, *, partition_tokens=0, variant="auto", waves=0, prefetch=0,
-                       schedule=0, heads_per_tile=0) -> dict:
+                       schedule=0, heads_per_tile=0, wave_partitions=0) -> dict:
     """The launch plan pa_decode would use (tensors or TensorSpecs; see decode_specs)."""
     lib = load_library()
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile, wave_partitions)
     p = pa_decode_plan()
     d = [desc(t) for t in (q, k_cache, block_tables)]
     st = lib.pa_decode_get_plan(*map(_ref, d), ctypes.byref(o), ctypes.byref(p))
@@ -265,8 +268,8 @@ def pa_decode_get_plan(q, k_cache, block_tables, *, partition_tokens=0, variant=
 
 
 def pa_decode_workspace_size(q, k_cache, block_tables, *, partition_tokens=0, variant="auto", waves=0, prefetch=0,
-                             schedule=0, heads_per_tile=0) -> int:
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
+                             schedule=0, heads_per_tile=0, wave_partitions=0) -> int:
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile, wave_partitions)
     d = [desc(t) for t in (q, k_cache, block_tables)]
     return int(load_library().pa_decode_workspace_size(*map(_ref, d), ctypes.byref(o)))
 
@@ -274,7 +277,7 @@ def pa_decode_workspace_size(q, k_cache, block_tables, *, partition_tokens=0, va
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
               k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, partition_tokens: int = 0,
               variant="auto", waves: int = 0, prefetch: int = 0, schedule: int = 0, heads_per_tile: int = 0,
-              stream=None):
+              wave_partitions: int = 0, stream=None):
     """Decode step: q [S, Hq, D] bf16 attends through block_tables [S, MB] int32 and
     context_lens [S] int32 over the paged caches [N, bs, Hkv, D] (any strides the
     library accepts). Returns out [S, Hq, D] bf16.
@@ -285,7 +288,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     lib = load_library()
     if out is None:
         out = _new(stream, lambda: torch.empty(q.shape, dtype=q.dtype, device=q.device))
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile, wave_partitions)
     dq, dk, dv, dt, dc, do = (desc(t) for t in (q, k_cache, v_cache, block_tables, context_lens, out))
     need = lib.pa_decode_workspace_size(_ref(dq), _ref(dk), _ref(dt), ctypes.byref(o))
     ws_ptr, ws_bytes = _workspace(need, workspace, q.device, stream)
@@ -298,14 +301,15 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
 
 def pa_decode_no_alloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
                        k_scale: float = 1.0, v_scale: float = 1.0, partition_tokens: int = 0, variant="auto",
-                       waves: int = 0, prefetch: int = 0, schedule: int = 0, heads_per_tile: int = 0, stream=None):
+                       waves: int = 0, prefetch: int = 0, schedule: int = 0, heads_per_tile: int = 0,
+                       wave_partitions: int = 0, stream=None):
     """pa_decode with the library's static scratch as its workspace: no
     device allocation anywhere, here or in the library (so `out` must be
     given). Raises PAError (PA_ERR_SCRATCH) when the plan needs more than
     PA_NO_ALLOC_SCRATCH bytes. Calls that overlap on one device race on the
     scratch."""
     lib = load_library()
-    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile)
+    o = _opts(partition_tokens, variant, waves, prefetch, schedule, heads_per_tile, wave_partitions)
     d = [desc(t) for t in (q, k_cache, v_cache, block_tables, context_lens, out)]
     st = lib.pa_decode_no_alloc(*map(_ref, d[:5]), float(scale), _ref(d[5]), float(k_scale), float(v_scale),
                                 ctypes.byref(o), _stream_ptr(stream))

@@ -72,7 +72,10 @@ constexpr int mfma_waves_per_eu() {
     return (HP > 1 && !FP8 && base > 2) ? base - 1 : base;
 }
 
-template <int D, bool FP8, int NB, int HP>
+// WPP: each wave takes one whole partition of the item (wave w: partition
+// item * W + w) and stores that partition's state itself; otherwise the
+// waves share the item's tiles round robin and combine their states in LDS.
+template <int D, bool FP8, int NB, int HP, bool WPP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<NB, HP, FP8>())))
 void pa_decode_mfma_kernel(DecodeArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
@@ -91,7 +94,7 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
     static_assert(LPC <= 64 && NI >= 1 && TPH % RPI == 0, "tile shape");
 
     extern __shared__ float smem[];
-    for_each_item(a, [&](const WorkItem& wi) {
+    for_each_item(a, reinterpret_cast<int*>(smem), [&](const WorkItem& wi) {
         const int W = (int)(blockDim.x >> 6);
         const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         const int lane = (int)(threadIdx.x & 63);
@@ -106,8 +109,10 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         // Q^T operands: MFMA j takes d = 32 j + 8 gq + 0..7 of column c, the
         // d range of the lane's K operand of MFMA j. Column c is query head
         // c % TPH of KV head kvh0 + c / TPH (zero when c % TPH >= g). The q
-        // rows sit in LDS after the staging tiles and are read per tile,
-        // which keeps 16 registers per lane free for the load ring.
+        // rows are staged in LDS after the staging tiles; with one KV head
+        // per tile (fewer registers in use) each lane then keeps its
+        // fragments in registers, otherwise they are read per tile, which
+        // keeps 16 registers per lane free for the load ring.
         uint16_t* qs = reinterpret_cast<uint16_t*>(smem) + W * 2 * kTile * RS;
         for (int i = (int)threadIdx.x; i < kTile * (D / 8); i += (int)blockDim.x) {
             const int col = i / (D / 8);
@@ -121,6 +126,14 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         }
         __syncthreads();
         const uint16_t* q_row = qs + c * RS + 8 * gq;
+        // q fragments in registers (one head per tile; not for the bf16
+        // 2-tile ring at D = 128, whose 128-register budget they overflow)
+        constexpr bool QR = HP == 1 && (FP8 || NB >= 3 || D == 64);
+        bf16x8 qf[QR ? NQK : 1];
+        if constexpr (QR) {
+#pragma unroll
+            for (int j = 0; j < NQK; ++j) qf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+        }
 
         float m = -INFINITY;  // running max of head c (log2 units), same in all four lane groups
         float l = 0.0f;       // running sum over this lane's tokens
@@ -128,7 +141,16 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        const int span = wi.t_end - wi.t_begin;
+        // The tokens this wave streams: the whole item's, shared round robin
+        // with the other waves, or (WPP) its own partition's, in order.
+        WorkItem wv = wi;
+        int part_w = wi.part;
+        if constexpr (WPP) {
+            part_w = wi.part * W + wave;
+            wv.t_begin = wi.t_begin + wave * a.partition_tokens;
+            wv.t_end = min(wv.t_begin + a.partition_tokens, wi.t_end);
+        }
+        const int span = wv.t_end - wv.t_begin;
         const int ntiles = span > 0 ? (span + TPH - 1) / TPH : 0;
         // The unit's first KV head is folded into each tile's descriptor base,
         // so a row's bytes start at a multiple of the row stride from it
@@ -154,13 +176,13 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         // number of loads in flight, so the wait before a tile's use never
         // has to drain the prefetch behind it.
         // Wave w takes tiles w, w + W, w + 2W, ... of the item.
-        const int t_first = wave, t_step = W, t_stop = ntiles;
+        const int t_first = WPP ? 0 : wave, t_step = WPP ? 1 : W, t_stop = ntiles;
 
         auto issue = [&](int t, int64_t blk, u32x4 (&kb)[NI], u32x4 (&vb)[NI]) {
             const bool live = t < t_stop;
-            const int t0 = wi.t_begin + (live ? t : t_stop - 1) * TPH;
+            const int t0 = wv.t_begin + (live ? t : t_stop - 1) * TPH;
             const uint32_t row0 = (uint32_t)(t0 & bs_mask) * a.cache.token;
-            const int valid = min(wi.t_end - t0, TPH);
+            const int valid = min(wv.t_end - t0, TPH);
             const uint32_t nbytes = live ? row0 + (uint32_t)valid * a.cache.token : 0u;
             const int64_t base = blk * a.cache.block + head_off;
             const auto rk = make_rsrc(a.k_cache + base, nbytes);
@@ -172,8 +194,8 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         };
 
         auto consume = [&](int t, const u32x4 (&kb)[NI], const u32x4 (&vb)[NI]) {
-            const int t0 = wi.t_begin + t * TPH;
-            const int valid = wi.t_end - t0;
+            const int t0 = wv.t_begin + t * TPH;
+            const int valid = wv.t_end - t0;
             const bool full = valid >= TPH;
 
             // With HP > 1 the P.V MFMA also multiplies each V row by the zero
@@ -222,7 +244,9 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
                 const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
-                const bf16x8 qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+                bf16x8 qb;
+                if constexpr (QR) qb = qf[j];
+                else qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
             }
 
@@ -310,7 +334,7 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             // leave the prefetch behind it outstanding. sched_barrier keeps
             // the compiler from sinking the prefetch below those waits.
             // The table entry of each issued tile was fetched one step earlier.
-            const TableReader tab = make_table_reader(a, wi, t_stop - 1, TPH);
+            const TableReader tab = make_table_reader(a, wv, t_stop - 1, TPH);
             uint32_t entry = table_fetch(tab, t_first);
 #pragma unroll
             for (int b = 0; b < NB - 1; ++b) {
@@ -337,6 +361,39 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         l += xor_shfl(l, 16);
         l += xor_shfl(l, 32);
 
+        if constexpr (WPP) {
+            // This wave's state is a whole partition's: store it directly.
+            // Partition 0 always stores (a zero-length context's zero row);
+            // a partition past the context's end stores nothing (the merge
+            // never reads it). Column c is query head (c / TPH) * g + c % TPH
+            // of the unit's HP * g heads; lane (gq, c) holds d = 16 j + 4 gq + r.
+            if ((wv.t_end > wv.t_begin || part_w == 0) && c % TPH < g) {
+                const int hq = wi.kvh * HP * g + (c / TPH) * g + c % TPH;
+                if (wi.final_out) {
+                    const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
+                    uint16_t* dst = a.out + (int64_t)wi.seq * a.out_seq + (int64_t)hq * a.out_head;
+#pragma unroll
+                    for (int j = 0; j < NPV; ++j) {
+                        const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[j][0] * inv) |
+                                            ((uint32_t)f32_to_bf16_rne(o[j][1] * inv) << 16);
+                        const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[j][2] * inv) |
+                                            ((uint32_t)f32_to_bf16_rne(o[j][3] * inv) << 16);
+                        *reinterpret_cast<u32x2*>(dst + 16 * j + 4 * gq) = u32x2{lo, hi};
+                    }
+                } else {
+                    const int64_t prow = ((int64_t)wi.seq * a.num_q_heads + hq) * a.num_partitions + part_w;
+#pragma unroll
+                    for (int j = 0; j < NPV; ++j)
+                        *reinterpret_cast<f32x4*>(a.part_o + prow * D + 16 * j + 4 * gq) = o[j] * a.v_scale;
+                    if (gq == 0) {
+                        a.part_ml[prow * 2] = m;
+                        a.part_ml[prow * 2 + 1] = l;
+                    }
+                }
+            }
+            return;
+        }
+
         __syncthreads();  // V staging is dead; reuse LDS for the combine
         // column c -> query head cc = (c / TPH) * g + c % TPH of the unit's
         // G = HP * g heads
@@ -359,22 +416,30 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
     });
 }
 
-template <int D, bool FP8, int NB, int HP>
+template <int D, bool FP8, int NB, int HP, bool WPP>
 hipError_t launch_d(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
     const dim3 block((unsigned)(64 * ls.waves));
     const size_t stage = ((size_t)ls.waves * 2 + 1) * kTile * (D + 8) * sizeof(uint16_t);
     const size_t comb = (size_t)ls.waves * HP * a.group * (D + 2) * sizeof(float);
+    static_assert(kSelfLdsInts * sizeof(int) <= kTile * (64 + 8) * sizeof(uint16_t), "item scratch fits the staging area");
     const size_t lds = stage > comb ? stage : comb;
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.units_per_seq * a.num_partitions));
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB, HP>), grid, block, lds, s, a);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.units_per_seq * a.num_items));
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, FP8, NB, HP, WPP>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
 template <int D, bool FP8, int HP>
 hipError_t launch_nb(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
-    if (ls.depth <= 2) return launch_d<D, FP8, 2, HP>(a, ls, s);
-    if (ls.depth == 3) return launch_d<D, FP8, 3, HP>(a, ls, s);
-    return launch_d<D, FP8, 4, HP>(a, ls, s);
+    if (ls.wave_partitions) {  // one partition per wave: rings of 2 or 3 tiles, one or two heads per tile
+        if constexpr (HP <= 2) {
+            if (ls.depth <= 2) return launch_d<D, FP8, 2, HP, true>(a, ls, s);
+            return launch_d<D, FP8, 3, HP, true>(a, ls, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    if (ls.depth <= 2) return launch_d<D, FP8, 2, HP, false>(a, ls, s);
+    if (ls.depth == 3) return launch_d<D, FP8, 3, HP, false>(a, ls, s);
+    return launch_d<D, FP8, 4, HP, false>(a, ls, s);
 }
 
 template <int D, bool FP8>

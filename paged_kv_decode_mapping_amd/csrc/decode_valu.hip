@@ -66,7 +66,7 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
     static_assert(NI >= 1 && kTile % RPI == 0, "tile shape");
 
     extern __shared__ float smem[];
-    for_each_item(a, [&](const WorkItem& wi) {
+    for_each_item(a, reinterpret_cast<int*>(smem), [&](const WorkItem& wi) {
         const int W = (int)(blockDim.x >> 6);
         const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         const int lane = (int)(threadIdx.x & 63);
@@ -262,8 +262,9 @@ __global__ __launch_bounds__(512) void pa_decode_valu_kernel(DecodeArgs a) {
 template <int D, bool FP8, int GM, int NB>
 hipError_t launch_k(const DecodeArgs& a, const LaunchShape& ls, hipStream_t s) {
     const dim3 block((unsigned)(64 * ls.waves));
-    const size_t lds = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
-    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions));
+    const size_t comb = (size_t)ls.waves * a.group * (D + 2) * sizeof(float);
+    const size_t lds = comb > kSelfLdsInts * sizeof(int) ? comb : kSelfLdsInts * sizeof(int);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.units_per_seq * a.num_items));
     hipLaunchKernelGGL((pa_decode_valu_kernel<D, FP8, GM, NB>), grid, block, lds, s, a);
     return hipGetLastError();
 }

@@ -45,8 +45,11 @@ struct Plan {
     int partition_tokens = 0;
     int num_partitions = 1;
     bool scheduled = true;
+    bool self_scheduled = false; // scheduled, each workgroup finding its own item (no builder pass)
     bool multi = false;          // the multi-row kernel (more than 16 query rows per KV head)
     int heads_per_unit = 1;      // MFMA kernel: adjacent KV heads sharing a 16-row tile
+    bool wave_partitions = false; // MFMA kernel: each wave takes one whole partition
+    int num_items = 1;           // work items per (sequence, unit): partitions, or groups of W
     int row_blocks = 1;          // multi: blocks of 16 * waves rows per (sequence, KV head)
     int64_t num_workgroups = 0;  // direct grid size, or the item bound when scheduled
     // workspace layout (byte offsets); total = workspace
@@ -56,6 +59,7 @@ struct Plan {
 };
 
 constexpr size_t kHeaderBytes = 256;  // scheduled: item count
+constexpr int64_t kSelfMaxPairs = 1024;  // default self-scheduling: grid size bound (see make_plan)
 
 int check_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB,
                 int32_t kv_dtype) {
@@ -103,7 +107,7 @@ int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int g
 // (sequence, KV head); one wave per 16 of them, up to 8 waves a workgroup
 // (more rows take more workgroups, each reading the K/V again).
 int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
-                    int32_t MB, int32_t partition_tokens, Plan* plan) {
+                    int32_t MB, int32_t partition_tokens, Plan* plan, int32_t schedule = 0) {
     if (Tq < 0 || maxq < 0) return PA_ERR_SHAPE;
     Plan p;
     p.variant = PA_VARIANT_MFMA;
@@ -134,7 +138,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     // long item started last would stretch the launch (measured: 8 queries
     // per sequence on a ragged batch, 531 -> 384 us). Unsplit, the direct
     // grid keeps the KV heads of a sequence adjacent, which measured faster.
-    p.scheduled = p.num_partitions > 1 && p.num_partitions < 32768 && Hkv < 65536;
+    p.scheduled = p.num_partitions > 1 && p.num_partitions < 32768 && Hkv < 65536 && schedule >= 0;
     size_t off = 0;
     if (p.scheduled) {
         p.items_off = kHeaderBytes;
@@ -156,7 +160,7 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
 // heads_adjacent: a token row's KV heads are one contiguous run (the head
 // stride is head_dim), which packing several KV heads into a tile needs.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t MB, int32_t kv_dtype,
-              bool heads_adjacent, const pa_decode_opts* opts, Plan* plan) {
+              bool heads_adjacent, const pa_decode_opts* opts, Plan* plan, bool allow_wave_partitions = true) {
     int st = check_sizes(S, Hq, Hkv, D, bs, MB, kv_dtype);
     if (st != PA_OK) return st;
     pa_decode_opts o{};
@@ -171,14 +175,14 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     p.variant = o.variant != PA_VARIANT_AUTO ? o.variant : (g >= 4 ? PA_VARIANT_MFMA : PA_VARIANT_VALU);
     if (p.variant == PA_VARIANT_VALU && g > 4) return PA_ERR_UNSUPPORTED;
     if (o.prefetch_tiles < 0 || o.prefetch_tiles > 3) return PA_ERR_SHAPE;
-    if (o.schedule < -1 || o.schedule > 1) return PA_ERR_SHAPE;
+    if (o.schedule < -1 || o.schedule > 2) return PA_ERR_SHAPE;
     if (o.waves_per_group != 0 && o.waves_per_group != 1 && o.waves_per_group != 2 &&
         o.waves_per_group != 4 && o.waves_per_group != 8)
         return PA_ERR_SHAPE;
     // More query heads per KV head than one 16-row tile holds (MQA): the
     // multi-row kernel, one wave per 16 heads (waves, prefetch and schedule
     // options do not apply to it).
-    if (g > 16) return make_multi_plan(S, S, 1, Hq, Hkv, D, bs, MB, o.partition_tokens, plan);
+    if (g > 16) return make_multi_plan(S, S, 1, Hq, Hkv, D, bs, MB, o.partition_tokens, plan, o.schedule);
     // Defaults measured on MI355X: the MFMA kernel's tiles are 16 whole K
     // and V rows (8 KiB per wave for bf16, D = 128), so one tile in flight
     // per wave already covers the memory latency; the VALU kernel for g = 1
@@ -245,18 +249,57 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t
     p.partition_tokens = (int)P;
     p.num_partitions = (int)((cap + P - 1) / P);
     if (p.num_partitions < 1) p.num_partitions = 1;
-    p.num_workgroups = units * p.num_partitions;
+    // One partition per wave: a workgroup covers W consecutive partitions,
+    // each wave streaming one of them and storing its state, instead of
+    // the W waves sharing one partition's tiles and combining in LDS. This
+    // amortises a workgroup's set-up (query rows, first loads, combine) over
+    // W times the bytes. Measured on MI355X: fp8 caches with 512-token
+    // partitions gain 4-6 % (long contexts 137.6 -> 131.6 us, mixed batch
+    // 169.0 -> 158.3 us); bf16 at 512 tokens is unchanged, and with longer
+    // partitions (1024-4096 tokens) it loses, as one wave then streams a
+    // whole long partition by itself.
+    if (o.wave_partitions < -1 || o.wave_partitions > 1) return PA_ERR_SHAPE;
+    const bool wpp_ok = p.variant == PA_VARIANT_MFMA && p.heads_per_unit <= 2 && p.depth <= 3 &&
+                        allow_wave_partitions;
+    if (o.wave_partitions == 1 && !wpp_ok) return PA_ERR_UNSUPPORTED;
+    p.wave_partitions = p.num_partitions > 1 && p.waves > 1 && wpp_ok &&
+                        (o.wave_partitions == 1 ||
+                         (o.wave_partitions == 0 && kv_dtype == PA_DTYPE_FP8_E4M3FN && P <= 512));
+    p.num_items = p.wave_partitions ? (p.num_partitions + p.waves - 1) / p.waves : p.num_partitions;
+    p.num_workgroups = units * p.num_items;
     if (!pa::grid_fits(p.num_workgroups, 64 * p.waves)) return PA_ERR_UNSUPPORTED;
-    if (o.schedule < -1 || o.schedule > 1) return PA_ERR_SHAPE;
-    // Device work list: by default only when contexts are split. Then most
-    // (sequence, partition) pairs of a ragged batch are empty and the real
-    // ones differ in length, so a compact longest-first list pays for its
-    // pre-pass; an unsplit grid has one workgroup per (sequence, KV head)
-    // and no empty ones. Items pack (partition << 16 | KV head) into 32 bits.
-    const bool want = o.schedule == 1 || (o.schedule == 0 && p.num_partitions > 1);
+    if (o.schedule < -1 || o.schedule > 2) return PA_ERR_SHAPE;
+    // Longest-first items: by default only when contexts are split. Then
+    // most (sequence, partition) pairs of a ragged batch are empty and the
+    // real ones differ in length, so a compact longest-first order pays for
+    // finding it; an unsplit grid has one workgroup per (sequence, KV head)
+    // and no empty ones. The order comes either from a one-workgroup builder
+    // pass that writes the list to the workspace (items pack partition << 16
+    // | KV head into 32 bits), or from each decode workgroup itself, which
+    // counts the items of context_lens by length in LDS and ranks its block
+    // index among them -- no extra launch, at the cost of reading
+    // context_lens in every workgroup, so only for batches of up to
+    // kSelfMaxSeqs sequences.
+    const bool want = o.schedule >= 1 || (o.schedule == 0 && p.num_partitions > 1);
     p.scheduled = want && p.num_partitions < 32768 && Hkv / p.heads_per_unit < 65536;
+    const int64_t span = P * (p.wave_partitions ? p.waves : 1);
+    const bool self_ok = S <= pa::kSelfMaxSeqs && span % pa::kTile == 0 && span / pa::kTile + 1 <= pa::kSelfBuckets;
+    if (o.schedule == 2 && !self_ok) return PA_ERR_UNSUPPORTED;
+    // By default when one wave ranks the batch (at most kSelfWaveSeqs
+    // sequences) and the grid holds at most kSelfMaxPairs (sequence, item)
+    // pairs: every workgroup of the grid, real item or not, first reads
+    // context_lens, so the search pays where the grid is small against the
+    // work. Measured on MI355X (decode + merge, % of 8 TB/s, list -> self):
+    // long contexts (4 sequences) bf16 at 2048-token partitions 75.7 -> 76.9,
+    // at 512 71.9 -> 73.4, fp8 69.3 -> 70.5; mixed batch (256 sequences, 2
+    // partitions) bf16 85.7 -> 86.3, fp8 71-78 -> 77.8; the 70B batch at 512
+    // tokens (1024 pairs) even; but the mixed batch at 512-token partitions
+    // (4096 pairs, ~3800 real items) 75.0 -> 68.6.
+    const int64_t pairs = (int64_t)S * p.num_items;
+    p.self_scheduled = p.scheduled && self_ok &&
+                       (o.schedule == 2 || (o.schedule == 0 && S <= pa::kSelfWaveSeqs && pairs <= kSelfMaxPairs));
     size_t off = 0;
-    if (p.scheduled) {
+    if (p.scheduled && !p.self_scheduled) {
         p.items_off = kHeaderBytes;
         off = p.items_off + align_up((size_t)p.num_workgroups * 4 * sizeof(int32_t), 256);
     }
@@ -292,7 +335,7 @@ int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
                       bool heads_adjacent, int32_t G, int32_t maxg, int32_t PMB, const pa_decode_opts* opts,
                       CascadePlan* out) {
     CascadePlan c;
-    int st = make_plan(S, Hq, Hkv, D, bs, MB, kv_dtype, heads_adjacent, opts, &c.suffix);
+    int st = make_plan(S, Hq, Hkv, D, bs, MB, kv_dtype, heads_adjacent, opts, &c.suffix, false);
     if (st != PA_OK) return st;
     if (G < 0 || maxg < 0 || PMB < 0) return PA_ERR_SHAPE;
     if (G >= (int64_t(1) << 30) || (int64_t)PMB * bs >= (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
@@ -302,6 +345,7 @@ int make_cascade_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
     if (p.num_partitions >= 32768 || Hkv / p.heads_per_unit >= 65536) return PA_ERR_UNSUPPORTED;
     if (!pa::grid_fits((int64_t)S * Hq, 512)) return PA_ERR_UNSUPPORTED;  // merge grid: a workgroup of <= 8 waves per row
     p.scheduled = true;
+    p.self_scheduled = false;  // the builder also offsets items past each sequence's prefix
     p.partials = true;
     size_t off = kHeaderBytes;
     p.items_off = off;
@@ -473,6 +517,8 @@ int run_multi(const Plan& p, const Geom& g, const int32_t* query_start, int32_t 
         sa.num_kv_heads = g.Hkv;
         sa.partition_tokens = p.partition_tokens;
         sa.num_partitions = p.num_partitions;
+        sa.split_tokens = p.partition_tokens;
+        sa.split_count = p.num_partitions;
         sa.max_context = g.MB * g.bs;
         if (pa::launch_schedule(sa, s) != hipSuccess) return PA_ERR_LAUNCH;
         a.items = sa.items;
@@ -504,10 +550,11 @@ pa::DecodeArgs decode_args(const Plan& p, const Geom& g, float scale, int32_t kv
         a.part_ml = reinterpret_cast<float*>(ws + p.ml_off);
         a.part_o = reinterpret_cast<float*>(ws + p.o_off);
     }
-    if (p.scheduled) {
+    if (p.scheduled && !p.self_scheduled) {
         a.item_count = reinterpret_cast<int*>(ws);
         a.items = reinterpret_cast<const int4*>(ws + p.items_off);
     }
+    a.self_schedule = p.self_scheduled ? 1 : 0;
     a.num_seqs = g.S;
     a.num_q_heads = g.Hq;
     a.num_kv_heads = g.Hkv;
@@ -517,6 +564,8 @@ pa::DecodeArgs decode_args(const Plan& p, const Geom& g, float scale, int32_t kv
     a.max_blocks_per_seq = g.MB;
     a.partition_tokens = p.partition_tokens;
     a.num_partitions = p.num_partitions;
+    a.wave_partitions = p.wave_partitions ? p.waves : 1;
+    a.num_items = p.num_items;
     a.last_block = last_block_id(g.N);
     a.cache = g.cache.lay;
     a.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * pa::kLog2e;
@@ -532,9 +581,11 @@ pa::ScheduleArgs schedule_args(const Plan& p, const pa::DecodeArgs& a, const int
     sa.items = const_cast<int4*>(a.items);
     sa.item_count = const_cast<int*>(a.item_count);
     sa.num_seqs = a.num_seqs;
-    sa.num_kv_heads = a.units_per_seq;  // items are (sequence, unit, partition)
-    sa.partition_tokens = p.partition_tokens;
-    sa.num_partitions = p.num_partitions;
+    sa.num_kv_heads = a.units_per_seq;  // items are (sequence, unit, partition or group of partitions)
+    sa.partition_tokens = p.partition_tokens * a.wave_partitions;
+    sa.num_partitions = p.num_items;
+    sa.split_tokens = p.partition_tokens;
+    sa.split_count = p.num_partitions;
     sa.max_context = max_context;
     sa.block_size_log2 = a.block_size_log2;
     return sa;
@@ -667,10 +718,11 @@ int pa_decode_get_plan(const pa_tensor* q, const pa_tensor* k_cache, const pa_te
     plan->partition_tokens = p.partition_tokens;
     plan->num_partitions = p.num_partitions;
     plan->prefetch_tiles = p.depth - 1;
-    plan->scheduled = p.scheduled ? 1 : 0;
+    plan->scheduled = p.self_scheduled ? 2 : (p.scheduled ? 1 : 0);
     plan->num_workgroups = p.num_workgroups;
     plan->workspace_bytes = p.workspace;
     plan->heads_per_tile = p.heads_per_unit;
+    plan->wave_partitions = p.wave_partitions ? 1 : 0;
     return PA_OK;
 }
 
@@ -707,12 +759,12 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_c
     pa::DecodeArgs a = decode_args(p, g, scale, kvd, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (p.scheduled) {
+    if (p.scheduled && !p.self_scheduled) {
         const pa::ScheduleArgs sa = schedule_args(p, a, g.context_lens, g.MB * g.bs);
         e = pa::launch_schedule(sa, s);
         if (e != hipSuccess) return PA_ERR_LAUNCH;
     }
-    const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit};
+    const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit, p.wave_partitions};
     const bool fp8 = kvd == PA_DTYPE_FP8_E4M3FN;
     e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, g.D, fp8, ls, s)
                                      : pa::launch_decode_valu(a, g.D, fp8, ls, s);
@@ -806,7 +858,7 @@ int pa_decode_cascade(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         if (pa::launch_multi(m, g.D, fp8, c.prefix.waves, s) != hipSuccess) return PA_ERR_LAUNCH;
     }
     // 3. suffix pass
-    const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit};
+    const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit, false};
     const hipError_t e = p.variant == PA_VARIANT_MFMA ? pa::launch_decode_mfma(a, g.D, fp8, ls, s)
                                                       : pa::launch_decode_valu(a, g.D, fp8, ls, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;

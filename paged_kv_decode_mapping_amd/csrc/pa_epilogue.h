@@ -68,31 +68,39 @@ struct WorkItem {
     bool active;          // false: nothing to do (empty partition)
 };
 
-__device__ __forceinline__ WorkItem make_work_item(const DecodeArgs& a, int seq, int kvh, int part) {
+// Item `item` of (seq, unit): partitions item * wave_partitions onward,
+// tokens [item * span, (item + 1) * span) clipped to the context, span =
+// wave_partitions * partition_tokens.
+__device__ __forceinline__ WorkItem make_work_item(const DecodeArgs& a, int seq, int kvh, int item) {
     WorkItem w;
     w.seq = seq;
     w.kvh = kvh;
-    w.part = part;
+    w.part = item;
     int ctx = a.context_lens[seq];
     const int cap = a.max_blocks_per_seq << a.block_size_log2;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int span = a.partition_tokens * a.wave_partitions;
+    const int items_used = (ctx + span - 1) / span;
     const int parts_used = (ctx + a.partition_tokens - 1) / a.partition_tokens;
-    w.t_begin = part * a.partition_tokens;
-    w.t_end = min(w.t_begin + a.partition_tokens, ctx);
-    // Partition 0 always runs, so that a zero-length context still gets its
+    w.t_begin = item * span;
+    w.t_end = min(w.t_begin + span, ctx);
+    // Item 0 always runs, so that a zero-length context still gets its
     // (all-zero) output row.
-    w.active = (part < parts_used) || (part == 0);
+    w.active = (item < items_used) || (item == 0);
     w.final_out = (a.num_partitions == 1) || (parts_used <= 1);
     return w;
 }
 
-// Direct grid: workgroup b takes item (unit = b / P, part = b % P); a
-// sequence has units_per_seq units (its KV heads, or groups of them).
+// Direct grid: workgroup b takes item b % num_items of unit b / num_items
+// (a sequence has units_per_seq units: its KV heads, or groups of them).
+// Consecutive workgroups are dispatched round robin over the XCDs, so the
+// items of one unit spread over all of them. (Item-major order, later items
+// first, was measured slower: with few sequences the early items then all
+// belong to the longest one, whose units map to the same few XCDs.)
 __device__ __forceinline__ WorkItem decode_work_item(const DecodeArgs& a) {
     const int bid = (int)blockIdx.x;
-    const int P = a.num_partitions;
-    const int unit = bid / P;
-    return make_work_item(a, unit / a.units_per_seq, unit % a.units_per_seq, bid % P);
+    const int unit = bid / a.num_items;
+    return make_work_item(a, unit / a.units_per_seq, unit % a.units_per_seq, bid % a.num_items);
 }
 
 __device__ __forceinline__ WorkItem scheduled_item(const int4& r) {
@@ -107,16 +115,280 @@ __device__ __forceinline__ WorkItem scheduled_item(const int4& r) {
     return w;
 }
 
+// Exclusive prefix sum over the workgroup of one value per thread (in
+// thread order); *total gets the sum. wsum: LDS scratch of >= 16 ints.
+// Contains barriers: every thread of the workgroup must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+    const int t = (int)threadIdx.x, lane = t & 63, wave = t >> 6, nw = (int)(blockDim.x >> 6);
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int s = wsum[w];
+        base += w < wave ? s : 0;
+        tot += s;
+    }
+    __syncthreads();  // wsum is free again
+    *total = tot;
+    return base + x - v;
+}
+
+// Exclusive prefix sum over one wave (lane order); *total gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
+    const int lane = (int)(threadIdx.x & 63);
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    *total = __builtin_amdgcn_readlane(x, 63);
+    return x - v;
+}
+
+// Batches of at most kSelfWaveSeqs sequences: the first wave alone finds
+// the item (lane l holds sequences kSelfSeqsPerLane * l onward in registers,
+// so context_lens is read once and the scans are wave-wide shuffles), and
+// one barrier hands it to the other waves. The grid is sized for the most
+// items there can be, so most workgroups of a ragged or short batch have
+// none: those learn it from the item total alone, one wave-wide sum after
+// the read, and exit before any of the ranking. Same order and result as
+// the workgroup-wide search below. lds: kSelfLdsInts ints of scratch,
+// reusable by the body once this returns.
+__device__ __forceinline__ bool self_scheduled_item_wave(const DecodeArgs& a, int* lds, WorkItem* out) {
+    const int t = (int)threadIdx.x, lane = t & 63;
+    const int S = a.num_seqs;
+    const int span = a.partition_tokens * a.wave_partitions;
+    const int KT = span / kTile;  // tiles of a full item (span is a multiple of the tile)
+    const int NB = KT + 1;        // buckets: k = KT - tiles, k = 0 holds full items
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    int* hist = lds;  // [NB <= kSelfBuckets]
+    int* res = lds + kSelfRes;
+    const int b = (int)blockIdx.x;
+    const int pb = b / a.units_per_seq, unit = b - pb * a.units_per_seq;
+    if (t < 64) {
+        int full[kSelfSeqsPerLane], last[kSelfSeqsPerLane];  // full items; bucket of the last (-1: none)
+        int fsum = 0, items = 0;
+#pragma unroll
+        for (int k = 0; k < kSelfSeqsPerLane; ++k) {
+            const int i = kSelfSeqsPerLane * lane + k;
+            full[k] = 0;
+            last[k] = -1;
+            if (i < S) {
+                int ctx = a.context_lens[i];
+                ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+                const int f = ctx / span, rem = ctx - f * span;
+                full[k] = f;
+                if (rem > 0 || ctx == 0) last[k] = KT - (rem + kTile - 1) / kTile;
+            }
+            fsum += full[k];
+            items += full[k] + (last[k] >= 0 ? 1 : 0);
+        }
+        int total;
+        (void)wave_exclusive_scan(items, &total);
+        int seq = -1, part = 0;
+        if (pb < total) {
+            for (int k = lane; k < NB; k += 64) hist[k] = 0;
+            int ftot;
+            (void)wave_exclusive_scan(fsum, &ftot);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (lane == 0) atomicAdd(&hist[0], ftot);
+#pragma unroll
+            for (int k = 0; k < kSelfSeqsPerLane; ++k)
+                if (last[k] >= 0) atomicAdd(&hist[last[k]], 1);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            // buckets [k0, k1) of this lane, then their scan
+            const int CB = (NB + 63) / 64;
+            const int k0 = min(lane * CB, NB), k1 = min(k0 + CB, NB);
+            int local = 0;
+            for (int k = k0; k < k1; ++k) local += hist[k];
+            int total_b;
+            const int run = wave_exclusive_scan(local, &total_b);
+            const bool mine = pb >= run && pb < run + local;
+            const uint64_t hold = __builtin_amdgcn_ballot_w64(mine);
+            // exactly one lane holds item pb's bucket (none only if the counts were inconsistent)
+            const int src = hold != 0 ? (int)__builtin_ctzll(hold) : 0;
+            int kb_l = -1, r_l = 0;
+            if (mine) {
+                int acc = run;
+                for (int k = k0; k < k1; ++k) {
+                    const int h = hist[k];
+                    if (kb_l < 0 && pb < acc + h) {
+                        kb_l = k;
+                        r_l = pb - acc;
+                    }
+                    acc += h;
+                }
+            }
+            const int kb = __builtin_amdgcn_readlane(kb_l, src), r = __builtin_amdgcn_readlane(r_l, src);
+            // the r-th item of bucket kb in sequence order
+            int cnt = 0;
+#pragma unroll
+            for (int k = 0; k < kSelfSeqsPerLane; ++k) cnt += (kb == 0 ? full[k] : 0) + (last[k] == kb ? 1 : 0);
+            int tot2;
+            const int pre = wave_exclusive_scan(cnt, &tot2);
+            const bool mine2 = kb >= 0 && r >= pre && r < pre + cnt;
+            const uint64_t hold2 = __builtin_amdgcn_ballot_w64(mine2);
+            if (hold2 != 0) {
+                const int src2 = (int)__builtin_ctzll(hold2);
+                int seq_l = -1, part_l = 0;
+                if (mine2) {
+                    int acc = pre;
+#pragma unroll
+                    for (int k = 0; k < kSelfSeqsPerLane; ++k) {
+                        const int c = (kb == 0 ? full[k] : 0) + (last[k] == kb ? 1 : 0);
+                        if (seq_l < 0 && r < acc + c) {
+                            const int j = r - acc;
+                            seq_l = kSelfSeqsPerLane * lane + k;
+                            part_l = (kb == 0 && j < full[k]) ? j : full[k];
+                        }
+                        acc += c;
+                    }
+                }
+                seq = __builtin_amdgcn_readlane(seq_l, src2);
+                part = __builtin_amdgcn_readlane(part_l, src2);
+            }
+        }
+        if (lane == 0) {
+            res[0] = seq;
+            res[1] = part;
+        }
+    }
+    __syncthreads();
+    const int seq = res[0], part = res[1];
+    __syncthreads();  // every thread has read res before the body may reuse the LDS
+    if (seq < 0 || seq >= S) return false;
+    *out = make_work_item(a, seq, unit, part);
+    return true;
+}
+
+// Self-scheduled item of this workgroup: the (blockIdx / U)-th item, in
+// longest-first order, of all (sequence, partition) items expanded over the
+// U units of a sequence -- the order the work-list builder writes, found by
+// each workgroup from context_lens without a pre-pass. Items are of `span`
+// tokens except each sequence's last (a zero-length context has one empty
+// item). Longest first means: by tile count, longest bucket first, and
+// within a bucket in (sequence, partition) order. All full items share the
+// first bucket; each sequence adds at most one shorter item. Returns false
+// (uniformly) when the block index is past the last item. lds: kSelfLdsInts
+// ints of scratch; contains barriers: every thread must call it.
+__device__ __forceinline__ bool self_scheduled_item(const DecodeArgs& a, int* lds, WorkItem* out) {
+    const int T = (int)blockDim.x, t = (int)threadIdx.x;
+    const int S = a.num_seqs;
+    const int span = a.partition_tokens * a.wave_partitions;
+    const int KT = span / kTile;  // tiles of a full item (span is a multiple of the tile)
+    const int NB = KT + 1;        // buckets: k = KT - tiles, k = 0 holds full items
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    int* hist = lds;               // [NB <= kSelfBuckets]
+    int* wsum = lds + kSelfBuckets;
+    int* res = wsum + 16;          // [4]: bucket, rank in it, then sequence, item
+    // thread t owns sequences [i0, i1) (contiguous, so prefix sums follow sequence order)
+    const int C = (S + T - 1) / T;
+    const int i0 = min(t * C, S), i1 = min(i0 + C, S);
+    for (int k = t; k < NB; k += T) hist[k] = 0;
+    if (t == 0) res[2] = -1;  // no sequence found: skip rather than read out of bounds
+    __syncthreads();
+    int full = 0;
+    for (int i = i0; i < i1; ++i) {
+        int ctx = a.context_lens[i];
+        ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+        const int f = ctx / span, rem = ctx - f * span;
+        full += f;
+        if (rem > 0 || ctx == 0) atomicAdd(&hist[KT - (rem + kTile - 1) / kTile], 1);
+    }
+    if (full > 0) atomicAdd(&hist[0], full);
+    __syncthreads();
+    // prefix over the buckets: thread t owns buckets [k0, k1)
+    const int CB = (NB + T - 1) / T;
+    const int k0 = min(t * CB, NB), k1 = min(k0 + CB, NB);
+    int local = 0;
+    for (int k = k0; k < k1; ++k) local += hist[k];
+    int total = 0;
+    const int run = block_exclusive_scan(local, wsum, &total);
+    const int b = (int)blockIdx.x;
+    const int pb = b / a.units_per_seq, unit = b - pb * a.units_per_seq;
+    if (pb >= total) return false;
+    if (pb >= run && pb < run + local) {  // exactly one thread holds the bucket of item pb
+        int acc = run;
+        for (int k = k0; k < k1; ++k) {
+            const int h = hist[k];
+            if (pb < acc + h) {
+                res[0] = k;
+                res[1] = pb - acc;
+                break;
+            }
+            acc += h;
+        }
+    }
+    __syncthreads();
+    const int kb = res[0], r = res[1];
+    // the r-th item of bucket kb in sequence order
+    auto count_in_bucket = [&](int ctx, int* part_of_last) -> int {
+        const int f = ctx / span, rem = ctx - f * span;
+        const bool partial = rem > 0 || ctx == 0;
+        *part_of_last = f;
+        return (kb == 0 ? f : 0) + ((partial && KT - (rem + kTile - 1) / kTile == kb) ? 1 : 0);
+    };
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) {
+        int ctx = a.context_lens[i];
+        ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+        int pl;
+        cnt += count_in_bucket(ctx, &pl);
+    }
+    int tot2 = 0;
+    const int pre = block_exclusive_scan(cnt, wsum, &tot2);
+    if (r >= pre && r < pre + cnt) {
+        int acc = pre;
+        for (int i = i0; i < i1; ++i) {
+            int ctx = a.context_lens[i];
+            ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+            int f;
+            const int c = count_in_bucket(ctx, &f);
+            if (r < acc + c) {
+                const int j = r - acc;  // the j-th item of this sequence in bucket kb
+                res[2] = i;
+                res[3] = (kb == 0 && j < f) ? j : f;  // a full item, or the sequence's last one
+                break;
+            }
+            acc += c;
+        }
+    }
+    __syncthreads();
+    const int seq = res[2], part = res[3];
+    __syncthreads();  // every thread has read res before the body may reuse the LDS
+    if (seq < 0 || seq >= S) return false;
+    *out = make_work_item(a, seq, unit, part);
+    return true;
+}
+
 // Runs `body(item)` for this workgroup's work item: with no schedule, the
-// (sequence, KV head, partition) its block index names; with a schedule, the
-// block index's entry of the device-built list. That list is compact and
-// longest first, so workgroups are dispatched in that order and those past
-// its end (the grid is sized for the most items there can be) exit at once,
-// after every real item has been dispatched. `body` must be called by the
-// whole workgroup.
+// (sequence, KV head, partition) its block index names; self-scheduled, the
+// item of the longest-first order it finds itself; with a schedule, the
+// block index's entry of the device-built list. The list (and the
+// self-scheduled order) is compact and longest first, so workgroups are
+// dispatched in that order and those past its end (the grid is sized for
+// the most items there can be) exit at once, after every real item has
+// been dispatched. `body` must be called by the whole workgroup. lds: the
+// kernel's LDS, kSelfLdsInts ints of which serve as scratch before `body`.
 template <class Body>
-__device__ __forceinline__ void for_each_item(const DecodeArgs& a, Body&& body) {
+__device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* lds, Body&& body) {
     if (a.items == nullptr) {
+        if (a.self_schedule) {
+            WorkItem wi;
+            const bool found = a.num_seqs <= kSelfWaveSeqs ? self_scheduled_item_wave(a, lds, &wi)
+                                                            : self_scheduled_item(a, lds, &wi);
+            if (found) body(wi);
+            return;
+        }
         const WorkItem wi = decode_work_item(a);
         if (wi.active) body(wi);
         return;

@@ -46,6 +46,10 @@ struct DecodeArgs {
     int32_t units_per_seq;         // work units per sequence: KV heads / heads per unit
     int32_t block_size_log2, max_blocks_per_seq;
     int32_t partition_tokens, num_partitions;
+    // Partitions per work item: 1, or the workgroup's W waves, each of which
+    // then takes one whole partition of the item (and stores its state);
+    // items per (sequence, unit) = ceil(num_partitions / wave_partitions).
+    int32_t wave_partitions, num_items;
     int32_t last_block;            // min(num_blocks, 2^31) - 1: the largest usable block id
     CacheLayout cache;
     float qk_scale_log2;           // scale * k_scale * log2(e)
@@ -53,7 +57,26 @@ struct DecodeArgs {
     // Device schedule (null = direct grid, one workgroup per item):
     const int4* items;             // see ScheduleArgs, longest first
     const int* item_count;         // number of valid items
+    // Self-scheduled (items null): workgroup b finds the b-th item of the
+    // longest-first order itself from context_lens (see pa_epilogue.h).
+    int32_t self_schedule;
 };
+
+// Self-scheduling: items (one per (sequence, unit) partition, or group of
+// partitions) are counted in buckets by tile count; full items all fall in
+// the first bucket, so a bucket per possible tile count of a sequence's last
+// item suffices: span / 16 + 1 <= kSelfBuckets for spans up to 4096 tokens.
+constexpr int kSelfBuckets = 264;
+constexpr int kSelfMaxSeqs = 4096;              // larger batches use the work-list builder
+// LDS scratch of the search (ints): bucket counts, then (workgroup-wide
+// search) the scan's wave sums and the handed-over item.
+constexpr int kSelfRes = kSelfBuckets + 16;
+constexpr int kSelfLdsInts = kSelfRes + 4;
+// Batches up to kSelfWaveSeqs sequences are ranked by one wave, with
+// kSelfSeqsPerLane sequences a lane (the default); larger ones (up to
+// kSelfMaxSeqs) by the whole workgroup.
+constexpr int kSelfSeqsPerLane = 4;
+constexpr int kSelfWaveSeqs = 64 * kSelfSeqsPerLane;
 
 // A scheduled work item: (seq, part << 16 | kv head, t_begin, t_end | kItemFinal).
 constexpr int kItemFinal = 1 << 30;  // the item stores the final output (no merge)
@@ -62,7 +85,13 @@ struct ScheduleArgs {
     const int32_t* context_lens;
     int4* items;
     int* item_count;
+    // Items cover partition_tokens each (num_partitions of them per
+    // sequence); an item stores the final output when its sequence's
+    // context, counted in split_tokens-token partitions (split_count per
+    // row), is a single partition. The two differ when an item spans
+    // several partitions, one per wave.
     int32_t num_seqs, num_kv_heads, partition_tokens, num_partitions;
+    int32_t split_tokens, split_count;
     int32_t max_context;           // max_blocks_per_seq * block_size
     // Cascade suffix pass: a sequence's items start after the tokens its
     // prefix group covers and, when it has any, none stores the final output.
@@ -161,6 +190,7 @@ struct LaunchShape {
     int waves;          // wavefronts per workgroup
     int depth;          // tiles a wave keeps in its register ring (2..4)
     int heads_per_unit; // MFMA kernel: adjacent KV heads sharing one 16-row tile (1, 2 or 4)
+    bool wave_partitions; // MFMA kernel: each wave takes one whole partition of the item
 };
 
 // A dispatch counts its work-items in 32 bits: the plans refuse

@@ -168,8 +168,8 @@ __global__ __launch_bounds__(kThreads) void pa_schedule_kernel(ScheduleArgs a) {
             const int p = f - soff[j];
             const int ctx = sctx[j], beg = sbeg[j];
             const int pos = atomicAdd(&hist[pair_key(min(P, ctx - beg - p * P))], 1);
-            const int np = pair_count(beg, ctx, P);
-            const int flags = (beg == 0 && (np <= 1 || a.num_partitions == 1)) ? kItemFinal : 0;
+            const int nsplit = (ctx - beg + a.split_tokens - 1) / a.split_tokens;
+            const int flags = (beg == 0 && (nsplit <= 1 || a.split_count == 1)) ? kItemFinal : 0;
             const int tb = beg + p * P;
             const int4 rec = make_int4(c0 + j, p << 16, tb, min(tb + P, ctx) | flags);
             int4* dst = a.items + (int64_t)pos * Hkv;

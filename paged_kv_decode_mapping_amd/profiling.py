@@ -31,8 +31,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # include, and the argument blocks they receive. The launch plan (waves,
 # tiles in flight, partitions) is stored next to the figure and compared
 # separately, so host-side changes elsewhere do not invalidate it. With a
-# plan, only the kernels it launches count: the work-list builder when it is
-# scheduled, the merge when it splits contexts.
+# plan, only the kernels it launches count: the work-list builder when it
+# uses a device-built list, the merge when it splits contexts.
 COMMON_SOURCES = ("pa_epilogue.h", "pa_device.h")
 KERNEL_SOURCES = {"mfma": "decode_mfma.hip", "valu": "decode_valu.hip"}
 COMMON_STRUCTS = ("DecodeArgs", "LaunchShape")
@@ -50,7 +50,7 @@ def kernel_source_hash(plan: Optional[dict] = None) -> str:
     structs = list(COMMON_STRUCTS)
     variants = [plan["variant"]] if plan else sorted(KERNEL_SOURCES)
     files += [KERNEL_SOURCES[v] for v in variants]
-    if plan is None or plan.get("scheduled"):
+    if plan is None or (plan.get("scheduled") and not plan.get("self_scheduled")):
         files += ["schedule.hip", "pa_cascade.h"]
         structs.append("ScheduleArgs")
     if plan is None or plan.get("num_partitions", 1) > 1:

@@ -136,7 +136,7 @@ def _with(d, **kw):
     (dict(opts=pa._opts(partition_tokens=32, schedule=-1)), -6), (dict(opts=pa._opts(prefetch=4)), -2),
     (dict(opts=pa._opts(prefetch=-1)), -2), (dict(Hq=16, Hkv=2, opts=pa._opts(variant="valu")), -3),
     (dict(opts=pa._opts(partition_tokens=32, schedule=-1), ws=A, wsb=16), -6),
-    (dict(opts=pa._opts(partition_tokens=-1, schedule=1)), -6), (dict(opts=pa._opts(partition_tokens=-1, schedule=2)), -2),
+    (dict(opts=pa._opts(partition_tokens=-1, schedule=1)), -6), (dict(opts=pa._opts(partition_tokens=-1, schedule=3)), -2),
     (dict(opts=pa._opts(partition_tokens=-1, schedule=1), ws=A + 16, wsb=1 << 20), -4),
     (dict(opts=_reserved(1)), -2), (dict(opts=_reserved(-1)), -2),
     (dict(opts=pa._opts(partition_tokens=-1, heads_per_tile=3)), -2),
@@ -235,11 +235,30 @@ def test_plan_with_explicit_partitions(lib):
     rows = S * Hq * 8
     assert p["workspace_bytes"] == _align(rows * 8) + rows * D * 4
     assert p["variant"] == "valu" and p["prefetch_tiles"] == 2
-    # scheduled (the default when contexts are split): a 256-byte header and
-    # the item list come first
-    ps = _plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4)
-    assert ps["scheduled"] and ps["num_workgroups"] == S * Hkv * 8
-    assert ps["workspace_bytes"] == 256 + _align(S * Hkv * 8 * 16) + _align(rows * 8) + rows * D * 4
+    # longest-first items (the default when contexts are split), found by
+    # each workgroup when the grid is small (S * partitions <= 1024): no
+    # list in the workspace
+    ps = _plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4, schedule=2)
+    assert ps["scheduled"] and ps["self_scheduled"] and ps["num_workgroups"] == S * Hkv * 8
+    assert ps["workspace_bytes"] == _align(rows * 8) + rows * D * 4
+    # the device-built list: a 256-byte header and the item list come first
+    pl = _plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4, schedule=1)
+    assert pl["scheduled"] and not pl["self_scheduled"] and pl["num_workgroups"] == S * Hkv * 8
+    assert pl["workspace_bytes"] == 256 + _align(S * Hkv * 8 * 16) + _align(rows * 8) + rows * D * 4
+    assert _plan(S, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4)["self_scheduled"]
+    assert not _plan(S, Hq, Hkv, D, 16, 512, partition_tokens=512, variant="valu", waves=4)["self_scheduled"]
+    # more sequences than one wave ranks: the list by default, and beyond
+    # what a workgroup ranks, only the list
+    assert _plan(256, Hq, Hkv, D, 16, 64, partition_tokens=256, variant="valu", waves=4)["self_scheduled"]
+    p257 = _plan(257, Hq, Hkv, D, 16, 64, partition_tokens=256, variant="valu", waves=4)
+    assert p257["scheduled"] and not p257["self_scheduled"]
+    assert _plan(4096, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4,
+                 schedule=2)["self_scheduled"]
+    pb = _plan(4097, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4)
+    assert pb["scheduled"] and not pb["self_scheduled"]
+    with pytest.raises(pa.PAError) as e:
+        _plan(4097, Hq, Hkv, D, 16, 256, partition_tokens=512, variant="valu", waves=4, schedule=2)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED
     p1 = _plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, prefetch=3, schedule=-1)
     assert p1["num_partitions"] == 1 and p1["workspace_bytes"] == 0 and p1["prefetch_tiles"] == 3
     assert p1["variant"] == "mfma" and p1["partition_tokens"] == 112
@@ -247,6 +266,8 @@ def test_plan_with_explicit_partitions(lib):
     assert not p1d["scheduled"] and p1d["workspace_bytes"] == 0
     p1s = _plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, schedule=1)
     assert p1s["scheduled"] and p1s["workspace_bytes"] == 256 + _align(4 * 2 * 16)
+    p1t = _plan(4, 8, 2, 64, 16, 7, partition_tokens=-1, schedule=2)
+    assert p1t["self_scheduled"] and p1t["workspace_bytes"] == 0
     # a partition longer than the longest possible context is no split
     p2 = _plan(4, 8, 2, 64, 16, 7, partition_tokens=4096)
     assert p2["num_partitions"] == 1

@@ -56,13 +56,46 @@ def test_split_and_waves_agree_with_oracle(lib, name, partition, waves, variant)
     ref = _oracle(w)
     d = DeviceWorkload(w)
     prefetch = 1 + (waves + partition) % 3  # every ring depth, spread over the cases
-    schedule = 1 if (waves + partition // 16) % 2 else -1  # device work list, or the direct grid
+    # device-built list, direct grid, or items found by each workgroup
+    schedule = (1, -1, 2)[(waves + partition // 16) % 3]
     note(f"decode {name} partition={partition} waves={waves} variant={variant} prefetch={prefetch} "
          f"schedule={schedule}")
     out = d.decode(partition_tokens=partition, waves=waves, variant=variant, prefetch=prefetch,
                    schedule=schedule)
     torch.cuda.synchronize()
     compare(host_bits(out), ref, *BF16_TOL)
+
+
+@pytest.mark.parametrize("name", ["tiny", "long_splitk", "mixed_batch"])
+@pytest.mark.parametrize("partition", [16, 48, 512, 1024])
+@pytest.mark.parametrize("wave_partitions", [1, -1])
+@pytest.mark.parametrize("schedule", [1, -1, 2])
+def test_wave_partitions_agree_with_oracle(lib, name, partition, wave_partitions, schedule):
+    """Split contexts with one partition per wave (a workgroup covers W
+    consecutive partitions, each wave storing its own state) and with the
+    waves sharing one partition, on the device work list, with each
+    workgroup finding its own item, and on the direct grid: ragged lengths, contexts shorter than one partition (whose single
+    partition stores the output itself), a last group with waves past the
+    context, and zero-length rows. bf16 and fp8 caches and both pool layouts
+    alternate over the cases."""
+    w = W.make_workload(name, **REDUCED[name])
+    i = (partition // 16 + wave_partitions + schedule) % 4
+    kv, layout = ("bf16", "fp8")[i % 2], ("page", "head_major")[i // 2]
+    ks = vs = 1.0
+    kc, vc, kvd, tol = w.k_cache, w.v_cache, oracle.KV_BF16, BF16_TOL
+    if kv == "fp8":
+        ks, vs = w.fp8_scales
+        kc, vc = oracle.quantize_pool(kc, ks), oracle.quantize_pool(vc, vs)
+        kvd, tol = oracle.KV_FP8_E4M3FN, FP8_TOL
+    d = DeviceWorkload(w, kc, vc, layout=layout)
+    opts = dict(partition_tokens=partition, wave_partitions=wave_partitions, schedule=schedule, variant="mfma")
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, **opts)
+    assert plan["wave_partitions"] == (wave_partitions == 1 and plan["num_partitions"] > 1)
+    note(f"wave partitions {name} {kv} {layout} {opts} plan={plan}")
+    out = d.decode(k_scale=ks, v_scale=vs, **opts)
+    torch.cuda.synchronize()
+    ref = oracle.decode_workload(w, kv_dtype=kvd, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+    compare(host_bits(out), ref, *tol)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -93,11 +126,13 @@ def test_decode_is_deterministic(lib, variant):
     a = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=1))
     b = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=1))
     c = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=-1))
+    e = host_bits(d.decode(partition_tokens=512, variant=variant, schedule=2))
     assert np.array_equal(a, b)
     assert np.array_equal(a, c)
+    assert np.array_equal(a, e)
 
 
-@pytest.mark.parametrize("schedule", [1, -1])
+@pytest.mark.parametrize("schedule", [1, -1, 2])
 def test_full_size_mixed_batch_sampled(lib, schedule):
     """The mixed continuous batch at its full size (256 sequences, lognormal
     lengths, shared prefix), in the launch configuration the benchmark uses,
@@ -522,8 +557,43 @@ def test_many_short_items_per_workgroup(lib, variant):
         note(f"many short items {variant} partition={part}")
         a = host_bits(d.decode(variant=variant, partition_tokens=part, schedule=1))
         b = host_bits(d.decode(variant=variant, partition_tokens=part, schedule=-1))
+        c = host_bits(d.decode(variant=variant, partition_tokens=part, schedule=2))
         compare(a, ref, *BF16_TOL)
         assert np.array_equal(a, b)
+        assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("S,waves,partition,wpp", [(4096, 1, 16, -1), (4096, 4, 32, 1), (1, 8, 512, 1),
+                                                    (37, 2, 48, -1), (256, 4, 16, -1), (64, 1, 512, -1),
+                                                    (257, 8, 16, 1)])
+def test_self_scheduled_items_cover_every_item(lib, S, waves, partition, wpp):
+    """Each workgroup ranks its own block index among the items of
+    context_lens (counts by length in LDS, then scans): by its first wave
+    alone up to 256 sequences (4 a lane; 1, 37, 64 and 256 here), by the
+    whole workgroup beyond (257, 4096), up to the largest batch it serves
+    (4096 sequences with one wave: 64 sequences per thread). Zero,
+    one-token, tile-edge, partition-edge and full-table contexts, spans of
+    one partition and of a wave per partition: the oracle's output and the
+    direct grid's bits."""
+    rng = np.random.default_rng(S + waves)
+    MB = 4
+    cap = MB * 16
+    edges = [0, 1, 15, 16, 17, partition - 1, partition, partition + 1, cap]
+    ctx = [int(min(cap, rng.choice(edges) if rng.random() < 0.5 else rng.integers(0, cap + 1))) for _ in range(S)]
+    w = W.make_workload("mixed_batch", num_seqs=S, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                        context=("list", ctx), shared_prefix_tokens=0)
+    ref = _oracle(w)
+    d = DeviceWorkload(w)
+    opts = dict(variant="mfma", waves=waves, partition_tokens=partition, wave_partitions=wpp)
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, schedule=2, **opts)
+    assert plan["self_scheduled"]
+    note(f"self-scheduled S={S} {opts} plan={plan}")
+    a = host_bits(d.decode(schedule=2, **opts))
+    b = host_bits(d.decode(schedule=-1, **opts))
+    compare(a, ref, *BF16_TOL)
+    assert np.array_equal(a, b)
+    va = host_bits(d.decode(schedule=2, variant="valu", waves=waves, partition_tokens=partition))
+    compare(va, ref, *BF16_TOL)
 
 
 def _copy_case(rng, N, n, extra_bad=True):
