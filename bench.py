@@ -491,6 +491,7 @@ PER_CONFIG = [
     ("long_splitk", "bf16", 0),
     ("mixed_batch", "bf16", 0),
     ("mixed_batch", "fp8", 0),
+    ("long_splitk", "fp8", 0),
     ("llama70b_gqa", "fp8", 0),
 ]
 EVICT_BELOW_BYTES = 1 << 30  # KV smaller than this could stay in the 256 MB Infinity Cache between steps

@@ -123,8 +123,9 @@ typedef struct pa_decode_opts {
                                  each workgroup ranks its block index among
                                  the items of context_lens itself (at most
                                  4096 sequences; PA_ERR_UNSUPPORTED beyond;
-                                 for more than 16 query heads per KV head,
-                                 as 1); -1 = one workgroup per (sequence, KV
+                                 for more than 16 query heads per KV head at
+                                 most 256, as 1 beyond); -1 = one workgroup
+                                 per (sequence, KV
                                  head, partition) in index order, empty ones
                                  included; 0 = when the plan splits
                                  contexts, 2 for batches of at most 256

@@ -57,10 +57,12 @@
 // context).
 //
 // Order. With a work list (the decode path's longest-first list of
-// (sequence, KV head, partition) items) workgroups take items in that order,
-// so the longest contexts start first; one cooperative tile stream per
-// workgroup makes a long item slow, and a long item started last would
-// stretch the whole launch.
+// (sequence, KV head, partition) items), or with each workgroup ranking its
+// block index in that order itself (batches of up to 256 sequences, no
+// builder pass), workgroups take items longest first, so the longest
+// contexts start first; one cooperative tile stream per workgroup makes a
+// long item slow, and a long item started last would stretch the whole
+// launch.
 #include "pa_cascade.h"
 #include "pa_merge.h"
 
@@ -148,8 +150,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
 
     // ---- the work item
     int bid = (int)blockIdx.x;
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
     MultiItem it;
-    if (a.items != nullptr) {
+    if (a.self_schedule) {
+        // longest-first (sequence, partition) items, ranked by this workgroup
+        // itself, expanded over (KV head, row block) units
+        int unit;
+        if (!rank_item_wave(a.context_lens, a.num_seqs, a.partition_tokens, cap, a.num_kv_heads * a.row_blocks, bid,
+                            reinterpret_cast<int*>(smem), &it.seq, &it.part, &unit))
+            return;
+        it.kvh = unit / a.row_blocks;
+        it.rb = unit - it.kvh * a.row_blocks;
+    } else if (a.items != nullptr) {
         const int idx = bid / a.row_blocks;
         it.rb = bid - idx * a.row_blocks;
         const int count = *a.item_count;
@@ -166,7 +178,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         it.kvh = bid % a.num_kv_heads;
         it.seq = bid / a.num_kv_heads;
     }
-    const int cap = a.max_blocks_per_seq << a.block_size_log2;
     // A cascade prefix pass: item "sequence" k is prefix group k, whose
     // member sequences are the query rows (one token each).
     const bool prefix_pass = a.cascade.group_start != nullptr;

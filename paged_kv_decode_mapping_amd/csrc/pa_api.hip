@@ -139,8 +139,16 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     // per sequence on a ragged batch, 531 -> 384 us). Unsplit, the direct
     // grid keeps the KV heads of a sequence adjacent, which measured faster.
     p.scheduled = p.num_partitions > 1 && p.num_partitions < 32768 && Hkv < 65536 && schedule >= 0;
+    // The longest-first order without the builder pass, by the rule of the
+    // decode kernels (make_plan): one wave ranks the batch, small grids.
+    // Measured on MQA (128 sequences of 4096 tokens, one KV head, 64 query
+    // heads, 1024-token partitions): the builder pass and its launch gap
+    // cost more than the workgroups' own search.
+    const bool self_ok = S <= pa::kSelfWaveSeqs && P / pa::kTile + 1 <= pa::kSelfBuckets;
+    p.self_scheduled = p.scheduled && self_ok &&
+                       (schedule == 2 || (schedule == 0 && (int64_t)S * p.num_partitions <= kSelfMaxPairs));
     size_t off = 0;
-    if (p.scheduled) {
+    if (p.scheduled && !p.self_scheduled) {
         p.items_off = kHeaderBytes;
         off = p.items_off + align_up((size_t)S * Hkv * p.num_partitions * 4 * sizeof(int32_t), 256);
     }
@@ -507,7 +515,8 @@ int run_multi(const Plan& p, const Geom& g, const int32_t* query_start, int32_t 
     pa::MultiArgs a =
         multi_args(p, g, g.tables, g.S, query_start, Tq, maxq, scale, kv_dtype, k_scale, v_scale, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.scheduled) {
+    a.self_schedule = p.self_scheduled ? 1 : 0;
+    if (p.scheduled && !p.self_scheduled) {
         char* ws = static_cast<char*>(workspace);
         pa::ScheduleArgs sa{};
         sa.context_lens = g.context_lens;

@@ -152,26 +152,29 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
     return x - v;
 }
 
-// Batches of at most kSelfWaveSeqs sequences: the first wave alone finds
-// the item (lane l holds sequences kSelfSeqsPerLane * l onward in registers,
-// so context_lens is read once and the scans are wave-wide shuffles), and
-// one barrier hands it to the other waves. The grid is sized for the most
-// items there can be, so most workgroups of a ragged or short batch have
-// none: those learn it from the item total alone, one wave-wide sum after
-// the read, and exit before any of the ranking. Same order and result as
-// the workgroup-wide search below. lds: kSelfLdsInts ints of scratch,
-// reusable by the body once this returns.
-__device__ __forceinline__ bool self_scheduled_item_wave(const DecodeArgs& a, int* lds, WorkItem* out) {
+// Rank `b` among the items of a batch of at most kSelfWaveSeqs sequences,
+// expanded over `units` units each, in longest-first order: the first wave
+// alone does it (lane l holds sequences kSelfSeqsPerLane * l onward in
+// registers, so context_lens is read once and the scans are wave-wide
+// shuffles), and one barrier hands the result to the other waves. Items
+// are `span` tokens of a sequence (a multiple of the tile), the last one
+// shorter, a zero-length context one empty item; lengths are clamped to
+// [0, cap]. The grid is sized for the most items there can be, so most
+// workgroups of a ragged or short batch have none: those learn it from the
+// item total alone, one wave-wide sum after the read, and exit before any
+// of the ranking. Same order and result as the workgroup-wide search
+// below. Returns false (uniformly) past the last item, else the item's
+// sequence, its index within the sequence and the unit. lds: kSelfLdsInts
+// ints of scratch, reusable by the caller once this returns. Contains
+// barriers: every thread of the workgroup must call it.
+__device__ __forceinline__ bool rank_item_wave(const int32_t* context_lens, int S, int span, int cap, int units,
+                                               int b, int* lds, int* seq_out, int* part_out, int* unit_out) {
     const int t = (int)threadIdx.x, lane = t & 63;
-    const int S = a.num_seqs;
-    const int span = a.partition_tokens * a.wave_partitions;
-    const int KT = span / kTile;  // tiles of a full item (span is a multiple of the tile)
+    const int KT = span / kTile;  // tiles of a full item
     const int NB = KT + 1;        // buckets: k = KT - tiles, k = 0 holds full items
-    const int cap = a.max_blocks_per_seq << a.block_size_log2;
     int* hist = lds;  // [NB <= kSelfBuckets]
     int* res = lds + kSelfRes;
-    const int b = (int)blockIdx.x;
-    const int pb = b / a.units_per_seq, unit = b - pb * a.units_per_seq;
+    const int pb = b / units, unit = b - pb * units;
     if (t < 64) {
         int full[kSelfSeqsPerLane], last[kSelfSeqsPerLane];  // full items; bucket of the last (-1: none)
         int fsum = 0, items = 0;
@@ -181,7 +184,7 @@ __device__ __forceinline__ bool self_scheduled_item_wave(const DecodeArgs& a, in
             full[k] = 0;
             last[k] = -1;
             if (i < S) {
-                int ctx = a.context_lens[i];
+                int ctx = context_lens[i];
                 ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
                 const int f = ctx / span, rem = ctx - f * span;
                 full[k] = f;
@@ -264,8 +267,22 @@ __device__ __forceinline__ bool self_scheduled_item_wave(const DecodeArgs& a, in
     }
     __syncthreads();
     const int seq = res[0], part = res[1];
-    __syncthreads();  // every thread has read res before the body may reuse the LDS
+    __syncthreads();  // every thread has read res before the caller may reuse the LDS
     if (seq < 0 || seq >= S) return false;
+    *seq_out = seq;
+    *part_out = part;
+    *unit_out = unit;
+    return true;
+}
+
+// The decode kernels' self-scheduled item for batches of at most
+// kSelfWaveSeqs sequences (see rank_item_wave).
+__device__ __forceinline__ bool self_scheduled_item_wave(const DecodeArgs& a, int* lds, WorkItem* out) {
+    int seq, part, unit;
+    if (!rank_item_wave(a.context_lens, a.num_seqs, a.partition_tokens * a.wave_partitions,
+                        a.max_blocks_per_seq << a.block_size_log2, a.units_per_seq, (int)blockIdx.x, lds, &seq,
+                        &part, &unit))
+        return false;
     *out = make_work_item(a, seq, unit, part);
     return true;
 }

@@ -149,6 +149,9 @@ struct MultiArgs {
     // item b / row_blocks, row block b % row_blocks.
     const int4* items;
     const int* item_count;
+    // Self-scheduled (items null): workgroup b ranks itself in the same order
+    // (batches of at most kSelfWaveSeqs sequences).
+    int32_t self_schedule;
     // Cascade prefix pass (cascade.group_start non-null): the grid's
     // "sequence" k is prefix group k, block_tables holds the prefix tables,
     // the query rows are the members' (one token each, q row = sequence),

@@ -383,13 +383,19 @@ def test_multi_nothing_to_do_is_a_no_op(lib):
 
 
 def test_multi_workspace_size(lib):
-    """Unsplit: nothing. Split: header (item count) + the work list of
-    (sequence, KV head, partition) items, then the split-K partials."""
+    """Unsplit: nothing. Split: the split-K partials, after a header (item
+    count) and the work list of (sequence, KV head, partition) items when
+    the batch is too large for the workgroups to rank their items
+    themselves (more than 256 sequences)."""
     S, Tq, Hq, Hkv, D = 4, 10, 8, 2, 64
     q, kc, bt = pa.TensorSpec((Tq, Hq, D), BF16), pa.TensorSpec((32, 16, Hkv, D), BF16), pa.TensorSpec((S, 7), I32)
     assert pa.pa_decode_multi_workspace_size(q, kc, bt, 4, partition_tokens=-1) == 0
     n = pa.pa_decode_multi_workspace_size(q, kc, bt, 4, partition_tokens=32)
     P = -(-7 * 16 // 32)
+    assert n == _align(Tq * Hq * P * 2 * 4) + Tq * Hq * P * D * 4
+    S, Tq = 300, 600
+    q, bt = pa.TensorSpec((Tq, Hq, D), BF16), pa.TensorSpec((S, 7), I32)
+    n = pa.pa_decode_multi_workspace_size(q, kc, bt, 4, partition_tokens=32)
     assert n == 256 + _align(S * Hkv * P * 16) + _align(Tq * Hq * P * 2 * 4) + Tq * Hq * P * D * 4
 
 

@@ -141,3 +141,45 @@ def test_decode_mqa_wide_groups(lib, Hq, Hkv, D, partition):
     got = host_bits(d.decode(partition_tokens=partition))
     torch.cuda.synchronize()
     compare(got, ref, *BF16_TOL)
+    if plan["num_partitions"] > 1:
+        # the builder's list, the workgroups' own ranking and the direct grid: the same bits
+        for schedule in (1, 2, -1):
+            assert np.array_equal(host_bits(d.decode(partition_tokens=partition, schedule=schedule)), got)
+
+
+@pytest.mark.parametrize("S", [256, 300])
+def test_multi_rows_ordered_by_the_workgroups_or_the_list(lib, S):
+    """Split multi-row items, longest first: ranked by each workgroup itself
+    up to 256 sequences (with MQA heads through pa_decode, schedule = 2), by
+    the builder's list beyond (300) or when asked (schedule = 1); ragged
+    and zero lengths; the same bits as the direct grid and the oracle."""
+    rng = np.random.default_rng(S)
+    ctx = [int(x) for x in rng.integers(0, 700, size=S)]
+    ctx[0], ctx[1] = 0, 699
+    w = W.make_workload("mixed_batch", num_seqs=S, context=("list", ctx), num_q_heads=32, num_kv_heads=1,
+                        head_dim=64, shared_prefix_tokens=0)
+    ref = oracle.decode_workload(w)
+    d = DeviceWorkload(w)
+    outs = {}
+    for schedule in (0, 1, 2, -1):
+        plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, partition_tokens=64, schedule=schedule)
+        assert plan["num_partitions"] > 1
+        if schedule == 0:
+            assert plan["self_scheduled"] == (S <= 256 and S * plan["num_partitions"] <= 1024)
+        if schedule == 2:
+            assert plan["self_scheduled"] == (S <= 256)
+        note(f"multi-row order S={S} schedule={schedule} plan={plan}")
+        outs[schedule] = host_bits(d.decode(partition_tokens=64, schedule=schedule))
+    compare(outs[0], ref, *BF16_TOL)
+    for schedule in (1, 2, -1):
+        assert np.array_equal(outs[schedule], outs[0])
+    # pa_decode_multi (several query tokens) on the same batch, with its own plan
+    qlens = [min(int(x), c) for x, c in zip(rng.integers(0, 4, size=S), ctx)]
+    mq = W.make_multi_query(w, qlens)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    qs = torch.from_numpy(mq.query_start).cuda()
+    note(f"multi-row order S={S} pa_decode_multi")
+    got = host_bits(pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, qs, w.scale,
+                                       int(max(qlens)), partition_tokens=64))
+    mref = oracle.multi_decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq.query_start, w.scale)
+    compare(got, mref, *BF16_TOL)
