@@ -52,18 +52,18 @@ def write_bytes(w, kv_bytes: int) -> int:
     return int(T * s.num_kv_heads * s.head_dim * (2 * 2 + 2 * kv_bytes) + 8 * T)
 
 
-def load_traffic(workload: str, kv: str, plan: dict):
+def load_traffic(workload: str, kv: str, plan: dict, layout: str = "page", partition_tokens: int = 0):
     """HBM traffic per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources with the same
-    launch plan."""
-    p = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}_{kv}.json")
+    summary of this configuration, if it was taken on the current kernel
+    sources with the same launch plan."""
+    from paged_kv_decode_mapping_amd.profiling import kernel_source_hash, traffic_file
+    p = traffic_file(workload, kv, layout, partition_tokens or 0)
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
     except Exception:
         return None
-    from paged_kv_decode_mapping_amd.profiling import kernel_source_hash
     if d.get("kernel_source_hash") != kernel_source_hash(plan) or d.get("plan") != plan:
         return None
     return d.get("bytes_per_launch")
@@ -642,7 +642,8 @@ def per_config(args, dev, skip) -> list:
                               "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
                 "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
                 "decode_tokens_per_s": round(w.spec.num_seqs / (avg * 1e-3), 1),
-                "cache_evicted_between_launches": evict}
+                "cache_evicted_between_launches": evict,
+                "traffic": load_traffic(name, kv, plan, layout, part)}
             if kv == "fp8" and layout == "page":
                 entry["fp8_accuracy"] = fp8_accuracy(b, out)
             if not args.no_cpu_baseline and layout == "page":
@@ -807,7 +808,7 @@ def main() -> int:
         log("timing the CPU oracle on a bounded sample")
         base = cpu_baseline(w, args.kv, kq, vq)
         log(f"cpu baseline {base}")
-    traffic = load_traffic(args.workload, args.kv, plan) if args.layout == "page" else None
+    traffic = load_traffic(args.workload, args.kv, plan, args.layout, args.partition)
     tok_s = s.num_seqs / (ms_per_step * 1e-3)
     head = dict(workload=args.workload, kv=args.kv, part=args.partition)
     del b, q, k_cache, v_cache, out, ws

@@ -2,7 +2,7 @@
 
     python -m paged_kv_decode_mapping_amd.profiling stats  <rocprof dir> <out.md> --cmd "<command>"
     python -m paged_kv_decode_mapping_amd.profiling traffic <fetch dir> <write dir> <out.json> \
-        --workload NAME --kv bf16 --copy-bytes N --cmd "<commands>"
+        --workload NAME --kv bf16 [--layout head_major] [--partition P] --copy-bytes N --cmd "<commands>"
 
 `stats` reads the kernel statistics CSV of a `rocprofv3 --kernel-trace
 --stats --output-format csv` run. `traffic` reads the counter-collection CSVs
@@ -68,8 +68,10 @@ def kernel_source_hash(plan: Optional[dict] = None) -> str:
     return h.hexdigest()[:16]
 
 
-def decode_plan(workload: str, kv: str) -> dict:
-    """The launch plan pa_decode uses for a named workload on this GPU."""
+def decode_plan(workload: str, kv: str, layout: str = "page", partition_tokens: int = 0) -> dict:
+    """The launch plan pa_decode uses for a named workload on this GPU, with
+    the page's pool layout or the head-major one, and the default partition
+    choice or a given partition size."""
     import paged_kv_decode_mapping_amd as pa
     from paged_kv_decode_mapping_amd import workloads as W
     s = W.SPECS[workload]
@@ -78,15 +80,30 @@ def decode_plan(workload: str, kv: str) -> dict:
            "list": lambda: max(ctx[1])}[ctx[0]]()
     mb = -(-int(cap) // s.block_size)
     specs = pa.decode_specs(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, mb,
-                            pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN)
-    return pa.pa_decode_get_plan(*specs)
+                            pa.PA_KV_BF16 if kv == "bf16" else pa.PA_KV_FP8_E4M3FN,
+                            head_major=(layout == "head_major"))
+    return pa.pa_decode_get_plan(*specs, partition_tokens=partition_tokens)
 
 
-def _plan_or_none(workload: str, kv: str):
+def traffic_file(workload: str, kv: str, layout: str = "page", partition_tokens: int = 0) -> str:
+    """Name of the committed traffic summary of a decode configuration."""
+    tag = ("" if layout == "page" else "_" + layout) + ("" if partition_tokens == 0 else f"_p{partition_tokens}")
+    return os.path.join(ROOT, "profiles", f"traffic_decode_{workload}_{kv}{tag}.json")
+
+
+def _plan_or_none(workload: str, kv: str, layout: str = "page", partition_tokens: int = 0):
     try:
-        return decode_plan(workload, kv)
+        return decode_plan(workload, kv, layout, partition_tokens)
     except Exception:  # unknown workload, or no GPU to plan for: the figure is then never reported
         return None
+
+
+def _plan_from_log(path: str):
+    """The launch plan a profiled bench.py run printed in its JSON line."""
+    for line in reversed(open(path).read().splitlines()):
+        if line.startswith("{"):
+            return json.loads(line).get("config", {}).get("plan")
+    return None
 
 
 def _find(d: str, suffix: str) -> str:
@@ -187,8 +204,9 @@ def cmd_traffic(a) -> None:
            "fetch_counter_per_copy_byte": cf / a.copy_bytes, "write_counter_per_copy_byte": cw / a.copy_bytes,
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
            "dispatches": len(dfetch)}
-    plan = _plan_or_none(a.workload, a.kv)
-    res.update({"kernel_source_hash": kernel_source_hash(plan), "plan": plan, "command": a.cmd})
+    plan = _plan_from_log(a.bench_log) if a.bench_log else _plan_or_none(a.workload, a.kv, a.layout, a.partition)
+    res.update({"layout": a.layout, "partition_tokens_asked": a.partition,
+                "kernel_source_hash": kernel_source_hash(plan), "plan": plan, "command": a.cmd})
     json.dump(res, open(a.out, "w"), indent=1)
     print(json.dumps(res, indent=1))
 
@@ -209,7 +227,12 @@ def main() -> int:
     t.add_argument("out")
     t.add_argument("--workload", required=True)
     t.add_argument("--kv", default="bf16")
+    t.add_argument("--layout", choices=["page", "head_major"], default="page")
+    t.add_argument("--partition", type=int, default=0, help="partition size asked for (0 = the plan's choice)")
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--bench-log", default="",
+                   help="output of one of the profiled bench.py runs: its plan is the one recorded "
+                        "(else the plan is asked of the library on this machine)")
     t.add_argument("--cmd", required=True)
     a = ap.parse_args()
     cmd_stats(a) if a.what == "stats" else cmd_traffic(a)

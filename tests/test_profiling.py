@@ -46,12 +46,16 @@ def test_traffic_scaling(tmp_path):
         fetch_dir, write_dir = str(tmp_path / "f"), str(tmp_path / "w")
         out = str(tmp_path / "t.json")
         workload, kv, copy_bytes, cmd = "w", "bf16", 1 << 20, "c"
+        layout, partition, bench_log = "head_major", 0, ""
     profiling.cmd_traffic(A)
     r = json.load(open(A.out))
     assert r["fetch_bytes_per_launch"] == 2100.0 * 1024
     assert r["write_bytes_per_launch"] == 12.0 * 1024
     assert r["kernel_source_hash"] == profiling.kernel_source_hash()
     assert r["plan"] is None  # unknown workload: no plan, so bench.py never reports this figure
+    assert r["layout"] == "head_major"
+    assert profiling.traffic_file("w", "fp8", "head_major", 512).endswith("traffic_decode_w_fp8_head_major_p512.json")
+    assert profiling.traffic_file("w", "bf16").endswith("traffic_decode_w_bf16.json")
 
 
 def test_source_hash_follows_the_plan():
