@@ -561,6 +561,40 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     }
 }
 
+// The sequence, first query row and query count of query row `qrow`: the
+// last i with query_start[i] <= qrow (n = 0 for rows no sequence owns).
+__device__ __forceinline__ void multi_row_owner(const MultiArgs& a, int qrow, int* seq, int* q0, int* n) {
+    if (a.query_start != nullptr) {
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.query_start[mid] <= qrow) lo = mid;
+            else hi = mid - 1;
+        }
+        *seq = lo;
+        *q0 = a.query_start[lo];
+        int k = a.query_start[lo + 1] - *q0;
+        k = k > a.max_query_len ? a.max_query_len : k;
+        if (*q0 < 0 || *q0 > a.num_query_rows) k = 0;
+        else if (k > a.num_query_rows - *q0) k = a.num_query_rows - *q0;
+        *n = k < 0 ? 0 : k;
+    } else {
+        *seq = qrow;
+        *q0 = qrow;
+        *n = 1;
+    }
+}
+
+// Partitions holding tokens query row r (of n) of a sequence with context L
+// attends to (positions 0..L - n + r).
+__device__ __forceinline__ int multi_row_partitions(const MultiArgs& a, int seq, int n, int r) {
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    int L = a.context_lens[seq];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int pos = L - n + r;
+    return pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
+}
+
 // One workgroup of 64 * W threads per (query row, query head): log-sum-exp
 // merge of the partitions that hold tokens the row attends to (positions
 // 0..p).
@@ -569,37 +603,33 @@ __global__ __launch_bounds__(64 * W) void pa_multi_merge_kernel(MultiArgs a) {
     __shared__ __align__(16) float red[merge_lds_floats<D, W>()];
     const int64_t wid = (int64_t)blockIdx.x;  // query row * Hq + query head
     const int qrow = (int)(wid / a.num_q_heads);
-    // the sequence of this query row: the last i with query_start[i] <= qrow
     int seq, q0, n;
-    if (a.query_start != nullptr) {
-        int lo = 0, hi = a.num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (a.query_start[mid] <= qrow) lo = mid;
-            else hi = mid - 1;
-        }
-        seq = lo;
-        q0 = a.query_start[seq];
-        n = a.query_start[seq + 1] - q0;
-        n = n > a.max_query_len ? a.max_query_len : n;
-        if (q0 < 0 || q0 > a.num_query_rows) n = 0;
-        else if (n > a.num_query_rows - q0) n = a.num_query_rows - q0;
-        n = n < 0 ? 0 : n;
-    } else {
-        seq = qrow;
-        q0 = qrow;
-        n = 1;
-    }
+    multi_row_owner(a, qrow, &seq, &q0, &n);
     const int r = qrow - q0;
     if (r < 0 || r >= n) return;  // not a row of this sequence's queries (malformed query_start)
-    const int cap = a.max_blocks_per_seq << a.block_size_log2;
-    int L = a.context_lens[seq];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int pos = L - n + r;
-    const int np = pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
+    const int np = multi_row_partitions(a, seq, n, r);
     const int head = (int)(wid - (int64_t)qrow * a.num_q_heads);
     merge_row<D, W>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np,
                     nullptr, nullptr, 0, a.out + (int64_t)qrow * a.out_row + (int64_t)head * a.out_head, red);
+}
+
+// Few partitions: one thread per (query row, query head, float4 column).
+template <int D, int NP>
+__global__ __launch_bounds__(256) void pa_multi_merge_flat_kernel(MultiArgs a) {
+    constexpr int C = D / 4;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t wid = gid / C;  // query row * Hq + query head
+    const int c = (int)(gid - wid * C);
+    if (wid >= (int64_t)a.num_query_rows * a.num_q_heads) return;
+    const int qrow = (int)(wid / a.num_q_heads);
+    int seq, q0, n;
+    multi_row_owner(a, qrow, &seq, &q0, &n);
+    const int r = qrow - q0;
+    if (r < 0 || r >= n) return;
+    const int np = multi_row_partitions(a, seq, n, r);
+    const int head = (int)(wid - (int64_t)qrow * a.num_q_heads);
+    merge_column<D, NP>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np, c,
+                        a.out + (int64_t)qrow * a.out_row + (int64_t)head * a.out_head);
 }
 
 template <int D, int W>
@@ -610,6 +640,14 @@ void launch_merge_w(const MultiArgs& a, int64_t rows, hipStream_t s) {
 template <int D>
 void launch_multi_merge(const MultiArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.num_query_rows * a.num_q_heads;
+    if (a.num_partitions <= kFlatMergeMaxStates) {
+        const dim3 grid((unsigned)((rows * (D / 4) + 255) / 256));
+        const int np = flat_merge_states(a.num_partitions);
+        if (np == 2) hipLaunchKernelGGL((pa_multi_merge_flat_kernel<D, 2>), grid, dim3(256), 0, s, a);
+        else if (np == 4) hipLaunchKernelGGL((pa_multi_merge_flat_kernel<D, 4>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((pa_multi_merge_flat_kernel<D, 8>), grid, dim3(256), 0, s, a);
+        return;
+    }
     const int w = merge_waves(D, a.num_partitions, rows);
     if (w <= 1) launch_merge_w<D, 1>(a, rows, s);
     else if (w == 2) launch_merge_w<D, 2>(a, rows, s);

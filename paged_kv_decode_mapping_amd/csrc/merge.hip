@@ -32,6 +32,25 @@ __global__ __launch_bounds__(64 * W) void pa_merge_kernel(MergeArgs a) {
                     red);
 }
 
+// Few partitions (at most kFlatMergeMaxStates): one thread per (sequence,
+// query head, float4 column), 256 threads a workgroup.
+template <int D, int NP>
+__global__ __launch_bounds__(256) void pa_merge_flat_kernel(MergeArgs a) {
+    constexpr int C = D / 4;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / C;  // seq * Hq + q head
+    const int c = (int)(gid - row * C);
+    if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;
+    const int seq = (int)(row / a.num_q_heads);
+    const int head = (int)(row - (int64_t)seq * a.num_q_heads);
+    int ctx = a.context_lens[seq];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+    const int np = (ctx + a.partition_tokens - 1) / a.partition_tokens;
+    if (np <= 1) return;  // the decode kernel stored the output itself
+    merge_column<D, NP>(a.part_ml + row * a.num_partitions * 2, a.part_o + row * a.num_partitions * D, np, c,
+                        a.out + (int64_t)seq * a.out_seq + (int64_t)head * a.out_head);
+}
+
 // Cascade merge: one workgroup per (sequence, query head). A sequence with
 // prefix tokens combines the prefix pass's states over them (partitions of
 // prefix_partition_tokens) with the suffix pass's states over the rest; a
@@ -85,8 +104,22 @@ hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D>
+void launch_flat(const MergeArgs& a, int64_t rows, hipStream_t s) {
+    const dim3 grid((unsigned)((rows * (D / 4) + 255) / 256));
+    const int np = flat_merge_states(a.num_partitions);
+    if (np == 2) hipLaunchKernelGGL((pa_merge_flat_kernel<D, 2>), grid, dim3(256), 0, s, a);
+    else if (np == 4) hipLaunchKernelGGL((pa_merge_flat_kernel<D, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((pa_merge_flat_kernel<D, 8>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+    if (a.num_partitions <= kFlatMergeMaxStates) {
+        if (a.head_dim == 64) launch_flat<64>(a, rows, s);
+        else launch_flat<128>(a, rows, s);
+        return hipGetLastError();
+    }
     const int w = merge_waves(a.head_dim, a.num_partitions, rows);
     if (a.head_dim == 64) launch_rows<64>(a, rows, w, s);
     else launch_rows<128>(a, rows, w, s);

@@ -116,4 +116,53 @@ __device__ __forceinline__ void merge_row(const float* ml0, const float* o0, int
     }
 }
 
+// Rows with few states (at most NP): one thread per (row, float4 column)
+// instead of a workgroup per row. A thread issues the loads of all the
+// row's states at once -- every (m, l) and its column of every o -- so a
+// row costs one memory round trip, and the C = D / 4 threads of a row each
+// compute the same M and L. States are summed in order 0..n-1. With one
+// workgroup per row the merge of hundreds of thousands of rows with 2
+// states (32 query tokens per sequence on the mixed batch: 262,144 rows)
+// was bound by that per-row latency: 142 us.
+constexpr int kFlatMergeMaxStates = 8;
+
+template <int D, int NP>
+__device__ __forceinline__ void merge_column(const float* ml, const float* o, int n, int c, uint16_t* dst) {
+    float m[NP], l[NP];
+    float4 v[NP];
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+        m[s] = -INFINITY;
+        l[s] = 0.0f;
+        v[s] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (s < n) {
+            const float2 st = *reinterpret_cast<const float2*>(ml + 2 * s);
+            m[s] = st.x;
+            l[s] = st.y;
+            v[s] = *reinterpret_cast<const float4*>(o + (int64_t)s * D + 4 * c);
+        }
+    }
+    float M = m[0];
+#pragma unroll
+    for (int s = 1; s < NP; ++s) M = fmaxf(M, m[s]);
+    float L = 0.0f, ox = 0.0f, oy = 0.0f, oz = 0.0f, ow = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+        const float f = state_weight(m[s], M);
+        L = fmaf(l[s], f, L);
+        ox = fmaf(v[s].x, f, ox);
+        oy = fmaf(v[s].y, f, oy);
+        oz = fmaf(v[s].z, f, oz);
+        ow = fmaf(v[s].w, f, ow);
+    }
+    const bool live = L > 0.0f;
+    uint2 packed;
+    packed.x = (uint32_t)f32_to_bf16_rne(live ? ox / L : 0.0f) | ((uint32_t)f32_to_bf16_rne(live ? oy / L : 0.0f) << 16);
+    packed.y = (uint32_t)f32_to_bf16_rne(live ? oz / L : 0.0f) | ((uint32_t)f32_to_bf16_rne(live ? ow / L : 0.0f) << 16);
+    *reinterpret_cast<uint2*>(dst + 4 * c) = packed;
+}
+
+// Smallest unrolled state count of merge_column covering n states (n <= 8).
+inline int flat_merge_states(int64_t n) { return n <= 2 ? 2 : (n <= 4 ? 4 : 8); }
+
 }  // namespace pa
