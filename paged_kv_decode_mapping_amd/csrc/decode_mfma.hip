@@ -31,7 +31,10 @@
 //     rounded to bf16 -- and A is V^T (row = d, token 4*gq + r), read from
 //     the LDS copy with gfx950's transposing LDS load. Lane l accumulates
 //     O[d = 16 j + 4 gq + r][head c], so the softmax rescale of head c stays
-//     in-lane.
+//     in-lane. The softmax denominator is one more such MFMA with A = ones:
+//     every element of its tile is the column's sum of the same rounded
+//     probabilities over all 16 tokens, with no VALU adds or cross-lane
+//     sums (measured on fp8 caches, where the SIMDs' issue is the limit).
 //   * fp8 caches: codes are widened to bf16 exactly (every e4m3fn value is a
 //     bf16 value) with v_cvt_scalef32_pk_bf16_fp8 while staging; the scales
 //     are folded into the score scale and the output.
@@ -136,7 +139,11 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
         }
 
         float m = -INFINITY;  // running max of head c (log2 units), same in all four lane groups
-        float l = 0.0f;       // running sum over this lane's tokens
+        // running sum of column c's probabilities over every token so far
+        // (all four lane groups' rows), as an MFMA accumulator: each tile adds
+        // ones(16 x 16) . P^T, so every element of the tile holds the sum
+        f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
         f32x4 o[NPV];
 #pragma unroll
         for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -253,11 +260,16 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             // online softmax for column c over rows 4*gq + r: a row counts
             // when it is a token of the column's KV head inside the context
             float x[4];
+            if (HP == 1 && full) {  // uniform: every row counts
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * gq + r;
-                const bool mine = HP == 1 || (row / TPH) == (c / TPH);
-                x[r] = (!mine || (!full && row % TPH >= valid)) ? -INFINITY : s[r] * qk;
+                for (int r = 0; r < 4; ++r) x[r] = s[r] * qk;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * gq + r;
+                    const bool mine = HP == 1 || (row / TPH) == (c / TPH);
+                    x[r] = (!mine || (!full && row % TPH >= valid)) ? -INFINITY : s[r] * qk;
+                }
             }
             float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
             mx = fmaxf(mx, xor_shfl(mx, 16));
@@ -269,19 +281,17 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             // tiles of a long context it rarely does).
             const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
             m = m_new;
+            // probabilities rounded to bf16: the P.V operand, and what the
+            // sum accumulates (so the normalisation matches the products)
             bf16x4 pb;
-            float psum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
-                pb[r] = b;
-                psum += (float)b;
-            }
-            l = fmaf(l, alpha, psum);
+            for (int r = 0; r < 4; ++r) pb[r] = (__bf16)fast_exp2(x[r] - ms);
             if (moved) {
 #pragma unroll
                 for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+                lacc *= alpha;
             }
+            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, lacc, 0, 0, 0);
 
             // O^T += V^T P^T. ds_read_b64_tr_b16: within each 16-lane group,
             // lane i receives element i % 4 of the 8-byte rows addressed by
@@ -357,9 +367,8 @@ void pa_decode_mfma_kernel(DecodeArgs a) {
             }
         }
 
-        // the four lane groups hold disjoint token subsets of the same state
-        l += xor_shfl(l, 16);
-        l += xor_shfl(l, 32);
+        // the sum over every token of column c, the same in all four lane groups
+        const float l = lacc[0];
 
         if constexpr (WPP) {
             // This wave's state is a whole partition's: store it directly.

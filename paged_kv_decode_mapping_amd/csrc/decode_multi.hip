@@ -280,7 +280,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     for (int off = 1; off < 16; off <<= 1) wave_pos = min(wave_pos, __shfl_xor(wave_pos, off, 64));
     wave_pos = __builtin_amdgcn_readfirstlane(wave_pos);
 
-    float m = -INFINITY, l = 0.0f;
+    float m = -INFINITY;
+    // running sum of row c's probabilities over every token so far, as an
+    // MFMA accumulator: each step adds ones . P^T, so every element of the
+    // tile holds the row's sum of the same rounded probabilities
+    f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 o[NPV];
 #pragma unroll
     for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -409,18 +413,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
             const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
             m = m_new;
             bf16x4 pb;
-            float psum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
-                pb[r] = b;
-                psum += (float)b;
-            }
-            l = fmaf(l, alpha, psum);
+            for (int r = 0; r < 4; ++r) pb[r] = (__bf16)fast_exp2(x[r] - ms);
             if (moved) {
 #pragma unroll
                 for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+                lacc *= alpha;
             }
+            const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, lacc, 0, 0, 0);
             // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c]
             const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RSV + 4 * (lane & 3);
 #pragma unroll
@@ -476,18 +477,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
             const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
             m = m_new;
             bf16x8 pb;
-            float psum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const __bf16 b = (__bf16)fast_exp2(x[r] - ms);
-                pb[r] = b;
-                psum += (float)b;
-            }
-            l = fmaf(l, alpha, psum);
+            for (int r = 0; r < 8; ++r) pb[r] = (__bf16)fast_exp2(x[r] - ms);
             if (moved) {
 #pragma unroll
                 for (int j = 0; j < NPV; ++j) o[j] *= alpha;
+                lacc *= alpha;
             }
+            // two 16-token halves against a 2-register ones operand (the
+            // 4- and 8-wave kernels sit at their 128-register budget)
+            const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_shufflevector(pb, pb, 0, 1, 2, 3), lacc, 0,
+                                                             0, 0);
+            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_shufflevector(pb, pb, 4, 5, 6, 7), lacc, 0,
+                                                             0, 0);
             // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c] of each tile
             const uint16_t* tr_a = vs + (4 * gq + (c >> 2)) * RSV + 4 * (lane & 3);
             const uint16_t* tr_b = tr_a + kTile * RSV;
@@ -534,9 +537,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         }
     }
 
-    // ---- store this lane's row (the four lane groups hold disjoint tokens)
-    l += xor_shfl(l, 16);
-    l += xor_shfl(l, 32);
+    // ---- store this lane's row (its sum over every token, in all four lane groups)
+    const float l = lacc[0];
     if (!my_valid) return;
     const int r = my_rho / g, hh = my_rho - (my_rho / g) * g;
     const int64_t row = (int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh;
