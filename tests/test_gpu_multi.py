@@ -11,7 +11,7 @@ import oracle
 import paged_kv_decode_mapping_amd as pa
 from paged_kv_decode_mapping_amd import workloads as W
 
-from _gpu_util import DeviceWorkload, compare, host_bits, note
+from _gpu_util import DeviceWorkload, bf16_to_f64, compare, host_bits, note
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +183,61 @@ def test_multi_rows_ordered_by_the_workgroups_or_the_list(lib, S):
                                        int(max(qlens)), partition_tokens=64))
     mref = oracle.multi_decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq.query_start, w.scale)
     compare(got, mref, *BF16_TOL)
+
+
+def _sampled_units(w, n, seed):
+    """n random (sequence, KV head) units plus every unit of the longest and
+    the shortest context."""
+    s = w.spec
+    rng = np.random.default_rng(seed)
+    extra = [int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))]
+    units = rng.choice(s.num_seqs * s.num_kv_heads, n, replace=False).tolist()
+    units += [i * s.num_kv_heads + k for i in extra for k in range(s.num_kv_heads)]
+    return np.unique(np.asarray(units, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name,qlen", [("llama70b_gqa", 16), ("mixed_batch", 32), ("llama70b_gqa", 4)])
+def test_full_size_multi_sampled(lib, name, qlen):
+    """pa_decode_multi at the full size and in the launch configuration the
+    benchmark times (the last qlen cached tokens of every sequence are its
+    queries; the library's own plan), checked on sampled (sequence, KV
+    head) units, the longest and the shortest context included, that the
+    oracle computes one by one."""
+    w = W.make_workload(name)
+    qlens = np.minimum(np.full(w.spec.num_seqs, qlen), w.context_lens)
+    mq = W.make_multi_query(w, qlens)
+    d = DeviceWorkload(w)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    qs = torch.from_numpy(mq.query_start).cuda()
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables)
+    note(f"full-size multi {name} qlen={qlen} decode plan={plan}")
+    got = bf16_to_f64(host_bits(pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, qs,
+                                                    w.scale, int(qlens.max()))))
+    torch.cuda.synchronize()
+    units = _sampled_units(w, 12, qlen)
+    ref = oracle.multi_decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq.query_start, w.scale,
+                              units=units)
+    mask = ~np.isnan(ref)
+    assert mask.sum() > 0
+    err = np.abs(got[mask] - ref[mask])
+    assert np.all(np.isfinite(got[mask]))
+    assert err.max() <= BF16_TOL[0] and err.mean() <= BF16_TOL[1], (err.max(), err.mean())
+
+
+def test_full_size_mqa_sampled(lib):
+    """The MQA batch (128 sequences of 4096 tokens, 64 query heads on one KV
+    head) through pa_decode's multi-row route, at full size with the
+    library's own plan, on sampled sequences the oracle computes one by
+    one."""
+    w = W.make_workload("mqa_70b")
+    d = DeviceWorkload(w)
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables)
+    note(f"full-size mqa plan={plan}")
+    out = host_bits(d.decode())
+    torch.cuda.synchronize()
+    units = _sampled_units(w, 10, 5)
+    ref = oracle.decode_workload(w, units=units)  # [n_units, g, D]
+    g = w.spec.num_q_heads // w.spec.num_kv_heads
+    got = np.stack([out[u // w.spec.num_kv_heads, (u % w.spec.num_kv_heads) * g:(u % w.spec.num_kv_heads + 1) * g]
+                    for u in units])
+    compare(got, ref, *BF16_TOL)
