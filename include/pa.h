@@ -118,20 +118,21 @@ typedef struct pa_decode_opts {
     int32_t schedule;         /* 1 = first build the work list on the device
                                  from context_lens: real (sequence, KV head,
                                  partition) items only, longest first, so
-                                 workgroups are dispatched in that order; 2 =
-                                 the same order without the builder pass:
-                                 each workgroup ranks its block index among
-                                 the items of context_lens itself (at most
-                                 4096 sequences; PA_ERR_UNSUPPORTED beyond;
-                                 for more than 16 query heads per KV head at
-                                 most 256, as 1 beyond); -1 = one workgroup
-                                 per (sequence, KV
-                                 head, partition) in index order, empty ones
-                                 included; 0 = when the plan splits
-                                 contexts, 2 for batches of at most 256
-                                 sequences whose grid holds at most 1024
-                                 (sequence, item) pairs, else 1; when it
-                                 does not split, -1 */
+                                 workgroups are dispatched in that order;
+                                 2 = the same order without the builder
+                                 pass: each workgroup ranks its block index
+                                 among the items of context_lens itself (at
+                                 most 4096 sequences, PA_ERR_UNSUPPORTED
+                                 beyond; with more than 16 query heads per
+                                 KV head at most 256, as 1 beyond);
+                                 -1 = one workgroup per (sequence, KV head,
+                                 partition) in index order, empty ones
+                                 included;
+                                 0 = chosen: when the plan splits contexts,
+                                 2 for batches of at most 256 sequences
+                                 whose grid holds at most 1024 (sequence,
+                                 item) pairs, else 1; when it does not
+                                 split, -1 */
     int32_t heads_per_tile;   /* MFMA kernel: 0 = chosen (2 for bf16 caches
                                  when g is 4..8, 2 for fp8 when g is 5..8,
                                  given an even num_kv_heads and adjacent KV
