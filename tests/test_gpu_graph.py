@@ -48,9 +48,13 @@ def _step_inputs(w, n_real, step):
     return ctx, tables, q, slots, nk, nv
 
 
-@pytest.mark.parametrize("partition", [-1, 64])
+@pytest.mark.parametrize("partition,schedule", [(-1, 0), (64, 2), (64, 1)])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_captured_step_replays_match_eager(lib, partition, kv):
+def test_captured_step_replays_match_eager(lib, partition, schedule, kv):
+    """Split plans are captured both with the items ranked by each
+    workgroup from the context lengths (schedule 2) and with the builder's
+    list (schedule 1): either way the order is found on the device at every
+    replay, from the lengths that replay's inputs hold."""
     w = W.make_workload("mixed_batch", num_seqs=12,
                         context=("list", [16, 100, 511, 512, 513, 900, 1000, 40, 2000, 77, 300, 1]))
     s = w.spec
@@ -75,7 +79,7 @@ def test_captured_step_replays_match_eager(lib, partition, kv):
     st_nk = torch.zeros((S, s.num_kv_heads, s.head_dim), dtype=torch.bfloat16, device=dev)
     st_nv = torch.zeros_like(st_nk)
     st_out = torch.zeros_like(st_q)
-    need = pa.pa_decode_workspace_size(st_q, kc_g, st_tab, partition_tokens=partition)
+    need = pa.pa_decode_workspace_size(st_q, kc_g, st_tab, partition_tokens=partition, schedule=schedule)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def load(step):
@@ -91,7 +95,7 @@ def test_captured_step_replays_match_eager(lib, partition, kv):
     def step_on(kc, vc, out):
         pa.pa_cache_write(st_nk, st_nv, st_slots, kc, vc, ks, vs)
         pa.pa_decode(st_q, kc, vc, st_tab, st_ctx, w.scale, out, workspace=ws, partition_tokens=partition,
-                     k_scale=ks, v_scale=vs)
+                     schedule=schedule, k_scale=ks, v_scale=vs)
 
     # warm up on a side stream (as torch asks before capture), on scratch caches
     load(0)
@@ -104,7 +108,10 @@ def test_captured_step_replays_match_eager(lib, partition, kv):
     torch.cuda.synchronize()
     del kc_w, vc_w
 
-    note(f"graph capture partition={partition}")
+    plan = pa.pa_decode_get_plan(st_q, kc_g, st_tab, partition_tokens=partition, schedule=schedule)
+    if partition > 0:
+        assert plan["scheduled"] and plan["self_scheduled"] == (schedule == 2)
+    note(f"graph capture partition={partition} schedule={schedule}")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step_on(kc_g, vc_g, st_out)
