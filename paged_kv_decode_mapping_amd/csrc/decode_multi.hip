@@ -17,12 +17,14 @@
 // included. Gather through the block table as in Tutorial §4.2 (get_kv).
 //
 // Rows. The (query token r, head hh) pairs of one (sequence, KV head) are
-// rows rho = r * g + hh; every wave of a workgroup owns one 16-row tile of
-// them (W = 1, 2, 4 or 8 waves: 16 W rows), so the online-softmax state of
-// a row never leaves its lanes and a workgroup needs no combine step. Rows are the
-// columns of the same MFMA tiles the decode kernel uses:
+// rows rho = r * g + hh; every wave of a workgroup owns RT 16-row tiles of
+// them (W = 1, 2, 4 or 8 waves, RT = 1 or 2: 16 W RT rows), so the
+// online-softmax state of a row never leaves its lanes and a workgroup needs
+// no combine step. Rows are the columns of the same MFMA tiles the decode
+// kernel uses:
 //   S = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q^T rows
-//               of this wave (in registers with 4 or 8 waves, else LDS);
+//               of this wave (in registers with 4 or 8 waves or two row
+//               tiles, else LDS);
 //   O^T += V^T P^T  A = V^T by the transposing LDS read, B = the lane's own
 //               probabilities (bf16): v_mfma_f32_16x16x16_bf16 per tile, or
 //               v_mfma_f32_16x16x32_bf16 per pair of tiles (below).
@@ -43,8 +45,9 @@
 // fp8 KV).
 //
 // Split-K. A workgroup covers one partition of at most P tokens; with more
-// than one partition it stores unnormalised partial states (m, l, o) per row
-// and pa_multi_merge_kernel combines them by log-sum-exp.
+// than one partition it stores unnormalised partial states (m, l, o) of the
+// rows that see tokens past partition 0, and pa_multi_merge_kernel combines
+// them by log-sum-exp; rows that see partition 0 only are finished here.
 //
 // Cascade prefix pass. Sequences that share a cached prefix (Tutorial §4.3,
 // prefix caching: the same physical blocks in every sharer's table) attend
@@ -105,8 +108,32 @@ struct MultiItem {
     int q0, n;    // first query row and number of query tokens
 };
 
-template <int D, bool FP8, int W, int NB>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ? 4 : 1))) void pa_multi_kernel(MultiArgs a) {
+// Sum over the four lanes of one MFMA column, returned to all four.
+__device__ __forceinline__ float column_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Register budget of the multi-row kernel, as waves per SIMD: four (128
+// registers) for 4 or 8 waves of one row tile; three (168) for two row tiles,
+// whose accumulators and query fragments double, except fp8 at D = 128,
+// whose staging conversion spills there (two, 256); unconstrained below 4
+// waves.
+constexpr int multi_waves_per_eu(int D, bool fp8, int W, int RT) {
+    return RT == 2 ? ((fp8 && D == 128) ? 2 : 3) : (W >= 4 ? 4 : 1);
+}
+
+// RT: 16-row tiles per wave. Every wave reads each staged K fragment and
+// each transposed V fragment from LDS once per tile and feeds it to RT
+// MFMAs, one per row tile: with 128 rows per KV head, 4 waves of 32 rows
+// read half the LDS bytes 8 waves of 16 rows do (the LDS, not HBM, bounds
+// the 16-row form there: all waves read the whole tile). The row sums then
+// stay per lane on the VALU (the matrix pipe is the busier one), reduced
+// over the column's four lanes at the end.
+template <int D, bool FP8, int W, int NB, int RT>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(multi_waves_per_eu(D, FP8, W, RT)))) void pa_multi_kernel(MultiArgs a) {
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int NQK = D / 32;
     constexpr int NPV = D / 16;
@@ -136,16 +163,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     // 16 lanes are conflict-free there and would collide at 288.
     constexpr int RSV = D + 16;
     static_assert(NB % 2 == 0, "the LDS buffer of a ring slot is its parity");
+    static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
+    constexpr int WROWS = 16 * RT;           // rows per wave
+    constexpr int GROWS = WROWS * W;         // rows per workgroup
 
-    // With 4 or 8 waves (many rows: LDS traffic counts), this wave's query
-    // fragments, the B operand of every q.K^T MFMA, stay in registers instead
-    // of being read from LDS for every tile, and the query rows' LDS is then
-    // reused for the K/V buffers; with 1 or 2 waves (few rows, memory-bound)
-    // the 16 registers would cost occupancy.
-    constexpr bool kQInRegs = W >= 4;
+    // With 4 or 8 waves, or two row tiles a wave (many rows: LDS traffic
+    // counts), this wave's query fragments, the B operands of every q.K^T
+    // MFMA, stay in registers instead of being read from LDS for every tile,
+    // and the query rows' LDS is then reused for the K/V buffers; with 1 or 2
+    // waves of one tile (few rows, memory-bound) the 16 registers would cost
+    // occupancy.
+    constexpr bool kQInRegs = W >= 4 || RT == 2;
     extern __shared__ float smem[];
-    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);   // [16 W][RS] query rows
-    uint16_t* kbuf = kQInRegs ? qs : qs + 16 * W * RS;   // [2][SROWS][RS]
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);   // [GROWS][RS] query rows
+    uint16_t* kbuf = kQInRegs ? qs : qs + GROWS * RS;    // [2][SROWS][RS]
     uint16_t* vbuf = kbuf + 2 * SROWS * RS;              // [2][SROWS][RSV]
 
     // ---- the work item
@@ -202,10 +233,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     }
     const int g = a.group;
     const int rows = it.n * g;
-    const int row0 = it.rb * 16 * W;
+    const int row0 = it.rb * GROWS;
     if (row0 >= rows) return;
     // the last position any row of this block attends to
-    const int last_row = min(rows, row0 + 16 * W) - 1;
+    const int last_row = min(rows, row0 + GROWS) - 1;
     const int pos_max = prefix_pass ? it.L - 1 : it.L - it.n + last_row / g;
     const int t_begin = it.part * a.partition_tokens;
     const int t_end = min(min(t_begin + a.partition_tokens, pos_max + 1), it.L);
@@ -240,7 +271,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
 
     // ---- query rows of this block -> LDS (zero rows past the block's rows):
     // every load first, then the stores
-    constexpr int QPT = (16 * W * (D / 8)) / (64 * W);  // 16-byte chunks per thread
+    constexpr int QPT = (GROWS * (D / 8)) / (64 * W);  // 16-byte chunks per thread
     u32x4 qv[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
@@ -256,15 +287,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         }
     }
 
-    // this lane's row (column c of the wave's tile) and its causal limit
-    const int my_rho = row0 + wave * 16 + c;
-    const bool my_valid = my_rho < rows;
-    int my_pos = my_valid ? it.L - it.n + my_rho / g : -1;  // sees tokens <= my_pos
-    if (prefix_pass && my_valid) {
-        // a member attends min(its context, the prefix) tokens here
-        int ctx = a.context_lens[it.q0 + my_rho / g];
-        ctx = ctx < 0 ? 0 : (ctx > a.cascade.max_context ? a.cascade.max_context : ctx);
-        my_pos = min(ctx, it.L) - 1;
+    // this lane's rows (column c of each of the wave's tiles) and their
+    // causal limits
+    int my_rho[RT], my_pos[RT];
+    bool my_valid[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+        my_rho[u] = row0 + (wave * RT + u) * 16 + c;
+        my_valid[u] = my_rho[u] < rows;
+        my_pos[u] = my_valid[u] ? it.L - it.n + my_rho[u] / g : -1;  // sees tokens <= my_pos
+        if (prefix_pass && my_valid[u]) {
+            // a member attends min(its context, the prefix) tokens here
+            int ctx = a.context_lens[it.q0 + my_rho[u] / g];
+            ctx = ctx < 0 ? 0 : (ctx > a.cascade.max_context ? a.cascade.max_context : ctx);
+            my_pos[u] = min(ctx, it.L) - 1;
+        }
     }
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
@@ -272,22 +309,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         const int rr = i / (D / 8);
         *reinterpret_cast<u32x4*>(qs + rr * RS + 8 * (i - rr * (D / 8))) = qv[k];
     }
-    const uint16_t* q_row = qs + (wave * 16 + c) * RS + 8 * gq;
+    const uint16_t* q_row = qs + (wave * WROWS + c) * RS + 8 * gq;  // row tile u at + 16 u RS
     // The last token every valid row of this wave sees (wave-uniform): tiles
     // that end at or before it, and before t_end, need no mask.
-    int wave_pos = my_valid ? my_pos : 0x7fffffff;
+    int wave_pos = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < RT; ++u) wave_pos = min(wave_pos, my_valid[u] ? my_pos[u] : 0x7fffffff);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) wave_pos = min(wave_pos, __shfl_xor(wave_pos, off, 64));
     wave_pos = __builtin_amdgcn_readfirstlane(wave_pos);
 
-    float m = -INFINITY;
-    // running sum of row c's probabilities over every token so far, as an
-    // MFMA accumulator: each step adds ones . P^T, so every element of the
-    // tile holds the row's sum of the same rounded probabilities
+    float m[RT];
+    // One row tile: the running sum of row c's probabilities over every
+    // token so far, as an MFMA accumulator: each step adds ones . P^T, so
+    // every element of the tile holds the row's sum of the same rounded
+    // probabilities. Two: lsum, this lane's share of it (unrounded).
     f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 o[NPV];
+    float lsum[RT];
+    f32x4 o[RT][NPV];
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < RT; ++u) {
+        m[u] = -INFINITY;
+        lsum[u] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) o[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int64_t head_off = (int64_t)it.kvh * a.cache.head;  // folded into each tile's descriptor base
     const int bs_mask = (1 << a.block_size_log2) - 1;
@@ -329,12 +375,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
     u32x4 kb[NB][NI], vb[NB][NI];
 
     __syncthreads();  // query rows in LDS
-    bf16x8 qf[NQK];
+    bf16x8 qf[RT][NQK];
     if constexpr (kQInRegs) {
 #pragma unroll
-        for (int j = 0; j < NQK; ++j) qf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
+        for (int u = 0; u < RT; ++u)
+#pragma unroll
+            for (int j = 0; j < NQK; ++j)
+                qf[u][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 16 * u * RS + 32 * j));
         __syncthreads();  // every wave has its fragments: the K/V staging may overwrite the rows
     }
+    // B operand of row tile u, fragment j
+    auto qfrag = [&](int u, int j) -> bf16x8 {
+        if constexpr (kQInRegs) return qf[u][j];
+        else return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 16 * u * RS + 32 * j));
+    };
 
     if (ntiles > 0) {
         // physical block of tile t (tiles past the last take the last one's),
@@ -384,44 +438,69 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
             }
         };
 
+        // Online-softmax update of row tile u from its NX scores x (already
+        // scaled and masked): new running max, rescale of the tile's output
+        // and row sum when the max moved, probabilities returned in p.
+        auto softmax_step = [&](int u, const float* x, float* p, auto nx_tag) {
+            constexpr int NX = decltype(nx_tag)::value;
+            float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+            for (int r = 2; r < NX; ++r) mx = fmaxf(mx, x[r]);
+            mx = column_max4(mx);
+            const float m_new = fmaxf(m[u], mx);
+            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m[u] - ms);
+            const bool moved = __builtin_amdgcn_ballot_w64(m_new != m[u]) != 0;
+            m[u] = m_new;
+            float ps = 0.0f;
+#pragma unroll
+            for (int r = 0; r < NX; ++r) {
+                p[r] = fast_exp2(x[r] - ms);
+                ps += p[r];
+            }
+            if (moved) {
+#pragma unroll
+                for (int j = 0; j < NPV; ++j) o[u][j] *= alpha;
+                if constexpr (RT == 1) lacc *= alpha;
+            }
+            if constexpr (RT != 1) lsum[u] = lsum[u] * alpha + ps;
+        };
+
         // one tile of a staged slot: scores, online softmax, P.V
         auto compute = [&](int t, const uint16_t* ks, const uint16_t* vs) {
             const int t0 = t_begin + t * kTile;
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 s[RT];
+#pragma unroll
+            for (int u = 0; u < RT; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
                 const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
-                const bf16x8 qb = kQInRegs ? qf[j]
-                                           : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, s, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < RT; ++u) s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qfrag(u, j), s[u], 0, 0, 0);
             }
-            float x[4];
-            if (t0 + kTile - 1 <= wave_pos && t0 + kTile <= t_end) {  // uniform: every row sees the whole tile
+            const bool whole = t0 + kTile - 1 <= wave_pos && t0 + kTile <= t_end;  // uniform: every row sees the whole tile
+            bf16x4 pb[RT];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = s[r] * qk;
-            } else {
+            for (int u = 0; u < RT; ++u) {
+                float x[4], p[4];
+                if (whole) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = t0 + 4 * gq + r;
-                    x[r] = (tok > my_pos || tok >= t_end) ? -INFINITY : s[r] * qk;
+                    for (int r = 0; r < 4; ++r) x[r] = s[u][r] * qk;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = t0 + 4 * gq + r;
+                        x[r] = (tok > my_pos[u] || tok >= t_end) ? -INFINITY : s[u][r] * qk;
+                    }
                 }
-            }
-            const float mx = column_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-            const float m_new = fmaxf(m, mx);
-            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m - ms);
-            const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
-            m = m_new;
-            bf16x4 pb;
+                softmax_step(u, x, p, std::integral_constant<int, 4>{});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pb[r] = (__bf16)fast_exp2(x[r] - ms);
-            if (moved) {
-#pragma unroll
-                for (int j = 0; j < NPV; ++j) o[j] *= alpha;
-                lacc *= alpha;
+                for (int r = 0; r < 4; ++r) pb[u][r] = (__bf16)p[r];
             }
-            const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, lacc, 0, 0, 0);
+            if constexpr (RT == 1) {
+                const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+                lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb[0], lacc, 0, 0, 0);
+            }
             // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c]
             const uint16_t* tr_base = vs + (4 * gq + (c >> 2)) * RSV + 4 * (lane & 3);
 #pragma unroll
@@ -430,7 +509,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
                 typedef __attribute__((address_space(3))) uint16_t lds_u16;
                 lds_s16x4* src = (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_base) + 16 * j);
                 const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(src));
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[j], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < RT; ++u) o[u][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[u], o[u][j], 0, 0, 0);
             }
         };
 
@@ -444,53 +524,55 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         // reads side by side.
         auto compute_pair = [&](int t, const uint16_t* ks, const uint16_t* vs) {
             const int t0 = t_begin + t * kTile;
-            f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 sa[RT], sb[RT];
+#pragma unroll
+            for (int u = 0; u < RT; ++u) {
+                sa[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int j = 0; j < NQK; ++j) {
-                const bf16x8 qb = kQInRegs ? qf[j]
-                                           : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_row + 32 * j));
                 const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + c * RS + 32 * j + 8 * gq));
                 const bf16x8 kb2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + (kTile + c) * RS + 32 * j + 8 * gq));
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, sa, 0, 0, 0);
-                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb2, qb, sb, 0, 0, 0);
-            }
-            float x[8];
-            if (t0 + 2 * kTile - 1 <= wave_pos && t0 + 2 * kTile <= t_end) {  // uniform: nothing to mask
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    x[r] = sa[r] * qk;
-                    x[4 + r] = sb[r] * qk;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ta = t0 + 4 * gq + r, tb = ta + kTile;
-                    x[r] = (ta > my_pos || ta >= t_end) ? -INFINITY : sa[r] * qk;
-                    x[4 + r] = (tb > my_pos || tb >= t_end) ? -INFINITY : sb[r] * qk;
+                for (int u = 0; u < RT; ++u) {
+                    const bf16x8 qb = qfrag(u, j);
+                    sa[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, sa[u], 0, 0, 0);
+                    sb[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb2, qb, sb[u], 0, 0, 0);
                 }
             }
-            const float mx = column_max4(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-            const float m_new = fmaxf(m, mx);
-            const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m - ms);
-            const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
-            m = m_new;
-            bf16x8 pb;
+            const bool whole = t0 + 2 * kTile - 1 <= wave_pos && t0 + 2 * kTile <= t_end;  // uniform: nothing to mask
+            bf16x8 pb[RT];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) pb[r] = (__bf16)fast_exp2(x[r] - ms);
-            if (moved) {
+            for (int u = 0; u < RT; ++u) {
+                float x[8], p[8];
+                if (whole) {
 #pragma unroll
-                for (int j = 0; j < NPV; ++j) o[j] *= alpha;
-                lacc *= alpha;
+                    for (int r = 0; r < 4; ++r) {
+                        x[r] = sa[u][r] * qk;
+                        x[4 + r] = sb[u][r] * qk;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ta = t0 + 4 * gq + r, tb = ta + kTile;
+                        x[r] = (ta > my_pos[u] || ta >= t_end) ? -INFINITY : sa[u][r] * qk;
+                        x[4 + r] = (tb > my_pos[u] || tb >= t_end) ? -INFINITY : sb[u][r] * qk;
+                    }
+                }
+                softmax_step(u, x, p, std::integral_constant<int, 8>{});
+#pragma unroll
+                for (int r = 0; r < 8; ++r) pb[u][r] = (__bf16)p[r];
             }
-            // two 16-token halves against a 2-register ones operand (the
-            // 4- and 8-wave kernels sit at their 128-register budget)
-            const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_shufflevector(pb, pb, 0, 1, 2, 3), lacc, 0,
-                                                             0, 0);
-            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_shufflevector(pb, pb, 4, 5, 6, 7), lacc, 0,
-                                                             0, 0);
+            if constexpr (RT == 1) {
+                // two 16-token halves against a 2-register ones operand (the
+                // 4- and 8-wave kernels sit at their 128-register budget)
+                const bf16x4 ones = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+                lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_shufflevector(pb[0], pb[0], 0, 1, 2, 3),
+                                                                 lacc, 0, 0, 0);
+                lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_shufflevector(pb[0], pb[0], 4, 5, 6, 7),
+                                                                 lacc, 0, 0, 0);
+            }
             // V^T by ds_read_b64_tr_b16: lane (gq, c) receives V[4 gq + k][16 j + c] of each tile
             const uint16_t* tr_a = vs + (4 * gq + (c >> 2)) * RSV + 4 * (lane & 3);
             const uint16_t* tr_b = tr_a + kTile * RSV;
@@ -503,7 +585,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
                 const bf16x4 vb2 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4*)((lds_u16*)const_cast<uint16_t*>(tr_b) + 16 * j)));
                 const bf16x8 v8 = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pb, o[j], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < RT; ++u) o[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pb[u], o[u][j], 0, 0, 0);
             }
         };
 
@@ -537,28 +620,41 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W >= 4 ?
         }
     }
 
-    // ---- store this lane's row (its sum over every token, in all four lane groups)
-    const float l = lacc[0];
-    if (!my_valid) return;
-    const int r = my_rho / g, hh = my_rho - (my_rho / g) * g;
-    const int64_t row = (int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh;
-    if (a.num_partitions == 1 && !prefix_pass) {
-        uint16_t* dst = a.out + (int64_t)(it.q0 + r) * a.out_row + (int64_t)(it.kvh * g + hh) * a.out_head;
-        const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
+    // ---- store this lane's rows (each row's sum over every token, in all
+    // four lanes of its column)
 #pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[j][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[j][1] * inv) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[j][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[j][3] * inv) << 16);
-            *reinterpret_cast<u32x2*>(dst + 16 * j + 4 * gq) = u32x2{lo, hi};
-        }
-    } else {
-        const int64_t prow = row * a.num_partitions + it.part;
+    for (int u = 0; u < RT; ++u) {
+        const float l = RT == 1 ? lacc[0] : column_sum4(lsum[u]);
+        if (!my_valid[u]) continue;
+        // A split plan still finishes here every row whose positions all lie
+        // in partition 0 (the merge skips rows of one partition: the same
+        // test on the same clamped lengths), and stores no state for a
+        // partition that holds none of a row's tokens (the merge reads
+        // states 0 .. (position / P) only).
+        if (!prefix_pass && it.part > 0 && my_pos[u] < t_begin) continue;
+        const bool direct = !prefix_pass && (a.num_partitions == 1 || my_pos[u] < a.partition_tokens);
+        const int r = my_rho[u] / g, hh = my_rho[u] - (my_rho[u] / g) * g;
+        const int64_t row = (int64_t)(it.q0 + r) * a.num_q_heads + it.kvh * g + hh;
+        if (direct) {
+            uint16_t* dst = a.out + (int64_t)(it.q0 + r) * a.out_row + (int64_t)(it.kvh * g + hh) * a.out_head;
+            const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
 #pragma unroll
-        for (int j = 0; j < NPV; ++j)
-            *reinterpret_cast<f32x4*>(a.part_o + prow * D + 16 * j + 4 * gq) = o[j] * a.v_scale;
-        if (gq == 0) {
-            a.part_ml[prow * 2] = m;
-            a.part_ml[prow * 2 + 1] = l;
+            for (int j = 0; j < NPV; ++j) {
+                const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[u][j][0] * inv) |
+                                    ((uint32_t)f32_to_bf16_rne(o[u][j][1] * inv) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[u][j][2] * inv) |
+                                    ((uint32_t)f32_to_bf16_rne(o[u][j][3] * inv) << 16);
+                *reinterpret_cast<u32x2*>(dst + 16 * j + 4 * gq) = u32x2{lo, hi};
+            }
+        } else {
+            const int64_t prow = row * a.num_partitions + it.part;
+#pragma unroll
+            for (int j = 0; j < NPV; ++j)
+                *reinterpret_cast<f32x4*>(a.part_o + prow * D + 16 * j + 4 * gq) = o[u][j] * a.v_scale;
+            if (gq == 0) {
+                a.part_ml[prow * 2] = m[u];
+                a.part_ml[prow * 2 + 1] = l;
+            }
         }
     }
 }
@@ -610,6 +706,7 @@ __global__ __launch_bounds__(64 * W) void pa_multi_merge_kernel(MultiArgs a) {
     const int r = qrow - q0;
     if (r < 0 || r >= n) return;  // not a row of this sequence's queries (malformed query_start)
     const int np = multi_row_partitions(a, seq, n, r);
+    if (np <= 1) return;  // finished by pa_multi_kernel
     const int head = (int)(wid - (int64_t)qrow * a.num_q_heads);
     merge_row<D, W>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np,
                     nullptr, nullptr, 0, a.out + (int64_t)qrow * a.out_row + (int64_t)head * a.out_head, red);
@@ -629,9 +726,44 @@ __global__ __launch_bounds__(256) void pa_multi_merge_flat_kernel(MultiArgs a) {
     const int r = qrow - q0;
     if (r < 0 || r >= n) return;
     const int np = multi_row_partitions(a, seq, n, r);
+    if (np <= 1) return;  // finished by pa_multi_kernel
     const int head = (int)(wid - (int64_t)qrow * a.num_q_heads);
     merge_column<D, NP>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np, c,
                         a.out + (int64_t)qrow * a.out_row + (int64_t)head * a.out_head);
+}
+
+// Few partitions, with query offsets: the grid walks (sequence, query head,
+// block of R = 256 / (D / 4) query rows), one thread per float4 column of a
+// row, so the sequence comes from the block index (no search of the
+// offsets) and a sequence whose context lies in partition 0, every row of
+// it finished by pa_multi_kernel, costs one load.
+template <int D, int NP>
+__global__ __launch_bounds__(256) void pa_multi_merge_flat_seq_kernel(MultiArgs a, int row_chunks) {
+    constexpr int C = D / 4;
+    constexpr int R = 256 / C;
+    int b = (int)blockIdx.x;
+    const int rc = b % row_chunks;
+    b /= row_chunks;
+    const int head = b % a.num_q_heads;
+    const int seq = b / a.num_q_heads;
+    const int cap = a.max_blocks_per_seq << a.block_size_log2;
+    int L = a.context_lens[seq];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    if (L <= a.partition_tokens) return;
+    // the query rows of the sequence, clamped as multi_row_owner clamps them
+    const int q0 = a.query_start[seq];
+    int n = a.query_start[seq + 1] - q0;
+    n = n > a.max_query_len ? a.max_query_len : n;
+    if (q0 < 0 || q0 > a.num_query_rows) n = 0;
+    else if (n > a.num_query_rows - q0) n = a.num_query_rows - q0;
+    const int r = rc * R + (int)threadIdx.x / C;
+    if (r >= n) return;
+    const int pos = L - n + r;
+    const int np = pos < 0 ? 1 : (pos + a.partition_tokens) / a.partition_tokens;
+    if (np <= 1) return;  // finished by pa_multi_kernel
+    const int64_t wid = (int64_t)(q0 + r) * a.num_q_heads + head;
+    merge_column<D, NP>(a.part_ml + wid * a.num_partitions * 2, a.part_o + wid * a.num_partitions * D, np,
+                        (int)threadIdx.x % C, a.out + (int64_t)(q0 + r) * a.out_row + (int64_t)head * a.out_head);
 }
 
 template <int D, int W>
@@ -643,8 +775,19 @@ template <int D>
 void launch_multi_merge(const MultiArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.num_query_rows * a.num_q_heads;
     if (a.num_partitions <= kFlatMergeMaxStates) {
-        const dim3 grid((unsigned)((rows * (D / 4) + 255) / 256));
+        const int64_t row_blocks = (rows * (D / 4) + 255) / 256;
         const int np = flat_merge_states(a.num_partitions);
+        constexpr int R = 256 / (D / 4);
+        const int chunks = (a.max_query_len + R - 1) / R;
+        const int64_t seq_blocks = (int64_t)a.num_seqs * a.num_q_heads * chunks;
+        if (a.query_start != nullptr && chunks > 0 && seq_blocks <= 2 * row_blocks) {
+            const dim3 grid((unsigned)seq_blocks);
+            if (np == 2) hipLaunchKernelGGL((pa_multi_merge_flat_seq_kernel<D, 2>), grid, dim3(256), 0, s, a, chunks);
+            else if (np == 4) hipLaunchKernelGGL((pa_multi_merge_flat_seq_kernel<D, 4>), grid, dim3(256), 0, s, a, chunks);
+            else hipLaunchKernelGGL((pa_multi_merge_flat_seq_kernel<D, 8>), grid, dim3(256), 0, s, a, chunks);
+            return;
+        }
+        const dim3 grid((unsigned)row_blocks);
         if (np == 2) hipLaunchKernelGGL((pa_multi_merge_flat_kernel<D, 2>), grid, dim3(256), 0, s, a);
         else if (np == 4) hipLaunchKernelGGL((pa_multi_merge_flat_kernel<D, 4>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((pa_multi_merge_flat_kernel<D, 8>), grid, dim3(256), 0, s, a);
@@ -657,37 +800,43 @@ void launch_multi_merge(const MultiArgs& a, hipStream_t s) {
     else launch_merge_w<D, 8>(a, rows, s);
 }
 
-template <int D, bool FP8, int W>
+template <int D, bool FP8, int W, int RT>
 hipError_t launch_w(const MultiArgs& a, hipStream_t s) {
     // as in the kernel: tiles per ring slot (two unless 1 or 2 waves fall
-    // short of a tile's chunks; a 2-slot ring when each lane loads one chunk
-    // of each), query rows' LDS reused by the K/V buffers at 4 or 8 waves
+    // short of a tile's chunks; with one row tile a wave, a 2-slot ring when
+    // each lane loads one chunk of each: the 128-register budget; two row
+    // tiles have 256 registers and keep 4 slots), query rows' LDS reused by
+    // the K/V buffers at 4 or 8 waves or two row tiles
     constexpr int CHUNKS = kTile * (D / (FP8 ? 16 : 8));
     constexpr int MODE = 64 * W >= 2 * CHUNKS ? 0 : ((W >= 4 && 64 * W == CHUNKS) ? 1 : 2);
     constexpr int TPS = MODE == 2 ? 1 : 2;
-    constexpr int NB = (W == 1 || MODE == 1) ? 2 : 4;
-    const size_t q_elems = (size_t)16 * W * (D + 8);
+    constexpr int NB = (W == 1 || MODE == 1 || RT == 2) ? 2 : 4;
+    const size_t q_elems = (size_t)16 * W * RT * (D + 8);
     const size_t kv_elems = (size_t)2 * TPS * kTile * (D + 8) + (size_t)2 * TPS * kTile * (D + 16);
-    const size_t lds = (W >= 4 ? (q_elems > kv_elems ? q_elems : kv_elems) : q_elems + kv_elems) * sizeof(uint16_t);
+    const bool reuse = W >= 4 || RT == 2;
+    const size_t lds = (reuse ? (q_elems > kv_elems ? q_elems : kv_elems) : q_elems + kv_elems) * sizeof(uint16_t);
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.row_blocks * a.num_partitions));
-    hipLaunchKernelGGL((pa_multi_kernel<D, FP8, W, NB>), grid, dim3(64 * W), lds, s, a);
+    hipLaunchKernelGGL((pa_multi_kernel<D, FP8, W, NB, RT>), grid, dim3(64 * W), lds, s, a);
     return hipGetLastError();
 }
 
 template <int D, bool FP8>
-hipError_t launch_df(const MultiArgs& a, int waves, hipStream_t s) {
-    if (waves <= 1) return launch_w<D, FP8, 1>(a, s);
-    if (waves == 2) return launch_w<D, FP8, 2>(a, s);
-    if (waves == 4) return launch_w<D, FP8, 4>(a, s);
-    return launch_w<D, FP8, 8>(a, s);
+hipError_t launch_df(const MultiArgs& a, int waves, int row_tiles, hipStream_t s) {
+    if (row_tiles == 2) return launch_w<D, FP8, 4, 2>(a, s);
+    if (waves <= 1) return launch_w<D, FP8, 1, 1>(a, s);
+    if (waves == 2) return launch_w<D, FP8, 2, 1>(a, s);
+    if (waves == 4) return launch_w<D, FP8, 4, 1>(a, s);
+    return launch_w<D, FP8, 8, 1>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, hipStream_t s) {
+hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, int row_tiles, hipStream_t s) {
     hipError_t e;
-    if (head_dim == 64) e = fp8 ? launch_df<64, true>(a, waves, s) : launch_df<64, false>(a, waves, s);
-    else e = fp8 ? launch_df<128, true>(a, waves, s) : launch_df<128, false>(a, waves, s);
+    if (head_dim == 64)
+        e = fp8 ? launch_df<64, true>(a, waves, row_tiles, s) : launch_df<64, false>(a, waves, row_tiles, s);
+    else
+        e = fp8 ? launch_df<128, true>(a, waves, row_tiles, s) : launch_df<128, false>(a, waves, row_tiles, s);
     if (e != hipSuccess || a.num_partitions == 1 || a.cascade.group_start != nullptr) return e;
     if (head_dim == 64) launch_multi_merge<64>(a, s);
     else launch_multi_merge<128>(a, s);

@@ -50,7 +50,8 @@ struct Plan {
     int heads_per_unit = 1;      // MFMA kernel: adjacent KV heads sharing a 16-row tile
     bool wave_partitions = false; // MFMA kernel: each wave takes one whole partition
     int num_items = 1;           // work items per (sequence, unit): partitions, or groups of W
-    int row_blocks = 1;          // multi: blocks of 16 * waves rows per (sequence, KV head)
+    int row_tiles = 1;           // multi: 16-row matrix tiles per wave (1 or 2)
+    int row_blocks = 1;          // multi: blocks of 16 * waves * row_tiles rows per (sequence, KV head)
     int64_t num_workgroups = 0;  // direct grid size, or the item bound when scheduled
     // workspace layout (byte offsets); total = workspace
     bool partials = false;       // split-K partial states in the workspace
@@ -104,8 +105,10 @@ int choose_partition(int64_t units, int64_t cap, int32_t partition_tokens, int g
 
 // Plan of the multi-row kernel: Tq query rows in all, at most maxq per
 // sequence, g = Hq / Hkv heads per KV head, so at most maxq * g rows per
-// (sequence, KV head); one wave per 16 of them, up to 8 waves a workgroup
-// (more rows take more workgroups, each reading the K/V again).
+// (sequence, KV head); one wave per 16 of them up to 64 rows, one per 32
+// beyond (every wave reads the whole staged tile from LDS, so fewer, wider
+// waves read less of it), up to 8 waves a workgroup (more rows take more
+// workgroups, each reading the K/V again).
 int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
                     int32_t MB, int32_t partition_tokens, Plan* plan, int32_t schedule = 0) {
     if (Tq < 0 || maxq < 0) return PA_ERR_SHAPE;
@@ -115,9 +118,11 @@ int make_multi_plan(int32_t S, int32_t Tq, int32_t maxq, int32_t Hq, int32_t Hkv
     p.scheduled = false;
     const int g = Hq / Hkv;
     const int64_t rows = (int64_t)(maxq > 0 ? maxq : 1) * g;
-    p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : (rows <= 64 ? 4 : 8));
+    p.row_tiles = rows > 64 ? 2 : 1;
+    p.waves = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
     p.depth = p.waves == 1 ? 2 : 4;  // register ring of the cooperative tile loads
-    const int64_t rb = (rows + 16 * p.waves - 1) / (16 * p.waves);
+    const int64_t block_rows = (int64_t)16 * p.waves * p.row_tiles;
+    const int64_t rb = (rows + block_rows - 1) / block_rows;
     if (rb >= (int64_t(1) << 20)) return PA_ERR_UNSUPPORTED;
     p.row_blocks = (int)rb;
     const int64_t cap = (int64_t)MB * bs;
@@ -533,7 +538,7 @@ int run_multi(const Plan& p, const Geom& g, const int32_t* query_start, int32_t 
         a.items = sa.items;
         a.item_count = sa.item_count;
     }
-    const hipError_t e = pa::launch_multi(a, g.D, kv_dtype == PA_DTYPE_FP8_E4M3FN, p.waves, s);
+    const hipError_t e = pa::launch_multi(a, g.D, kv_dtype == PA_DTYPE_FP8_E4M3FN, p.waves, p.row_tiles, s);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -864,7 +869,7 @@ int pa_decode_cascade(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         m = multi_args(c.prefix, g, gr.prefix, gr.G, nullptr, g.S, max_group_size, scale, kvd, k_scale, v_scale,
                        workspace);
         m.cascade = groups;
-        if (pa::launch_multi(m, g.D, fp8, c.prefix.waves, s) != hipSuccess) return PA_ERR_LAUNCH;
+        if (pa::launch_multi(m, g.D, fp8, c.prefix.waves, c.prefix.row_tiles, s) != hipSuccess) return PA_ERR_LAUNCH;
     }
     // 3. suffix pass
     const pa::LaunchShape ls{p.waves, p.depth, p.heads_per_unit, false};

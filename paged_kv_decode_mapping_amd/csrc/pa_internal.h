@@ -140,7 +140,7 @@ struct MultiArgs {
     int32_t num_q_heads, num_kv_heads, group;
     int32_t block_size_log2, max_blocks_per_seq;
     int32_t partition_tokens, num_partitions;
-    int32_t row_blocks;            // blocks of 16 * waves rows per (sequence, KV head)
+    int32_t row_blocks;            // blocks of 16 * waves * row tiles rows per (sequence, KV head)
     int32_t last_block;
     CacheLayout cache;
     float qk_scale_log2, v_scale;
@@ -217,7 +217,7 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_probe_read(const void* buf, int64_t bytes, bool nontemporal, uint32_t* sink, int cus,
                              hipStream_t s);
 // the multi-row kernel, then (split, not a cascade prefix pass) its merge
-hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, hipStream_t s);
+hipError_t launch_multi(const MultiArgs& a, int head_dim, bool fp8, int waves, int row_tiles, hipStream_t s);
 
 // PA_DEBUG_VALIDATE set (and not "0"): the hot-path calls first run the
 // precondition checks of validate.hip.

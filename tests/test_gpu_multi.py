@@ -33,7 +33,7 @@ CASES = {
     "chunk_prefill": ("mixed_batch", dict(num_seqs=3, context=("list", [600, 1500, 100])), [100, 37, 100]),
     "long_bs128": ("long_splitk", dict(num_seqs=2, context=("list", [5000, 2049])), [16, 3]),
     "mha_multi": ("llama7b_mha", dict(num_seqs=3, context=("list", [512, 1000, 33])), [6, 2, 33]),
-    # 128 rows per KV head: one 8-wave workgroup
+    # 128 rows per KV head: one workgroup of 4 waves x 32 rows
     "verify16_70b": ("llama70b_gqa", dict(num_seqs=2, context=("list", [300, 2000])), [16, 9]),
     # groups and block sizes the named workloads do not have
     "g3_bs32": ("tiny", dict(num_seqs=3, context=("list", [40, 300, 1000]), num_q_heads=12, num_kv_heads=4,
