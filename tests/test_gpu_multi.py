@@ -147,6 +147,58 @@ def test_decode_mqa_wide_groups(lib, Hq, Hkv, D, partition):
             assert np.array_equal(host_bits(d.decode(partition_tokens=partition, schedule=schedule)), got)
 
 
+@pytest.mark.parametrize("shape", ["rows128", "mqa"])
+@pytest.mark.parametrize("scale", [0.0, 1.0, 8.0, 64.0])
+def test_multi_extreme_logits_and_a_moving_max(lib, shape, scale):
+    """The multi-row kernel's online softmax under stress. In every sequence
+    the keys of each KV head are aligned with the query of the head's first
+    row and grow with the position, so that row's running maximum climbs on
+    every tile: across a 32-token step by less than the kernel's lazy-rescale
+    slack on the long contexts (probabilities above 1 against an older
+    reference) and by more on the short ones (a rescale every step); scale 64
+    makes the softmax nearly one-hot, scale 0 gives the mean of V. 128 rows
+    per KV head (waves of two row tiles) through pa_decode_multi, and MQA
+    (64 heads on one KV head) through pa_decode; unsplit and split.
+
+    V is the workload's scaled by 1/4 (exact in bf16): a nearly one-hot row
+    returns about one V element, and for |x| >= 4 one rounding to bf16
+    alone can miss x by up to 1/64 > 1e-2, so full-size V would test the
+    output format rather than the softmax."""
+    ctx = [40, 300, 1000, 2100]
+    if shape == "rows128":
+        w = W.make_workload("llama70b_gqa", num_seqs=len(ctx), context=("list", ctx))
+        qlens = [16, 16, 9, 16]
+    else:
+        w = W.make_workload("mixed_batch", num_seqs=len(ctx), context=("list", ctx), num_q_heads=64,
+                            num_kv_heads=1)
+        qlens = [1] * len(ctx)
+    mq = W.make_multi_query(w, qlens)
+    q32 = W.bf16_bits_to_f32(mq.q)
+    g, bs = w.spec.group, w.spec.block_size
+    kc = w.k_cache.copy()
+    for i, L in enumerate(ctx):
+        js = np.arange(L)
+        blocks, offs = w.block_tables[i, js // bs], js % bs
+        f = (np.float32(0.5) * (js + 1) / L).astype(np.float32)
+        for h in range(w.spec.num_kv_heads):
+            kc[blocks, offs, h] = W._to_bf16_bits(q32[mq.query_start[i], h * g][None, :] * f[:, None])
+    vc = W._to_bf16_bits(W.bf16_bits_to_f32(w.v_cache) * np.float32(0.25))
+    ref = oracle.multi_decode(mq.q, kc, vc, w.block_tables, w.context_lens, mq.query_start, scale)
+    d = DeviceWorkload(w, kc, vc)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    qs = torch.from_numpy(mq.query_start).cuda()
+    for part in (-1, 64):
+        note(f"multi extreme logits {shape} scale={scale} partition={part}")
+        if shape == "rows128":
+            out = pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, qs, scale,
+                                     int(max(qlens)), partition_tokens=part)
+        else:
+            out = pa.pa_decode(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, scale,
+                               partition_tokens=part)
+        torch.cuda.synchronize()
+        compare(host_bits(out), ref, *BF16_TOL)
+
+
 @pytest.mark.parametrize("S", [256, 300])
 def test_multi_rows_ordered_by_the_workgroups_or_the_list(lib, S):
     """Split multi-row items, longest first: ranked by each workgroup itself
