@@ -148,7 +148,7 @@ def test_decode_mqa_wide_groups(lib, Hq, Hkv, D, partition):
 
 
 @pytest.mark.parametrize("shape", ["rows128", "mqa"])
-@pytest.mark.parametrize("scale", [0.0, 1.0, 8.0, 64.0])
+@pytest.mark.parametrize("scale", [0.0, 1.0, 8.0, 64.0, -8.0])
 def test_multi_extreme_logits_and_a_moving_max(lib, shape, scale):
     """The multi-row kernel's online softmax under stress. In every sequence
     the keys of each KV head are aligned with the query of the head's first
@@ -156,7 +156,8 @@ def test_multi_extreme_logits_and_a_moving_max(lib, shape, scale):
     every tile: across a 32-token step by less than the kernel's lazy-rescale
     slack on the long contexts (probabilities above 1 against an older
     reference) and by more on the short ones (a rescale every step); scale 64
-    makes the softmax nearly one-hot, scale 0 gives the mean of V. 128 rows
+    makes the softmax nearly one-hot, scale 0 gives the mean of V, scale -8
+    favours the smallest scores (the earliest tokens for those rows). 128 rows
     per KV head (waves of two row tiles) through pa_decode_multi, and MQA
     (64 heads on one KV head) through pa_decode; unsplit and split.
 
