@@ -200,6 +200,40 @@ def test_multi_extreme_logits_and_a_moving_max(lib, shape, scale):
         compare(host_bits(out), ref, *BF16_TOL)
 
 
+@pytest.mark.parametrize("layout", ["dense", "sparse"])
+def test_multi_split_merge_grids(lib, layout):
+    """The split merge of pa_decode_multi, both grids: rows that see partition
+    0 only are finished by the kernel, the others merged. With queries on
+    every sequence ("dense": 24 sequences x 8 queries x 32 heads, D 128) the
+    merge walks (sequence, head, block of 8 rows): 24 * 32 * 1 blocks against
+    192 * 32 * 32 / 256 by rows. With queries on 2 of 64 sequences
+    ("sparse") that grid would be 64 * 32 * 2 blocks against 32 * 32 * 32 /
+    256, so the merge walks the rows. 512-token partitions over contexts of
+    17 to 3000 tokens: rows see 1 to 6 partitions, few enough for the flat
+    merge (one thread per float4 column of a row)."""
+    rng = np.random.default_rng(11)
+    if layout == "dense":
+        S = 24
+        ctx = rng.integers(17, 3000, size=S)
+        qlens = [8] * S
+    else:
+        S = 64
+        ctx = rng.integers(17, 3000, size=S)
+        qlens = [0] * S
+        qlens[5], qlens[40] = 16, 16
+    w = W.make_workload("mixed_batch", num_seqs=S, context=("list", [int(x) for x in ctx]))
+    mq = W.make_multi_query(w, qlens)
+    ref = oracle.multi_decode(mq.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, mq.query_start, w.scale)
+    d = DeviceWorkload(w)
+    q = torch.from_numpy(mq.q.view(np.int16)).view(torch.bfloat16).cuda()
+    qs = torch.from_numpy(mq.query_start).cuda()
+    note(f"multi split merge {layout}")
+    out = pa.pa_decode_multi(q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, qs, w.scale,
+                             int(max(qlens)), partition_tokens=512)
+    torch.cuda.synchronize()
+    compare(host_bits(out), ref, *BF16_TOL)
+
+
 @pytest.mark.parametrize("S", [256, 300])
 def test_multi_rows_ordered_by_the_workgroups_or_the_list(lib, S):
     """Split multi-row items, longest first: ranked by each workgroup itself
