@@ -18,9 +18,9 @@
 //
 // Rows. The (query token r, head hh) pairs of one (sequence, KV head) are
 // rows rho = r * g + hh; every wave of a workgroup owns RT 16-row tiles of
-// them (W = 1, 2, 4 or 8 waves, RT = 1 or 2: 16 W RT rows), so the
-// online-softmax state of a row never leaves its lanes and a workgroup needs
-// no combine step. Rows are the columns of the same MFMA tiles the decode
+// them (W = 1, 2, 4 or 8 waves of one tile, or 4 waves of two: 16 W RT
+// rows), so the online-softmax state of a row never leaves its lanes and a
+// workgroup needs no combine step. Rows are the columns of the same MFMA tiles the decode
 // kernel uses:
 //   S = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q^T rows
 //               of this wave (in registers with 4 or 8 waves or two row
