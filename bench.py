@@ -286,7 +286,7 @@ def bench_multi(args, w, k_cache, v_cache, tables, ctx, kv_b: int, k_scale: floa
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.kv, "data": "synthetic",
         "config": {"workload": f"{s.name} with {args.qlen} query tokens per sequence", "num_seqs": s.num_seqs,
                    "query_tokens": mq.num_tokens, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
-                   "head_dim": s.head_dim, "block_size": s.block_size},
+                   "head_dim": s.head_dim, "block_size": s.block_size, "layout": args.layout},
         "query_tokens_per_s": round(mq.num_tokens / (avg * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_decode_multi"},
