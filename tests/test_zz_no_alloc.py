@@ -2,8 +2,9 @@
 scratch in place of a caller workspace must give exactly pa_decode's output
 (same plan, same kernels) and match the float64 oracle, on consecutive
 calls that reuse the scratch -- a split plan, then a smaller batch, then
-one that needs no workspace -- and must refuse a plan whose workspace
-exceeds the scratch before touching any tensor."""
+one that needs no workspace, and the MQA route (the multi-row kernel) --
+and must refuse a plan whose workspace exceeds the scratch before touching
+any tensor."""
 import ctypes
 
 import numpy as np
@@ -75,3 +76,24 @@ def test_no_alloc_refuses_plans_beyond_the_scratch(lib):
     cl = pa.TensorSpec((256,), pa.PA_DTYPE_I32)
     note("no-alloc: oversized plan refused")
     assert _no_alloc(lib, (q, kc, kc, bt, cl), 0.1, q, **opts) == PA_ERR_SCRATCH
+
+
+def test_no_alloc_mqa_route(lib):
+    """More than 16 query heads per KV head (MQA: 64 on one) go to the
+    multi-row kernel; split, its partial states and merge use the scratch
+    as well. Same bits as pa_decode, and the oracle's values."""
+    w = W.make_workload("mixed_batch", num_seqs=6, context=("list", [1, 17, 300, 1000, 2100, 64]), num_q_heads=64,
+                        num_kv_heads=1)
+    d = DeviceWorkload(w)
+    tensors = (d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens)
+    opts = dict(partition_tokens=256)
+    plan = pa.pa_decode_get_plan(d.q, d.k_cache, d.block_tables, **opts)
+    assert plan["num_partitions"] > 1 and 0 < plan["workspace_bytes"] <= SCRATCH
+    note(f"no-alloc MQA opts={opts} plan={plan}")
+    ref_out = pa.pa_decode(*tensors, w.scale, **opts)
+    out = torch.full_like(d.q, float("nan"))
+    assert _no_alloc(lib, tensors, w.scale, out, **opts) == pa.PA_OK
+    torch.cuda.synchronize()
+    got = host_bits(out)
+    assert np.array_equal(got, host_bits(ref_out)), "differs from pa_decode"
+    compare(got, oracle.decode_workload(w), 1e-2, 1e-3)
